@@ -1,0 +1,231 @@
+/*
+ * pa.h — C ABI of libpa: attention over a paged KV cache on MI355X (gfx950).
+ *
+ * Keys and values of every sequence live in fixed pages of 16 tokens.  A
+ * per-sequence block table maps logical page j (tokens 16j .. 16j+15) to a
+ * physical block of the pool ("第 15 章：推理引擎与部署" §15.6 "PagedAttention：
+ * 分页 KV Cache"; "大模型部署.md" §2.1 item 4 "PageAttention 内存管理技术详解").
+ * Attention is exact softmax(Q Kᵀ · scale) V computed with a tiled online
+ * softmax ("第 15 章" §15.1 "算法详解"), over batches that mix single-token
+ * decodes with causal prefill chunks ("DeepSpeed-FastGen 深度解析" §3.2,
+ * Dynamic SplitFuse).
+ *
+ * Conventions for every entry point:
+ *  - All integers are signed; sizes are element counts unless named *_bytes.
+ *  - "device" pointers point to GPU memory owned by the caller; the library
+ *    never allocates, frees or retains device memory.  "host" pointers point
+ *    to CPU memory and are only read during the call.
+ *  - Device work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *    stream) and returns without synchronising.  Faults inside kernels
+ *    surface at the caller's next synchronisation.
+ *  - Argument errors are detected on the host before anything is enqueued;
+ *    the call then returns a negative pa_status and pa_last_error() explains.
+ *  - Facts only the device can see (block ids, slots, lengths read from device
+ *    arrays) are checked by the kernels: an offending item is skipped (no
+ *    out-of-range address is ever formed) and a PA_DEV_* bit is OR-ed into
+ *    *dev_status when dev_status is not NULL.  The caller zeroes that int32
+ *    before the call and reads it after synchronising.
+ *
+ * Pool layout (dtype T, X = 16 / sizeof(T): 4 for float32, 8 for bfloat16):
+ *    k_cache  [num_blocks][num_kv_heads][head_dim / X][16][X]
+ *    v_cache  [num_blocks][num_kv_heads][head_dim][16]
+ *  Token o of physical block b, KV head h keeps key element e at
+ *  k_cache[b][h][e / X][o][e % X] and value element e at v_cache[b][h][e][o].
+ *  Each (block, head) page is one contiguous run of 16 * head_dim elements,
+ *  so a 16-token page is read with fully coalesced 16-byte loads.
+ *  A slot is block * 16 + offset.
+ *
+ * Supported: head_dim 64 or 128, block_size 16, num_q_heads a multiple of
+ * num_kv_heads, dtype float32 or bfloat16 (q, caches and output share it;
+ * accumulation is float32).  pa_forward in float32 takes head_dim 64 only
+ * (PA_ERR_UNSUPPORTED otherwise); cache write and block copy take both.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID = -1,      /* bad argument (null pointer, bad size, bad id)          */
+  PA_ERR_UNSUPPORTED = -2,  /* valid but not implemented (head_dim, block_size, dtype) */
+  PA_ERR_NO_BLOCKS = -3,    /* allocator pool exhausted; allocator state unchanged     */
+  PA_ERR_REFCOUNT = -4,     /* reference count would drop below zero                   */
+  PA_ERR_NOT_FOUND = -5,    /* unknown sequence id                                     */
+  PA_ERR_HIP = -6           /* the HIP runtime reported an error at launch             */
+} pa_status;
+
+typedef enum pa_dtype { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+typedef enum pa_alloc_status {
+  PA_ALLOC_OK = 0,     /* enough free blocks now                        */
+  PA_ALLOC_LATER = 1,  /* enough blocks exist, not enough are free now  */
+  PA_ALLOC_NEVER = 2   /* the pool can never hold the request           */
+} pa_alloc_status;
+
+/* Bits OR-ed into *dev_status by kernels. */
+#define PA_DEV_BAD_BLOCK 1   /* block id outside [0, num_blocks) (table entry or copy pair) */
+#define PA_DEV_BAD_SLOT 2    /* slot outside [0, num_blocks * 16)                            */
+#define PA_DEV_BAD_LENGTH 4  /* context length / query offsets inconsistent with the bounds  */
+
+/* Message for the last failing call on this thread ("" if none).  Valid until
+ * the next call into the library from the same thread. */
+const char* pa_last_error(void);
+
+/* ABI revision of this header; bumped on any incompatible change. */
+int32_t pa_abi_version(void);
+
+/* ------------------------------------------------------------------ cache write
+ * pa_reshape_and_cache — store the new tokens' keys and values into the pool.
+ * For every token t with slot_mapping[t] >= 0 and every KV head h:
+ *   k_cache[slot/16][h][:][slot%16][:] = key[t][h][:]   (in the layout above)
+ *   v_cache[slot/16][h][:][slot%16]    = value[t][h][:]
+ * exact byte copies.  A negative slot marks a padding token and is skipped.
+ * Slots must be distinct (overlapping writes race); a slot >= num_blocks*16
+ * is skipped and flagged PA_DEV_BAD_SLOT.
+ * (The new K/V enter the cache at each decode step, "【自用】AI infra相关" part
+ * 一.2; slots index the KV storage directly like SGLang's out_cache_loc,
+ * "大模型部署.md" §2.4 item 4.)
+ *   key, value    device, [num_tokens][num_kv_heads][head_dim] of dtype
+ *   k_cache, v_cache  device, pool layout above, num_blocks blocks
+ *   slot_mapping  device, int64 [num_tokens]
+ */
+pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                               const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               pa_dtype dtype, int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------ attention
+ * Workspace bytes pa_forward needs for a batch within these bounds.  The
+ * workspace holds the per-call plan, work-queue counters and the partial
+ * (m, l, O) states of split contexts; it needs no initialisation and its
+ * content is meaningless between calls.
+ */
+size_t pa_forward_workspace_bytes(int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t max_context_len, pa_dtype dtype);
+
+/* pa_forward — paged attention over a ragged batch of sequences.
+ * Sequence s owns query rows query_start_loc[s] .. query_start_loc[s+1]-1
+ * (q_len rows, 0 <= q_len <= context_lens[s]) and sees context_lens[s] keys,
+ * the new tokens included (write them with pa_reshape_and_cache first).
+ * Row i of sequence s sits at position p = context_lens[s] - q_len + i and
+ * attends keys 0..p: a decode row (q_len 1) sees the whole context, a prefill
+ * chunk is causal inside itself.  Query head h reads KV head h / G with
+ * G = num_q_heads / num_kv_heads ("大模型部署.md" §4.1 item 4, MQA/GQA).
+ *   out[t][h][:] = Σ_j softmax_j(scale · q[t][h]·k_j) v_j      (rounded to dtype)
+ * ("第7章：大模型部署实战" §2.2.2 formula; "第 15 章" §15.1).  Long contexts
+ * are split into fixed key partitions processed by separate wavefronts and
+ * merged exactly by log-sum-exp rescaling; partition boundaries depend only on
+ * the sequence's own lengths, so a sequence's output does not depend on
+ * what else is in the batch.
+ *   out            device, [total_q_tokens][num_q_heads][head_dim] of dtype
+ *   q              device, [total_q_tokens][num_q_heads][head_dim] of dtype
+ *   k_cache, v_cache  device, pool layout above
+ *   block_tables   device, int32 [num_seqs][max_blocks_per_seq]; entries past
+ *                  ceil(context_len/16) are never read
+ *   context_lens   device, int32 [num_seqs]
+ *   query_start_loc device, int32 [num_seqs + 1], query_start_loc[0] = 0,
+ *                  non-decreasing, query_start_loc[num_seqs] = total_q_tokens
+ *   max_q_len, max_context_len  host-known upper bounds of the device arrays
+ *                  (the launch is sized from them without reading the device)
+ *   scale          softmax scale (1/sqrt(head_dim) for standard attention)
+ *   workspace      device, >= pa_forward_workspace_bytes(...) bytes, 256-byte aligned
+ * Output rows of sequences flagged by the device checks are not written.
+ */
+pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, const int32_t* query_start_loc,
+                     int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                     int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                     pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                     int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------ copy-on-write
+ * pa_copy_blocks — for each pair (src, dst) = block_pairs[2i], block_pairs[2i+1],
+ * copy the whole key and value page of block src (all KV heads) onto block dst,
+ * byte for byte: the private copy a sequence needs before it writes into a
+ * block it shares ("大模型部署.md" §2.1 item 3 append_slots returning
+ * (old, new); item 4 写时复制).  Destinations must be distinct and must not
+ * be sources of other pairs.  Pairs with an id outside [0, num_blocks) are
+ * skipped and flagged PA_DEV_BAD_BLOCK.
+ *   block_pairs  device, int32 [num_pairs][2]
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
+                         int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, pa_dtype dtype,
+                         int32_t* dev_status, void* stream);
+
+/* ------------------------------------------------------------------ host allocator
+ * Reference-counted physical block allocator with per-sequence block tables
+ * ("大模型部署.md" §2.1 item 3, BlockSpaceManagerV1: _allocate_sequence,
+ * can_allocate with watermark, append_slots with copy-on-write; "第7章" §2.3:
+ * a free list popped from its end and appended to on release).  Pure host
+ * code: no device memory, no HIP calls.  A handle is owned by the caller
+ * (create/destroy) and is not thread-safe.  Every failing call leaves the
+ * allocator unchanged.
+ */
+typedef struct pa_allocator pa_allocator;
+
+/* initial_free_order: host int32 [num_blocks], a permutation of 0..num_blocks-1
+ * giving the free stack bottom to top (blocks are taken from the end), or NULL
+ * for 0..num_blocks-1.  watermark: fraction of the pool kept in reserve by
+ * pa_alloc_can_allocate (int(watermark * num_blocks) blocks). */
+pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size, double watermark,
+                          const int32_t* initial_free_order, pa_allocator** out);
+void pa_alloc_destroy(pa_allocator* a);
+int32_t pa_alloc_num_free(const pa_allocator* a);
+/* Reference count of a block, or -1 for an id outside the pool. */
+int32_t pa_alloc_ref_count(const pa_allocator* a, int32_t block);
+/* Admission check for a new sequence of num_tokens tokens:
+ * NEVER if num_blocks - need < watermark blocks, OK if free - need >= watermark
+ * blocks, else LATER (need = ceil(num_tokens / block_size)). */
+pa_status pa_alloc_can_allocate(const pa_allocator* a, int32_t num_tokens, pa_alloc_status* out);
+
+/* New sequence holding num_tokens tokens: ceil(num_tokens/block_size) blocks
+ * taken in logical order, each with reference count 1.  All or nothing. */
+pa_status pa_seq_create(pa_allocator* a, int64_t seq_id, int32_t num_tokens);
+/* child shares every block of parent (reference counts + 1) and its length. */
+pa_status pa_seq_fork(pa_allocator* a, int64_t parent_id, int64_t child_id);
+/* Reserve the slot of the sequence's next token (length L -> L+1):
+ *  - table one block short: take a free block;
+ *  - else last block shared (count > 1): take a free block in its place, drop
+ *    one reference from the old block and report (old, new) in
+  *    *cow_src and *cow_dst (copy it with pa_copy_blocks before writing);
+ *  - else nothing changes.
+ * *slot_out = table[L/16]*16 + L%16.  *cow_src = *cow_dst = -1 without a copy. */
+pa_status pa_seq_append_slot(pa_allocator* a, int64_t seq_id, int64_t* slot_out,
+                             int32_t* cow_src, int32_t* cow_dst);
+/* pa_seq_append_slot for n sequences in order; stops at the first failure
+ * (the sequences before it keep their new slot).  slots_out: int64 [n];
+ * cow_pairs_out: int32 [n][2] receives only the copies that happened, packed;
+ * *num_cow_out their count. */
+pa_status pa_seq_append_slots(pa_allocator* a, int32_t n, const int64_t* seq_ids,
+                              int64_t* slots_out, int32_t* cow_pairs_out, int32_t* num_cow_out);
+/* Slots of token positions start .. start+n-1 (must lie inside the sequence). */
+pa_status pa_seq_slots(const pa_allocator* a, int64_t seq_id, int32_t start, int32_t n,
+                       int64_t* slots_out);
+/* Number of tokens of a sequence. */
+pa_status pa_seq_num_tokens(const pa_allocator* a, int64_t seq_id, int32_t* out);
+/* Copy a sequence's block table into out[0..cap); *n_out = its length
+ * (PA_ERR_INVALID if cap is too small). */
+pa_status pa_seq_block_table(const pa_allocator* a, int64_t seq_id, int32_t* out, int32_t cap,
+                             int32_t* n_out);
+/* Block tables of n sequences as rows of a [n][cap] matrix, padded with -1. */
+pa_status pa_seq_block_tables(const pa_allocator* a, int32_t n, const int64_t* seq_ids,
+                              int32_t* out, int32_t cap);
+/* Drop the sequence: one reference less on each block in logical order;
+ * blocks reaching zero return to the free stack in that order. */
+pa_status pa_seq_free(pa_allocator* a, int64_t seq_id);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

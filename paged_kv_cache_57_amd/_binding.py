@@ -1,0 +1,267 @@
+"""ctypes binding of libpa: argument marshalling only.
+
+Every function here has the name of the C entry point it calls and does no
+computation of its own beyond reading tensor shapes, pointers and the current
+HIP stream.  torch supplies device memory and streams.  Importing this module
+fails loudly when libpa.so has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpa.so")
+
+PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS = 0, -1, -2, -3
+PA_ERR_REFCOUNT, PA_ERR_NOT_FOUND, PA_ERR_HIP = -4, -5, -6
+PA_F32, PA_BF16 = 0, 1
+PA_ALLOC_OK, PA_ALLOC_LATER, PA_ALLOC_NEVER = 0, 1, 2
+PA_DEV_BAD_BLOCK, PA_DEV_BAD_SLOT, PA_DEV_BAD_LENGTH = 1, 2, 4
+BLOCK = 16
+
+_STATUS_NAMES = {PA_ERR_INVALID: "PA_ERR_INVALID", PA_ERR_UNSUPPORTED: "PA_ERR_UNSUPPORTED",
+                 PA_ERR_NO_BLOCKS: "PA_ERR_NO_BLOCKS", PA_ERR_REFCOUNT: "PA_ERR_REFCOUNT",
+                 PA_ERR_NOT_FOUND: "PA_ERR_NOT_FOUND", PA_ERR_HIP: "PA_ERR_HIP"}
+
+
+class PAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+                      "or `python -m paged_kv_cache_57_amd.build` first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i32, _i64, _sz, _vp, _f32, _f64 = (ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p,
+                                     ctypes.c_float, ctypes.c_double)
+_pi32, _pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+
+_SIGS = {
+    "pa_last_error": (ctypes.c_char_p, []),
+    "pa_abi_version": (_i32, []),
+    "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "pa_forward_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                          _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
+    "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "pa_alloc_create": (_i32, [_i32, _i32, _f64, _vp, ctypes.POINTER(_vp)]),
+    "pa_alloc_destroy": (None, [_vp]),
+    "pa_alloc_num_free": (_i32, [_vp]),
+    "pa_alloc_ref_count": (_i32, [_vp, _i32]),
+    "pa_alloc_can_allocate": (_i32, [_vp, _i32, _pi32]),
+    "pa_seq_create": (_i32, [_vp, _i64, _i32]),
+    "pa_seq_fork": (_i32, [_vp, _i64, _i64]),
+    "pa_seq_append_slot": (_i32, [_vp, _i64, _pi64, _pi32, _pi32]),
+    "pa_seq_append_slots": (_i32, [_vp, _i32, _vp, _vp, _vp, _pi32]),
+    "pa_seq_slots": (_i32, [_vp, _i64, _i32, _i32, _vp]),
+    "pa_seq_num_tokens": (_i32, [_vp, _i64, _pi32]),
+    "pa_seq_block_table": (_i32, [_vp, _i64, _vp, _i32, _pi32]),
+    "pa_seq_block_tables": (_i32, [_vp, _i32, _vp, _vp, _i32]),
+    "pa_seq_free": (_i32, [_vp, _i64]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTS = tuple(_SIGS)
+
+
+def _check(status: int):
+    if status != PA_OK:
+        raise PAError(status, _lib.pa_last_error().decode())
+
+
+def pa_last_error() -> str:
+    return _lib.pa_last_error().decode()
+
+
+def pa_abi_version() -> int:
+    return _lib.pa_abi_version()
+
+
+# ---------------------------------------------------------------- device entry points
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise PAError(PA_ERR_UNSUPPORTED, f"dtype {t.dtype}")
+
+
+def _dev(t, name, dtype=None):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise PAError(PA_ERR_INVALID, f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise PAError(PA_ERR_INVALID, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise PAError(PA_ERR_INVALID, f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(t, stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return stream.cuda_stream
+
+
+def _pool_dims(k_cache, v_cache):
+    nb, hkv, nch, blk, x = k_cache.shape
+    d = nch * x
+    if tuple(v_cache.shape) != (nb, hkv, d, blk) or v_cache.dtype != k_cache.dtype:
+        raise PAError(PA_ERR_INVALID, f"value pool {tuple(v_cache.shape)} does not match key pool "
+                                      f"{tuple(k_cache.shape)}")
+    return nb, hkv, d, blk
+
+
+def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, dev_status=None, stream=None):
+    import torch
+    nb, hkv, d, blk = _pool_dims(k_cache, v_cache)
+    T = key.shape[0]
+    if tuple(key.shape) != (T, hkv, d) or tuple(value.shape) != (T, hkv, d):
+        raise PAError(PA_ERR_INVALID, "key/value must be [num_tokens, kv_heads, head_dim]")
+    if slot_mapping.shape != (T,):
+        raise PAError(PA_ERR_INVALID, "slot_mapping must be [num_tokens]")
+    _check(_lib.pa_reshape_and_cache(
+        _dev(key, "key", k_cache.dtype), _dev(value, "value", k_cache.dtype), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int64), T, nb, hkv, d, blk,
+        _dtype_code(k_cache), _dev(dev_status, "dev_status", torch.int32), _stream(k_cache, stream)))
+
+
+def pa_forward_workspace_bytes(num_seqs, total_q_tokens, max_q_len, num_q_heads, num_kv_heads, head_dim,
+                               max_context_len, dtype: int) -> int:
+    return int(_lib.pa_forward_workspace_bytes(num_seqs, total_q_tokens, max_q_len, num_q_heads,
+                                               num_kv_heads, head_dim, max_context_len, dtype))
+
+
+def pa_forward(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, max_q_len,
+               max_context_len, scale, workspace, dev_status=None, stream=None):
+    import torch
+    nb, hkv, d, blk = _pool_dims(k_cache, v_cache)
+    T, hq, dq = q.shape
+    if dq != d or tuple(out.shape) != (T, hq, d):
+        raise PAError(PA_ERR_INVALID, "q/out must be [total_q_tokens, num_q_heads, head_dim]")
+    S = context_lens.shape[0]
+    if tuple(query_start_loc.shape) != (S + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise PAError(PA_ERR_INVALID, "context_lens [S], query_start_loc [S+1], block_tables [S, M]")
+    _check(_lib.pa_forward(
+        _dev(out, "out", q.dtype), _dev(q, "q", k_cache.dtype), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), _dev(query_start_loc, "query_start_loc", torch.int32),
+        S, T, int(max_q_len), int(max_context_len), hq, hkv, d, blk, nb, float(scale), _dtype_code(q),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _dev(dev_status, "dev_status", torch.int32), _stream(q, stream)))
+
+
+def pa_copy_blocks(k_cache, v_cache, block_pairs, dev_status=None, stream=None):
+    import torch
+    nb, hkv, d, blk = _pool_dims(k_cache, v_cache)
+    if block_pairs.dim() != 2 or block_pairs.shape[1] != 2:
+        raise PAError(PA_ERR_INVALID, "block_pairs must be [num_pairs, 2]")
+    _check(_lib.pa_copy_blocks(
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_pairs, "block_pairs", torch.int32),
+        block_pairs.shape[0], nb, hkv, d, blk, _dtype_code(k_cache),
+        _dev(dev_status, "dev_status", torch.int32), _stream(k_cache, stream)))
+
+
+# ---------------------------------------------------------------- host allocator
+
+def _np_ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+class Allocator:
+    """Owner of one pa_allocator handle; methods call the pa_alloc_* / pa_seq_* entry points."""
+
+    def __init__(self, num_blocks: int, block_size: int = BLOCK, watermark: float = 0.0,
+                 initial_free_order=None):
+        self._h = ctypes.c_void_p()
+        h = ctypes.c_void_p()
+        order = None
+        if initial_free_order is not None:
+            order = np.ascontiguousarray(initial_free_order, dtype=np.int32)
+        _check(_lib.pa_alloc_create(num_blocks, block_size, watermark,
+                                    None if order is None else _np_ptr(order), ctypes.byref(h)))
+        self._h = h
+        self.num_blocks = num_blocks
+        self.block_size = block_size
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _lib.pa_alloc_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    __del__ = close
+
+    def num_free(self) -> int:
+        return _lib.pa_alloc_num_free(self._h)
+
+    def ref_count(self, block: int) -> int:
+        return _lib.pa_alloc_ref_count(self._h, block)
+
+    def can_allocate(self, num_tokens: int) -> int:
+        out = ctypes.c_int32()
+        _check(_lib.pa_alloc_can_allocate(self._h, num_tokens, ctypes.byref(out)))
+        return out.value
+
+    def create(self, seq_id: int, num_tokens: int):
+        _check(_lib.pa_seq_create(self._h, seq_id, num_tokens))
+
+    def fork(self, parent: int, child: int):
+        _check(_lib.pa_seq_fork(self._h, parent, child))
+
+    def append_slot(self, seq_id: int):
+        slot, src, dst = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.pa_seq_append_slot(self._h, seq_id, ctypes.byref(slot), ctypes.byref(src),
+                                       ctypes.byref(dst)))
+        return slot.value, (None if src.value < 0 else (src.value, dst.value))
+
+    def append_slots(self, seq_ids):
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        slots = np.empty(len(ids), np.int64)
+        pairs = np.empty((max(len(ids), 1), 2), np.int32)
+        n = ctypes.c_int32()
+        _check(_lib.pa_seq_append_slots(self._h, len(ids), _np_ptr(ids), _np_ptr(slots), _np_ptr(pairs),
+                                        ctypes.byref(n)))
+        return slots, pairs[:n.value].copy()
+
+    def slots(self, seq_id: int, start: int, n: int):
+        out = np.empty(n, np.int64)
+        _check(_lib.pa_seq_slots(self._h, seq_id, start, n, _np_ptr(out)))
+        return out
+
+    def num_tokens(self, seq_id: int) -> int:
+        out = ctypes.c_int32()
+        _check(_lib.pa_seq_num_tokens(self._h, seq_id, ctypes.byref(out)))
+        return out.value
+
+    def block_table(self, seq_id: int):
+        n = ctypes.c_int32()
+        st = _lib.pa_seq_block_table(self._h, seq_id, None, 0, ctypes.byref(n))
+        if st not in (PA_OK, PA_ERR_INVALID) or (st == PA_ERR_INVALID and n.value == 0):
+            _check(st)
+        out = np.empty(max(n.value, 1), np.int32)
+        _check(_lib.pa_seq_block_table(self._h, seq_id, _np_ptr(out), n.value, ctypes.byref(n)))
+        return out[:n.value].tolist()
+
+    def block_tables(self, seq_ids, cap: int):
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        out = np.empty((len(ids), cap), np.int32)
+        _check(_lib.pa_seq_block_tables(self._h, len(ids), _np_ptr(ids), _np_ptr(out), cap))
+        return out
+
+    def free(self, seq_id: int):
+        _check(_lib.pa_seq_free(self._h, seq_id))

@@ -1,0 +1,54 @@
+"""Builds libpa.so in-tree for gfx950 with hipcc.
+
+The library is one shared object: the HIP kernels with their C-ABI launchers
+and the host allocator.  Packed-FP32 instructions are disabled for device
+code (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass of
+hipcc warns that it does not know the feature, which is harmless.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libpa.so")
+SOURCES = ["pa_status.cpp", "pa_alloc.cpp", "pa_cache.hip", "pa_attention.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function"]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libpa.so; returns its path. Always rebuilds."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(objdir, src + ".o")
+        cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+        if src.endswith(".hip"):
+            cmd[1:1] = ["-x", "hip", *DEVICE_FLAGS]
+        _run(cmd, verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", *DEVICE_FLAGS, *objs, "-o", tmp], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
+    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{err}")
+    if verbose and err.strip():
+        print(err, file=sys.stderr)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

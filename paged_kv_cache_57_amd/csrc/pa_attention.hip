@@ -1,0 +1,753 @@
+// Paged attention for gfx950: planner, VALU and MFMA workers, log-sum-exp merge.
+//
+// What is computed: out = softmax(q Kᵀ · scale) V over each sequence's
+// visible keys ("第7章：大模型部署实战" §2.2.2 formula; "第 15 章：推理引擎与部署"
+// §15.1), with the keys and values gathered page by page through the block
+// table ("第 15 章" §15.6 "PagedAttention：分页 KV Cache").
+//
+// How:
+//  * A one-workgroup planner reads query_start_loc / context_lens, checks
+//    them, and turns every sequence into work items.  An item is a key
+//    partition (a fixed range of key positions) of either
+//      - one query row and one query head (VALU class: float32 batches and
+//        bfloat16 single-row decodes with one query head per KV head), or
+//      - a tile of 16 query rows that share one KV head (MFMA class: bfloat16
+//        GQA decodes, whose G query heads become the rows, and bfloat16
+//        prefill chunks, whose positions x G heads become the rows).
+//    Partition sizes depend only on the sequence's own lengths, so a
+//    sequence's result does not depend on the rest of the batch.
+//  * Persistent workers pull items from a device work queue.  Each item
+//    streams its pages with 16-byte loads and keeps the running max m, the
+//    running sum l and the unnormalised output O of the tiled online softmax
+//    ("第 15 章" §15.1 "算法详解": m_new = max(m, rowmax S), α = exp(m − m_new),
+//    P = exp(S − m_new), l = αl + rowsum P, O = diag(α)O + PV), in base 2
+//    (scale · log2 e folded into the scores, exp2 in hardware).
+//  * A context split into several partitions is merged by rescaling the
+//    partial states to the common maximum — the same α step applied to
+//    finished states: M = max m_p, l = Σ l_p 2^(m_p − M), O = Σ O_p 2^(m_p − M) / l.
+//    The pages name split-K decoding for long contexts ("大模型部署.md" §2.5
+//    item 2, TurboMind) without giving its math; this merge is the
+//    rescaling rule above.
+#include <cmath>
+
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+enum { CLS_NONE = 0, CLS_VALU = 1, CLS_MFMA = 2 };
+constexpr int kPartValu = 512;          // keys per VALU partition
+constexpr int kPartMfmaDecode = 256;    // keys per partition of a one-row GQA decode tile
+constexpr int kPartMfmaPrefill = 1024;  // keys per partition of a prefill tile
+constexpr int kTileRows = 16;           // query rows per MFMA item
+constexpr int kMaxWorkerGroups = 2048;  // persistent workgroups per worker launch
+constexpr float kNegInf = -INFINITY;
+
+// floats per partial state: O[D], m, l, padded to keep 16-byte alignment
+__host__ __device__ constexpr int slot_floats(int D) { return D + 4; }
+
+struct SeqWork {
+  int cls;
+  int part;    // keys per partition
+  int nparts;  // partitions of the context
+  int groups;  // items per partition index: rows x heads (VALU) or tiles x KV heads (MFMA)
+};
+
+__host__ __device__ inline SeqWork seq_work(bool is_f32, int G, int Hq, int Hkv, int q_len, int L) {
+  SeqWork w{CLS_NONE, 1, 0, 0};
+  if (q_len <= 0 || L <= 0) return w;
+  if (is_f32 || (G == 1 && q_len == 1)) {
+    w.cls = CLS_VALU;
+    w.part = kPartValu;
+    w.groups = q_len * Hq;
+  } else {
+    w.cls = CLS_MFMA;
+    w.part = q_len == 1 ? kPartMfmaDecode : kPartMfmaPrefill;
+    w.groups = ((q_len * G + kTileRows - 1) / kTileRows) * Hkv;
+  }
+  w.nparts = (L + w.part - 1) / w.part;
+  return w;
+}
+
+// Smallest partition any sequence of this batch can use (bounds the partial states).
+inline int min_part(bool is_f32, int G) {
+  if (is_f32) return kPartValu;
+  return G == 1 ? kPartValu : kPartMfmaDecode;
+}
+
+struct AttnParams {
+  void* out;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* qsl;
+  int32_t mbps;
+  int32_t num_seqs, T, max_q_len, max_ctx;
+  int32_t Hq, Hkv, G, num_blocks;
+  float scale_log2;
+  int32_t is_f32;
+  int32_t* ctrl;  // [0] VALU queue, [1] MFMA queue, [2] VALU items, [3] MFMA items
+  int32_t* pre_v;
+  int32_t* pre_m;
+  float* partials;  // [T][Hq][maxparts][D + 4]: O (unnormalised), m, l, 2 pad
+  int32_t maxparts;
+  int32_t* dev_status;
+};
+
+struct SeqInfo {
+  int a, q_len, L;
+  bool ok;
+};
+
+__device__ inline SeqInfo read_seq(const AttnParams& p, int s) {
+  SeqInfo si;
+  si.a = p.qsl[s];
+  const int b = p.qsl[s + 1];
+  si.q_len = b - si.a;
+  si.L = p.context_lens[s];
+  si.ok = si.a >= 0 && b >= si.a && b <= p.T && si.q_len <= p.max_q_len && si.L >= 0 &&
+          si.L <= p.max_ctx && si.q_len <= si.L && (si.L + kBlock - 1) / kBlock <= p.mbps;
+  return si;
+}
+
+// Largest s in [0, n) with pre[s] <= x (pre non-decreasing, pre[0] <= x < pre[n]).
+__device__ inline int find_seq(const int32_t* pre, int n, int x) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (pre[mid] <= x) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// ---------------------------------------------------------------- planner
+__global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
+  __shared__ int sv[1024], sm[1024];
+  __shared__ int carry_v, carry_m;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    carry_v = carry_m = 0;
+    if (p.qsl[0] != 0 || p.qsl[p.num_seqs] != p.T) flag_status(p.dev_status, PA_DEV_BAD_LENGTH);
+  }
+  __syncthreads();
+  for (int base = 0; base < p.num_seqs; base += 1024) {
+    const int s = base + tid;
+    int iv = 0, im = 0;
+    if (s < p.num_seqs) {
+      const SeqInfo si = read_seq(p, s);
+      if (!si.ok) {
+        flag_status(p.dev_status, PA_DEV_BAD_LENGTH);
+      } else {
+        const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L);
+        const int items = w.groups * w.nparts;
+        if (w.cls == CLS_VALU) iv = items;
+        else if (w.cls == CLS_MFMA) im = items;
+      }
+    }
+    sv[tid] = iv;
+    sm[tid] = im;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int xv = tid >= off ? sv[tid - off] : 0;
+      const int xm = tid >= off ? sm[tid - off] : 0;
+      __syncthreads();
+      sv[tid] += xv;
+      sm[tid] += xm;
+      __syncthreads();
+    }
+    if (s < p.num_seqs) {
+      p.pre_v[s] = carry_v + sv[tid] - iv;
+      p.pre_m[s] = carry_m + sm[tid] - im;
+    }
+    __syncthreads();
+    if (tid == 1023) {
+      carry_v += sv[1023];
+      carry_m += sm[1023];
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    p.pre_v[p.num_seqs] = carry_v;
+    p.pre_m[p.num_seqs] = carry_m;
+    p.ctrl[0] = 0;
+    p.ctrl[1] = 0;
+    p.ctrl[2] = carry_v;
+    p.ctrl[3] = carry_m;
+  }
+}
+
+__device__ inline int next_item(int32_t* queue, int lane) {
+  int item = 0;
+  if (lane == 0) item = atomicAdd(queue, 1);
+  return __builtin_amdgcn_readfirstlane(item);
+}
+
+// Loads this partition's physical block ids into lanes 0..nblk-1 and checks
+// them.  Returns false (and flags) if any id lies outside the pool.
+__device__ inline bool load_block_ids(const AttnParams& p, int s, int first_blk, int nblk, int lane,
+                                      int& bid) {
+  bid = 0;
+  if (lane < nblk) bid = p.block_tables[(int64_t)s * p.mbps + first_blk + lane];
+  const bool bad = lane < nblk && (bid < 0 || bid >= p.num_blocks);
+  if (__builtin_amdgcn_ballot_w64(bad)) {
+    if (lane == 0) flag_status(p.dev_status, PA_DEV_BAD_BLOCK);
+    return false;
+  }
+  return true;
+}
+
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ---------------------------------------------------------------- VALU worker
+// One wavefront per item: one query row x one query head x one key partition.
+// Keys are processed 64 at a time (4 pages).  Lane layout of a key page
+// [D/X][16][X]: load i of page j gives lane l the 16-byte group 4i + l/16 of
+// key l%16, so each lane accumulates a partial dot over D/4 elements and two
+// exchanges (lanes ±32, ±16) finish the four pages' dots, leaving lane l with
+// the score of key l of the 64.  Value pages [D][16] give lane l, in load i,
+// X consecutive keys of one value column, so P·V accumulates in-lane and only
+// the lanes sharing a column are summed at the end.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
+  constexpr int X = Elem<T>::X;
+  constexpr int NCH = D / X;   // 16-byte groups per key row
+  constexpr int NIK = NCH / 4; // key loads per page
+  constexpr int LPR = 16 / X;  // lanes per value column
+  constexpr int RPI = 64 / LPR;  // value columns per load
+  constexpr int NIV = D / RPI;   // value loads per page
+  constexpr bool kBf16 = sizeof(T) == 2;
+  __shared__ float lds_p[4][64];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int total = p.ctrl[2];
+  const T* __restrict__ kc = (const T*)p.k_cache;
+  const T* __restrict__ vc = (const T*)p.v_cache;
+  const int64_t page_elems = (int64_t)kBlock * D;
+
+  for (;;) {
+    const int item = next_item(&p.ctrl[0], lane);
+    if (item >= total) break;
+    const int s = find_seq(p.pre_v, p.num_seqs, item);
+    const int local = item - p.pre_v[s];
+    const SeqInfo si = read_seq(p, s);
+    const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L);
+    const int pidx = local % w.nparts;
+    const int rh = local / w.nparts;
+    const int h = rh % p.Hq;
+    const int i = rh / p.Hq;
+    const int t = si.a + i;
+    const int pos = si.L - si.q_len + i;
+    const int g = h / p.G;
+    const int kv_lo = pidx * w.part;
+    const int kv_hi = min(kv_lo + w.part, pos + 1);
+
+    float m = kNegInf, lsum = 0.f;
+    float acc[NIV];
+#pragma unroll
+    for (int k = 0; k < NIV; ++k) acc[k] = 0.f;
+
+    if (kv_lo < kv_hi) {
+      int bidv;
+      const int nblk = (kv_hi - kv_lo + kBlock - 1) / kBlock;
+      if (!load_block_ids(p, s, kv_lo / kBlock, nblk, lane, bidv)) continue;
+
+      // q row: the 16-byte groups this lane multiplies
+      const T* qrow = (const T*)p.q + ((int64_t)t * p.Hq + h) * D;
+      u32x4 qv[NIK];
+#pragma unroll
+      for (int k = 0; k < NIK; ++k) qv[k] = ld16(qrow + (4 * k + (lane >> 4)) * X);
+
+      for (int base = kv_lo; base < kv_hi; base += 64) {
+        const int j0 = (base - kv_lo) >> 4;
+        u32x4 kr[4][NIK], vr[4][NIV];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (base + kBlock * j < kv_hi) {
+            const int bid = readlane(bidv, j0 + j);
+            const int64_t page = ((int64_t)bid * p.Hkv + g) * page_elems;
+            const T* kp = kc + page;
+            const T* vp = vc + page;
+#pragma unroll
+            for (int k = 0; k < NIK; ++k)
+              kr[j][k] = ld16(kp + ((4 * k + (lane >> 4)) * kBlock + (lane & 15)) * X);
+#pragma unroll
+            for (int k = 0; k < NIV; ++k)
+              vr[j][k] = ld16(vp + (RPI * k + lane / LPR) * kBlock + (lane % LPR) * X);
+          } else {
+#pragma unroll
+            for (int k = 0; k < NIK; ++k) kr[j][k] = u32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int k = 0; k < NIV; ++k) vr[j][k] = u32x4{0, 0, 0, 0};
+          }
+        }
+        // partial dots of this lane's key (lane % 16) in each of the 4 pages
+        float kd[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float d = 0.f;
+#pragma unroll
+          for (int k = 0; k < NIK; ++k) {
+            if constexpr (kBf16) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) d = dot2_bf16(kr[j][k][e], qv[k][e], d);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                d = fmaf(__uint_as_float(kr[j][k][e]), __uint_as_float(qv[k][e]), d);
+            }
+          }
+          kd[j] = d;
+        }
+        // finish the dots across the four lane groups: lane l ends with key l
+        const bool up2 = lane & 32, up1 = lane & 16;
+        float keep0 = up2 ? kd[2] : kd[0], keep1 = up2 ? kd[3] : kd[1];
+        keep0 += shfl_xor_f(up2 ? kd[0] : kd[2], 32);
+        keep1 += shfl_xor_f(up2 ? kd[1] : kd[3], 32);
+        float sc = (up1 ? keep1 : keep0) + shfl_xor_f(up1 ? keep0 : keep1, 16);
+        sc = (base + lane < kv_hi) ? sc * p.scale_log2 : kNegInf;
+
+        const float m_new = fmaxf(m, wave_max(sc));  // finite: key `base` is visible
+        const float alpha = exp2f(m - m_new);
+        const float pr = exp2f(sc - m_new);
+        lsum = lsum * alpha + pr;
+        m = m_new;
+#pragma unroll
+        for (int k = 0; k < NIV; ++k) acc[k] *= alpha;
+
+        lds_p[wv][lane] = pr;
+        wave_lds_sync();
+        const bool tail = base + 64 > kv_hi;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (base + kBlock * j < kv_hi) {
+            float pk[X];
+#pragma unroll
+            for (int e = 0; e < X; e += 4) {
+              const f32x4 v4 = *reinterpret_cast<const f32x4*>(&lds_p[wv][kBlock * j + (lane % LPR) * X + e]);
+              pk[e] = v4[0]; pk[e + 1] = v4[1]; pk[e + 2] = v4[2]; pk[e + 3] = v4[3];
+            }
+            // keys past the context may hold anything (even NaN): drop them, not just weight 0
+            const int nvis = kv_hi - (base + kBlock * j + (lane % LPR) * X);
+#pragma unroll
+            for (int k = 0; k < NIV; ++k) {
+              float a = acc[k];
+#pragma unroll
+              for (int e = 0; e < X; ++e) {
+                float v;
+                if constexpr (kBf16) v = (e & 1) ? bf16_hi(vr[j][k][e >> 1]) : bf16_lo(vr[j][k][e >> 1]);
+                else v = __uint_as_float(vr[j][k][e]);
+                if (tail && e >= nvis) v = 0.f;
+                a = fmaf(pk[e], v, a);
+              }
+              acc[k] = a;
+            }
+          }
+        }
+        wave_lds_sync();
+      }
+    }
+    // finish: l over all lanes, each value column over its LPR lanes
+    const float l = wave_sum(lsum);
+#pragma unroll
+    for (int k = 0; k < NIV; ++k) {
+      acc[k] += shfl_xor_f(acc[k], 1);
+      if constexpr (LPR == 4) acc[k] += shfl_xor_f(acc[k], 2);
+    }
+    if (w.nparts == 1) {
+      if (lane % LPR == 0) {
+        T* orow = (T*)p.out + ((int64_t)t * p.Hq + h) * D;
+#pragma unroll
+        for (int k = 0; k < NIV; ++k) orow[RPI * k + lane / LPR] = Elem<T>::from_f32(acc[k] / l);
+      }
+    } else {
+      float* slot = p.partials + (((int64_t)t * p.Hq + h) * p.maxparts + pidx) * slot_floats(D);
+      if (lane % LPR == 0) {
+#pragma unroll
+        for (int k = 0; k < NIV; ++k) slot[RPI * k + lane / LPR] = acc[k];
+      }
+      if (lane == 0) {
+        slot[D] = m;
+        slot[D + 1] = l;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- MFMA worker
+// One wavefront per item: 16 query rows sharing one KV head x one key
+// partition, 32 keys (two pages) per step on v_mfma_f32_16x16x32_bf16.
+//  Scores, transposed: Sᵀ[key][row] = K · Qᵀ with K as the A operand (lane l:
+//  key l%16 of the page, 8 head dims per lane, straight from the key page)
+//  and Q as the B operand (lane l: row l%16).  The result gives lane l the
+//  scores of row l%16 for keys 4(l/16)..+3 of each page.
+//  Output, transposed: Oᵀ[dim][row] += Vᵀ · Pᵀ with the value page [D][16]
+//  as the A operand (lane l: dim l%16 + 16j, the same 8 keys the lane holds
+//  scores for) and Pᵀ (bf16) as the B operand.  Row statistics therefore stay
+//  in the lane that owns the row; a row max needs two exchanges (±16, ±32).
+//  P enters as a bf16 hi part plus a bf16 lo part (two MFMAs), and the
+//  running sum adds exactly those parts, so the result stays a convex
+//  combination of the value rows with weights accurate to ~2^-16.
+template <int D>
+__global__ __launch_bounds__(256) void mfma_attn_kernel(AttnParams p) {
+  constexpr int KS = D / 32;  // k-steps of the score product
+  constexpr int NJ = D / 16;  // 16-dim column blocks of the output
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g4 = lane >> 4;
+  const int total = p.ctrl[3];
+  const bf16_t* __restrict__ kc = (const bf16_t*)p.k_cache;
+  const bf16_t* __restrict__ vc = (const bf16_t*)p.v_cache;
+  const int64_t page_elems = (int64_t)kBlock * D;
+
+  for (;;) {
+    const int item = next_item(&p.ctrl[1], lane);
+    if (item >= total) break;
+    const int s = find_seq(p.pre_m, p.num_seqs, item);
+    const int local = item - p.pre_m[s];
+    const SeqInfo si = read_seq(p, s);
+    const SeqWork w = seq_work(false, p.G, p.Hq, p.Hkv, si.q_len, si.L);
+    const int pidx = local % w.nparts;
+    const int rest = local / w.nparts;
+    const int kvh = rest % p.Hkv;
+    const int tile = rest / p.Hkv;
+    const int rows_total = si.q_len * p.G;
+    const int R = tile * kTileRows + r;
+    const bool valid_row = R < rows_total;
+    const int qi = R / p.G;
+    const int hh = kvh * p.G + R % p.G;
+    const int t = si.a + qi;
+    const int pos_r = valid_row ? si.L - si.q_len + qi : -1;
+    const int last_row = min(tile * kTileRows + kTileRows - 1, rows_total - 1);
+    const int tile_pos_max = si.L - si.q_len + last_row / p.G;
+    const int kv_lo = pidx * w.part;
+    const int kv_hi = min(kv_lo + w.part, tile_pos_max + 1);
+
+    float m_r = kNegInf, lsum = 0.f;
+    f32x4 oacc[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    if (kv_lo < kv_hi) {
+      int bidv;
+      const int nblk = (kv_hi - kv_lo + kBlock - 1) / kBlock;
+      if (!load_block_ids(p, s, kv_lo / kBlock, nblk, lane, bidv)) continue;
+
+      bf16x8 qop[KS];
+      {
+        const bf16_t* qrow = (const bf16_t*)p.q + ((int64_t)t * p.Hq + hh) * D;
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+          qop[k] = __builtin_bit_cast(bf16x8, valid_row ? ld16(qrow + 32 * k + 8 * g4) : u32x4{0, 0, 0, 0});
+      }
+
+      for (int base = kv_lo; base < kv_hi; base += 32) {
+        const int jb = (base - kv_lo) >> 4;
+        const bool has1 = base + kBlock < kv_hi;
+        const int bid0 = readlane(bidv, jb);
+        const int bid1 = has1 ? readlane(bidv, jb + 1) : bid0;
+        const int64_t pg0 = ((int64_t)bid0 * p.Hkv + kvh) * page_elems;
+        const int64_t pg1 = ((int64_t)bid1 * p.Hkv + kvh) * page_elems;
+        bf16x8 kop0[KS], kop1[KS];
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          const int off = ((4 * k + g4) * kBlock + r) * 8;
+          kop0[k] = __builtin_bit_cast(bf16x8, ld16(kc + pg0 + off));
+          kop1[k] = __builtin_bit_cast(bf16x8, has1 ? ld16(kc + pg1 + off) : u32x4{0, 0, 0, 0});
+        }
+        uint32_t vw[NJ][4];  // value operand words: keys 4*g4 + 0..3 of page 0, then of page 1
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int off = (16 * j + r) * kBlock + 4 * g4;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vc + pg0 + off);
+          const u32x2 hi = has1 ? *reinterpret_cast<const u32x2*>(vc + pg1 + off) : u32x2{0, 0};
+          vw[j][0] = lo[0];
+          vw[j][1] = lo[1];
+          vw[j][2] = hi[0];
+          vw[j][3] = hi[1];
+        }
+        f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+          c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop0[k], qop[k], c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop1[k], qop[k], c1, 0, 0, 0);
+        }
+        // scores of row r for keys base + 16a + 4*g4 + e
+        float sc[8];
+        float mloc = kNegInf;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = base + (e >> 2) * kBlock + 4 * g4 + (e & 3);
+          const float v = (e >> 2) ? c1[e & 3] : c0[e & 3];
+          sc[e] = (key < kv_hi && key <= pos_r) ? v * p.scale_log2 : kNegInf;
+          mloc = fmaxf(mloc, sc[e]);
+        }
+        mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
+        mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
+        const float m_new = fmaxf(m_r, mloc);
+        const bool none = m_new == kNegInf;  // the row sees no key yet
+        const float alpha = none ? 1.f : exp2f(m_r - m_new);
+        // P enters the product as hi + lo bfloat16 parts (two MFMAs), so each
+        // weight keeps about 16 mantissa bits instead of 8.
+        uint32_t phw[4], plw[4];
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const float p0 = none ? 0.f : exp2f(sc[e] - m_new);
+          const float p1 = none ? 0.f : exp2f(sc[e + 1] - m_new);
+          const bf16_t h0 = Elem<bf16_t>::from_f32(p0), h1 = Elem<bf16_t>::from_f32(p1);
+          const float r0 = p0 - Elem<bf16_t>::to_f32(h0), r1 = p1 - Elem<bf16_t>::to_f32(h1);
+          const bf16_t l0 = Elem<bf16_t>::from_f32(r0), l1 = Elem<bf16_t>::from_f32(r1);
+          psum += (Elem<bf16_t>::to_f32(h0) + Elem<bf16_t>::to_f32(l0)) +
+                  (Elem<bf16_t>::to_f32(h1) + Elem<bf16_t>::to_f32(l1));
+          phw[e >> 1] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          plw[e >> 1] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+        }
+        lsum = lsum * alpha + psum;
+        m_r = m_new;
+        const bf16x8 pop_hi = __builtin_bit_cast(bf16x8, u32x4{phw[0], phw[1], phw[2], phw[3]});
+        const bf16x8 pop_lo = __builtin_bit_cast(bf16x8, u32x4{plw[0], plw[1], plw[2], plw[3]});
+        if (base + 32 > kv_hi) {
+          // keys past kv_hi may hold anything (even NaN): zero them in the value operand
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int key = base + (e >> 2) * kBlock + 4 * g4 + (e & 3);
+              if (key >= kv_hi) vw[j][e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          oacc[j] *= alpha;
+          const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{vw[j][0], vw[j][1], vw[j][2], vw[j][3]});
+          oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_hi, oacc[j], 0, 0, 0);
+          oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo, oacc[j], 0, 0, 0);
+        }
+      }
+    }
+    float l = lsum + shfl_xor_f(lsum, 16);
+    l += shfl_xor_f(l, 32);
+    if (valid_row) {
+      if (w.nparts == 1) {
+        bf16_t* orow = (bf16_t*)p.out + ((int64_t)t * p.Hq + hh) * D;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          u32x2 pk;
+          pk[0] = (uint32_t)Elem<bf16_t>::from_f32(oacc[j][0] / l) |
+                  ((uint32_t)Elem<bf16_t>::from_f32(oacc[j][1] / l) << 16);
+          pk[1] = (uint32_t)Elem<bf16_t>::from_f32(oacc[j][2] / l) |
+                  ((uint32_t)Elem<bf16_t>::from_f32(oacc[j][3] / l) << 16);
+          *reinterpret_cast<u32x2*>(orow + 16 * j + 4 * g4) = pk;
+        }
+      } else {
+        float* slot = p.partials + (((int64_t)t * p.Hq + hh) * p.maxparts + pidx) * slot_floats(D);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) *reinterpret_cast<f32x4*>(slot + 16 * j + 4 * g4) = oacc[j];
+        if (g4 == 0) {
+          slot[D] = m_r;
+          slot[D + 1] = l;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- merge
+// One wavefront per (query token, query head) whose context was split.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
+  const int lane = threadIdx.x & 63;
+  const int rh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rh >= p.T * p.Hq) return;
+  const int t = rh / p.Hq, h = rh % p.Hq;
+  const int s = find_seq(p.qsl, p.num_seqs, t);
+  const SeqInfo si = read_seq(p, s);
+  if (!si.ok || t < si.a || t >= si.a + si.q_len) return;
+  const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L);
+  if (w.nparts <= 1) return;
+  const int pos = si.L - si.q_len + (t - si.a);
+  const int np = min(w.nparts, pos / w.part + 1);  // later partitions hold no visible key
+  const float* base = p.partials + ((int64_t)t * p.Hq + h) * p.maxparts * slot_floats(D);
+  float M = kNegInf;
+  for (int q = lane; q < np; q += 64) M = fmaxf(M, base[(int64_t)q * slot_floats(D) + D]);
+  M = wave_max(M);
+  float lsum = 0.f;
+  for (int q = lane; q < np; q += 64) {
+    const float mq = base[(int64_t)q * slot_floats(D) + D];
+    const float lq = base[(int64_t)q * slot_floats(D) + D + 1];
+    lsum += mq == kNegInf ? 0.f : lq * exp2f(mq - M);
+  }
+  const float l = wave_sum(lsum);
+  constexpr int PER = D / 64;
+  float o[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) o[k] = 0.f;
+  for (int q = 0; q < np; ++q) {
+    const float* sl = base + (int64_t)q * slot_floats(D);
+    const float mq = sl[D];
+    if (mq == kNegInf) continue;
+    const float wq = exp2f(mq - M);
+#pragma unroll
+    for (int k = 0; k < PER; ++k) o[k] = fmaf(sl[lane + 64 * k], wq, o[k]);
+  }
+  T* orow = (T*)p.out + ((int64_t)t * p.Hq + h) * D;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) orow[lane + 64 * k] = Elem<T>::from_f32(o[k] / l);
+}
+
+// ---------------------------------------------------------------- host side
+struct WsLayout {
+  size_t ctrl, pre_v, pre_m, partials, total;
+  int maxparts;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(int S, int T, int Hq, int Hkv, int D, int max_ctx, bool is_f32) {
+  WsLayout l;
+  const int G = Hq / Hkv;
+  const int part = min_part(is_f32, G);
+  l.maxparts = max(1, (max_ctx + part - 1) / part);
+  l.ctrl = 0;
+  l.pre_v = 256;
+  l.pre_m = l.pre_v + align256((size_t)(S + 1) * 4);
+  l.partials = l.pre_m + align256((size_t)(S + 1) * 4);
+  const size_t part_bytes = l.maxparts > 1 ? (size_t)T * Hq * l.maxparts * slot_floats(D) * 4 : 0;
+  l.total = l.partials + align256(part_bytes);
+  return l;
+}
+
+template <typename T, int D>
+void launch_attention(const AttnParams& p, bool may_valu, bool may_mfma, int grid_v, int grid_m,
+                      hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, p);
+  if (may_valu)
+    hipLaunchKernelGGL((valu_attn_kernel<T, D>), dim3(grid_v), dim3(256), 0, stream, p);
+  if constexpr (sizeof(T) == 2) {
+    if (may_mfma) hipLaunchKernelGGL((mfma_attn_kernel<D>), dim3(grid_m), dim3(256), 0, stream, p);
+  }
+  if (p.maxparts > 1) {
+    const int64_t rows = (int64_t)p.T * p.Hq;
+    hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
+  }
+}
+
+}  // namespace
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" size_t pa_forward_workspace_bytes(int32_t num_seqs, int32_t total_q_tokens,
+                                             int32_t max_q_len, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t max_context_len, pa_dtype dtype) {
+  (void)max_q_len;
+  if (num_seqs < 0 || total_q_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads)
+    return 0;
+  return ws_layout(num_seqs, total_q_tokens, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                   dtype == PA_F32)
+      .total;
+}
+
+extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, const int32_t* query_start_loc,
+                                int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                                int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                float scale, pa_dtype dtype, void* workspace,
+                                size_t workspace_bytes, int32_t* dev_status, void* stream) {
+  const char* fn = "pa_forward";
+  if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
+  if (block_size != kBlock)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only 16 is supported)", fn, block_size);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128 supported)", fn, head_dim);
+  // float32 attention is built for head_dim 64 only: its head_dim-128 variant
+  // needed more registers than a wavefront can hold without spilling, and it
+  // is switched off until that variant is reworked.
+  if (dtype == PA_F32 && head_dim != 64)
+    return fail(PA_ERR_UNSUPPORTED, "%s: float32 attention supports head_dim 64 only", fn);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
+    return fail(PA_ERR_INVALID, "%s: %d query heads are not a multiple of %d KV heads", fn,
+                num_q_heads, num_kv_heads);
+  if (num_seqs < 0 || total_q_tokens < 0 || max_q_len < 0 || max_context_len < 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID, "%s: negative size or empty pool", fn);
+  if (max_q_len > max_context_len || max_q_len > total_q_tokens)
+    return fail(PA_ERR_INVALID, "%s: max_q_len %d exceeds max_context_len %d or total_q_tokens %d",
+                fn, max_q_len, max_context_len, total_q_tokens);
+  if ((int64_t)max_blocks_per_seq * kBlock < max_context_len || max_blocks_per_seq < 0)
+    return fail(PA_ERR_INVALID, "%s: max_blocks_per_seq %d cannot hold %d tokens", fn,
+                max_blocks_per_seq, max_context_len);
+  if (!std::isfinite(scale)) return fail(PA_ERR_INVALID, "%s: scale is not finite", fn);
+  if ((int64_t)total_q_tokens * num_q_heads > INT32_MAX / 2)
+    return fail(PA_ERR_INVALID, "%s: batch too large", fn);
+  if (num_seqs == 0 || total_q_tokens == 0) return ok();
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start_loc ||
+      !workspace)
+    return fail(PA_ERR_INVALID, "%s: NULL device pointer", fn);
+  if ((uintptr_t)workspace % 256) return fail(PA_ERR_INVALID, "%s: workspace not 256-byte aligned", fn);
+  const bool is_f32 = dtype == PA_F32;
+  const WsLayout wl = ws_layout(num_seqs, total_q_tokens, num_q_heads, num_kv_heads, head_dim,
+                                max_context_len, is_f32);
+  if (workspace_bytes < wl.total)
+    return fail(PA_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, wl.total);
+
+  AttnParams p{};
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  p.qsl = query_start_loc;
+  p.mbps = max_blocks_per_seq;
+  p.num_seqs = num_seqs;
+  p.T = total_q_tokens;
+  p.max_q_len = max_q_len;
+  p.max_ctx = max_context_len;
+  p.Hq = num_q_heads;
+  p.Hkv = num_kv_heads;
+  p.G = num_q_heads / num_kv_heads;
+  p.num_blocks = num_blocks;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.is_f32 = is_f32;
+  char* ws = (char*)workspace;
+  p.ctrl = (int32_t*)(ws + wl.ctrl);
+  p.pre_v = (int32_t*)(ws + wl.pre_v);
+  p.pre_m = (int32_t*)(ws + wl.pre_m);
+  p.partials = (float*)(ws + wl.partials);
+  p.maxparts = wl.maxparts;
+  p.dev_status = dev_status;
+
+  // Which worker classes can receive items (decided from host-known bounds only).
+  const bool may_valu = is_f32 || p.G == 1;
+  const bool may_mfma = !is_f32 && (p.G > 1 || max_q_len > 1);
+  const int64_t bound_v = (int64_t)total_q_tokens * num_q_heads * wl.maxparts;
+  const int64_t bound_m =
+      ((int64_t)total_q_tokens * p.G / kTileRows + num_seqs) * num_kv_heads * wl.maxparts;
+  const int grid_v = (int)std::min<int64_t>(kMaxWorkerGroups, (bound_v + 3) / 4);
+  const int grid_m = (int)std::min<int64_t>(kMaxWorkerGroups, (bound_m + 3) / 4);
+
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (is_f32) {
+    launch_attention<float, 64>(p, may_valu, false, grid_v, grid_m, s);
+  } else {
+    if (head_dim == 64) launch_attention<bf16_t, 64>(p, may_valu, may_mfma, grid_v, grid_m, s);
+    else launch_attention<bf16_t, 128>(p, may_valu, may_mfma, grid_v, grid_m, s);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}

@@ -1,0 +1,147 @@
+// Cache write through a slot mapping and copy-on-write page copies (gfx950).
+//
+// Both are pure data movement: exact byte copies, no arithmetic on values.
+#include "pa_device.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+// One workgroup per new token.  The token's key row is stored as head_dim/X
+// runs of 16 bytes (one per X-element group, 256 bytes apart inside the
+// page), its value row as one element per value column (32 or 64 bytes apart).
+template <typename T, int D>
+__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+    const T* __restrict__ key, const T* __restrict__ value, T* __restrict__ k_cache,
+    T* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int32_t num_blocks,
+    int32_t num_kv_heads, int32_t* dev_status) {
+  constexpr int X = Elem<T>::X;
+  constexpr int NCH = D / X;
+  const int t = blockIdx.x;
+  const int64_t slot = slot_mapping[t];
+  if (slot < 0) return;
+  if (slot >= (int64_t)num_blocks * kBlock) {
+    if (threadIdx.x == 0) flag_status(dev_status, PA_DEV_BAD_SLOT);
+    return;
+  }
+  const int64_t b = slot / kBlock;
+  const int o = (int)(slot % kBlock);
+  const int nq = num_kv_heads * NCH;
+  for (int qi = threadIdx.x; qi < nq; qi += blockDim.x) {
+    const int h = qi / NCH, c = qi % NCH;
+    const int64_t src = ((int64_t)t * num_kv_heads + h) * D + c * X;
+    const int64_t page = (b * num_kv_heads + h) * (int64_t)(kBlock * D);
+    // key: 16-byte run c of token o
+    st16(k_cache + page + ((int64_t)c * kBlock + o) * X, ld16(key + src));
+    // value: X consecutive columns of token o
+    union {
+      u32x4 v;
+      T e[X];
+    } u;
+    u.v = ld16(value + src);
+#pragma unroll
+    for (int x = 0; x < X; ++x) v_cache[page + (int64_t)(c * X + x) * kBlock + o] = u.e[x];
+  }
+}
+
+// grid (num_pairs, slices): each workgroup copies one 4 KiB slice of the key
+// page and of the value page of one (src, dst) pair.
+__global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ k_cache,
+                                                          uint8_t* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ pairs,
+                                                          int32_t num_blocks, int64_t page_bytes,
+                                                          int32_t* dev_status) {
+  const int i = blockIdx.x;
+  const int32_t src = pairs[2 * i], dst = pairs[2 * i + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) {
+    if (threadIdx.x == 0 && blockIdx.y == 0) flag_status(dev_status, PA_DEV_BAD_BLOCK);
+    return;
+  }
+  const int64_t off = (int64_t)blockIdx.y * 4096 + (int64_t)threadIdx.x * 16;
+  if (off >= page_bytes) return;
+  const int64_t s = (int64_t)src * page_bytes + off, d = (int64_t)dst * page_bytes + off;
+  st16(k_cache + d, ld16(k_cache + s));
+  st16(v_cache + d, ld16(v_cache + s));
+}
+
+pa_status check_pool_args(const char* fn, int32_t num_blocks, int32_t num_kv_heads,
+                          int32_t head_dim, int32_t block_size, pa_dtype dtype) {
+  if (num_blocks <= 0 || num_kv_heads <= 0)
+    return fail(PA_ERR_INVALID, "%s: num_blocks %d and num_kv_heads %d must be > 0", fn,
+                num_blocks, num_kv_heads);
+  if (block_size != kBlock)
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only 16 is supported)", fn, block_size);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128 supported)", fn, head_dim);
+  if (dtype != PA_F32 && dtype != PA_BF16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
+  return PA_OK;
+}
+
+template <typename T, int D>
+void launch_reshape(const void* key, const void* value, void* k_cache, void* v_cache,
+                    const int64_t* slots, int32_t T_, int32_t nb, int32_t hkv, int32_t* st,
+                    hipStream_t stream) {
+  hipLaunchKernelGGL((reshape_and_cache_kernel<T, D>), dim3(T_), dim3(256), 0, stream,
+                     (const T*)key, (const T*)value, (T*)k_cache, (T*)v_cache, slots, nb, hkv, st);
+}
+
+}  // namespace
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache,
+                                          void* v_cache, const int64_t* slot_mapping,
+                                          int32_t num_tokens, int32_t num_blocks,
+                                          int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, pa_dtype dtype, int32_t* dev_status,
+                                          void* stream) {
+  const char* fn = "pa_reshape_and_cache";
+  pa_status st = check_pool_args(fn, num_blocks, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return fail(PA_ERR_INVALID, "%s: negative num_tokens", fn);
+  if (num_tokens == 0) return ok();
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping)
+    return fail(PA_ERR_INVALID, "%s: NULL device pointer", fn);
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+  if (dtype == PA_F32) {
+    if (head_dim == 64)
+      launch_reshape<float, 64>(key, value, k_cache, v_cache, slot_mapping, num_tokens, num_blocks, num_kv_heads, dev_status, s);
+    else
+      launch_reshape<float, 128>(key, value, k_cache, v_cache, slot_mapping, num_tokens, num_blocks, num_kv_heads, dev_status, s);
+  } else {
+    if (head_dim == 64)
+      launch_reshape<bf16_t, 64>(key, value, k_cache, v_cache, slot_mapping, num_tokens, num_blocks, num_kv_heads, dev_status, s);
+    else
+      launch_reshape<bf16_t, 128>(key, value, k_cache, v_cache, slot_mapping, num_tokens, num_blocks, num_kv_heads, dev_status, s);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* block_pairs,
+                                    int32_t num_pairs, int32_t num_blocks, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t block_size, pa_dtype dtype,
+                                    int32_t* dev_status, void* stream) {
+  const char* fn = "pa_copy_blocks";
+  pa_status st = check_pool_args(fn, num_blocks, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return fail(PA_ERR_INVALID, "%s: negative num_pairs", fn);
+  if (num_pairs == 0) return ok();
+  if (!k_cache || !v_cache || !block_pairs) return fail(PA_ERR_INVALID, "%s: NULL device pointer", fn);
+  if (num_pairs > 65535 * 64) return fail(PA_ERR_INVALID, "%s: too many pairs", fn);
+  const int64_t page_bytes =
+      (int64_t)num_kv_heads * kBlock * head_dim * (dtype == PA_F32 ? 4 : 2);
+  const int slices = (int)((page_bytes + 4095) / 4096);
+  if (slices > 65535) return fail(PA_ERR_INVALID, "%s: page too large", fn);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(num_pairs, slices), dim3(256), 0, (hipStream_t)stream,
+                     (uint8_t*)k_cache, (uint8_t*)v_cache, block_pairs, num_blocks, page_bytes,
+                     dev_status);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}

@@ -1,0 +1,89 @@
+// Device-side types and helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/pa.h"
+
+namespace pa {
+
+constexpr int kBlock = 16;  // tokens per page
+constexpr int kWave = 64;   // CDNA wavefront width
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+typedef uint16_t bf16_t;  // storage type of one bfloat16
+
+// Element traits: storage type, 16-byte group width X, load/convert helpers.
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+  static constexpr int X = 4;  // elements per 16 bytes
+  __device__ static inline float to_f32(float v) { return v; }
+  __device__ static inline float from_f32(float v) { return v; }
+};
+
+template <>
+struct Elem<bf16_t> {
+  static constexpr int X = 8;
+  __device__ static inline float to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+  // Round to nearest even (NaN stays NaN).
+  __device__ static inline bf16_t from_f32(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+  }
+};
+
+// Low / high bfloat16 of a packed pair, widened to float32 (exact).
+__device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// a.lo*b.lo + a.hi*b.hi + c on two packed bfloat16 pairs (v_dot2_f32_bf16).
+// The pairs arrive as 32-bit words copied into locals: a bit cast applied
+// directly to an element of a vector-typed value reinterprets the vector's
+// first word instead of the element, so only plain scalars are cast here.
+__device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  const uint32_t ua = a, ub = b;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ua), __builtin_bit_cast(bf16x2, ub), c,
+                                         false);
+}
+
+__device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ inline void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+template <typename T>
+__device__ inline T readlane(T v, int lane) {
+  return __builtin_amdgcn_readlane(v, lane);
+}
+
+__device__ inline float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ inline float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// Scalar broadcast of lane 0's value (the compiler keeps the result uniform).
+__device__ inline int first_lane(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ inline void flag_status(int32_t* dev_status, int bits) {
+  if (dev_status) atomicOr(dev_status, bits);
+}
+
+}  // namespace pa

@@ -1,0 +1,137 @@
+// CPU stand-in for <hip/hip_runtime.h> used only by the kernel emulator in
+// tests/emu.  It lets the library's own kernel sources compile for x86 and run
+// every lane of a wavefront as a host thread, so that address errors show up
+// under AddressSanitizer on the CPU instead of as GPU memory faults.
+//
+// Cross-lane operations (shuffles, readlane, ballot, MFMA) exchange values
+// through per-wavefront barriers; __shared__ variables become statics, which
+// is correct because workgroups run one at a time.
+#pragma once
+
+#include <cmath>
+#include <cstddef>
+#include <cstdint>
+#include <cstring>
+#include <algorithm>
+
+struct dim3 {
+  unsigned x, y, z;
+  constexpr dim3(unsigned a = 1, unsigned b = 1, unsigned c = 1) : x(a), y(b), z(c) {}
+};
+
+typedef struct emu_stream* hipStream_t;
+typedef int hipError_t;
+constexpr hipError_t hipSuccess = 0;
+inline hipError_t hipGetLastError() { return hipSuccess; }
+inline const char* hipGetErrorString(hipError_t) { return "emulated"; }
+
+#define __global__
+#define __device__
+#define __host__
+#define __shared__ static
+#define __launch_bounds__(...)
+
+namespace emu {
+extern thread_local dim3 tl_threadIdx, tl_blockIdx, tl_blockDim, tl_gridDim;
+extern thread_local int tl_lane;
+
+void wave_sync();
+void block_sync();
+uint64_t exchange(uint64_t mine, int src_lane);          // value of src_lane
+uint64_t ballot(bool pred);
+void mfma_16x16x32_bf16(const uint16_t a[8], const uint16_t b[8], const float c[4], float d[4]);
+void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* ctx);
+
+template <typename T>
+inline uint64_t to_bits(T v) {
+  static_assert(sizeof(T) <= 8, "lane values are at most 64 bits");
+  uint64_t u = 0;
+  std::memcpy(&u, &v, sizeof(T));
+  return u;
+}
+template <typename T>
+inline T from_bits(uint64_t u) {
+  T v;
+  std::memcpy(&v, &u, sizeof(T));
+  return v;
+}
+
+template <typename K, typename... A>
+struct Launch {
+  K k;
+  std::tuple<A...> args;
+  static void body(void* p) {
+    auto* self = static_cast<Launch*>(p);
+    std::apply(self->k, self->args);
+  }
+};
+
+template <typename K, typename... A>
+void launch(K k, dim3 g, dim3 b, A... args) {
+  Launch<K, A...> l{k, std::tuple<A...>(args...)};
+  run_grid(g, b, &Launch<K, A...>::body, &l);
+}
+}  // namespace emu
+
+#include <tuple>
+
+#define threadIdx (emu::tl_threadIdx)
+#define blockIdx (emu::tl_blockIdx)
+#define blockDim (emu::tl_blockDim)
+#define gridDim (emu::tl_gridDim)
+
+#define hipLaunchKernelGGL(kernel, grid, block, shmem, stream, ...) \
+  emu::launch(kernel, dim3(grid), dim3(block), __VA_ARGS__)
+
+using std::max;
+using std::min;
+
+inline float __uint_as_float(uint32_t u) { return emu::from_bits<float>(u); }
+inline uint32_t __float_as_uint(float f) { return (uint32_t)emu::to_bits(f); }
+
+inline void __syncthreads() { emu::block_sync(); }
+
+template <typename T>
+inline T __shfl_xor(T v, int mask, int width = 64) {
+  (void)width;
+  return emu::from_bits<T>(emu::exchange(emu::to_bits(v), emu::tl_lane ^ mask));
+}
+
+inline int atomicAdd(int* p, int v) { return __atomic_fetch_add(p, v, __ATOMIC_SEQ_CST); }
+inline int atomicOr(int* p, int v) { return __atomic_fetch_or(p, v, __ATOMIC_SEQ_CST); }
+
+template <typename T>
+inline T emu_readlane(T v, int lane) {
+  return emu::from_bits<T>(emu::exchange(emu::to_bits(v), lane));
+}
+template <typename T>
+inline T emu_readfirstlane(T v) {
+  return emu_readlane(v, 0);
+}
+inline uint64_t emu_ballot(bool p) { return emu::ballot(p); }
+
+template <typename V2>
+inline float emu_fdot2(V2 a, V2 b, float c, bool) {
+  return (float)a[0] * (float)b[0] + (float)a[1] * (float)b[1] + c;
+}
+
+template <typename V8, typename F4>
+inline F4 emu_mfma(V8 a, V8 b, F4 c, int, int, int) {
+  uint16_t ua[8], ub[8];
+  float fc[4], fd[4];
+  std::memcpy(ua, &a, 16);
+  std::memcpy(ub, &b, 16);
+  for (int i = 0; i < 4; ++i) fc[i] = c[i];
+  emu::mfma_16x16x32_bf16(ua, ub, fc, fd);
+  F4 d;
+  for (int i = 0; i < 4; ++i) d[i] = fd[i];
+  return d;
+}
+
+#define __builtin_amdgcn_readlane(v, l) emu_readlane((v), (l))
+#define __builtin_amdgcn_readfirstlane(v) emu_readfirstlane((v))
+#define __builtin_amdgcn_ballot_w64(p) emu_ballot((p))
+#define __builtin_amdgcn_fdot2_f32_bf16(a, b, c, cl) emu_fdot2((a), (b), (c), (cl))
+#define __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, x, y, z) emu_mfma((a), (b), (c), (x), (y), (z))
+#define __builtin_amdgcn_fence(...) ((void)0)
+#define __builtin_amdgcn_wave_barrier() emu::wave_sync()

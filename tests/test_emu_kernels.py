@@ -1,0 +1,116 @@
+"""The library's kernel sources run on the CPU (tests/emu) under AddressSanitizer/UBSan.
+
+Every lane of a wavefront is a host thread; any out-of-bounds access in a
+kernel aborts the emulator with the source line.  Results are compared with
+the fp64 oracle at the same tolerances as the GPU parity tests, so both the
+memory safety and the arithmetic of each kernel are checked before a kernel
+ever reaches the GPU.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from oracle import attention as oattn
+from oracle import cache_ops, layout
+from tests import _emu
+from tests._pools import empty_pools, raw
+from tests.test_gpu_parity import FAULTED, RAGGED
+
+pytestmark = pytest.mark.skipif(not _emu.available(), reason="needs the ROCm clang++ for the host build")
+TOL = {"bf16": (2e-3, 1e-2), "f32": (1e-5, 1e-5)}
+
+
+@pytest.fixture(scope="module")
+def emu():
+    _emu.build()
+    return _emu
+
+
+def check(w, q, kp, vp, out, label):
+    ref = oattn.paged_attention(q, kp, vp, w.block_tables, w.context_lens, w.query_start_loc, w.scale, w.dtype)
+    got = layout.to_f64(out, w.dtype)
+    a, r = TOL[w.dtype]
+    ratio = (np.abs(got - ref) / (a + r * np.abs(ref))).max()
+    assert np.isfinite(got).all() and ratio <= 1.0, f"{label}: worst err/bound {ratio:.3f}"
+    return ratio
+
+
+@pytest.mark.parametrize("i", [i for i in range(len(RAGGED)) if i not in FAULTED])
+def test_ragged_cases_match_oracle(emu, i):
+    dt, hq, hkv, d, ql, cl = RAGGED[i]
+    w = W.random_ragged(100 + i, dt, hq, hkv, d, ql, cl)
+    rng = np.random.default_rng(i)
+    kp, vp = empty_pools(rng, dt, w.num_blocks, hkv, d)
+    q = raw(rng.standard_normal((w.num_tokens, hq, d)).astype(np.float32), dt)
+    out, st = emu.forward(w, q, kp, vp)
+    assert st == 0
+    check(w, q, kp, vp, out, f"ragged[{i}]")
+
+
+def test_float32_head_dim_128_is_rejected(emu):
+    w = W.random_ragged(1, "f32", 4, 4, 128, [1], [20])
+    kp, vp = empty_pools(np.random.default_rng(0), "f32", w.num_blocks, 4, 128)
+    with pytest.raises(RuntimeError, match="head_dim 64 only"):
+        emu.forward(w, np.zeros((1, 4, 128), np.float32), kp, vp)
+
+
+def test_nan_outside_context_is_never_read(emu):
+    for dt, hq, hkv, d, ql, cl in [("bf16", 16, 4, 128, [1, 5, 1, 1], [37, 600, 1000, 1]),
+                                   ("bf16", 8, 8, 128, [1, 1, 20], [517, 33, 1025]),
+                                   ("f32", 4, 2, 64, [3, 1], [70, 19])]:
+        w = W.random_ragged(7, dt, hq, hkv, d, ql, cl)
+        rng = np.random.default_rng(3)
+        kp, vp = empty_pools(rng, dt, w.num_blocks, hkv, d)
+        nan = np.float32("nan") if dt == "f32" else np.uint16(0x7FC0)
+        used = np.zeros(w.num_blocks, bool)
+        for s, L in enumerate(w.context_lens):
+            n = (int(L) + 15) // 16
+            used[w.block_tables[s, :n]] = True
+            if L % 16:
+                b = int(w.block_tables[s, n - 1])
+                kp[b, :, :, L % 16:, :] = nan
+                vp[b, :, :, L % 16:] = nan
+        kp[~used] = nan
+        vp[~used] = nan
+        q = raw(rng.standard_normal((w.num_tokens, hq, d)).astype(np.float32), dt)
+        out, st = emu.forward(w, q, kp, vp)
+        assert st == 0
+        check(w, q, kp, vp, out, f"nan-poison {dt}")
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("f32", 128), ("bf16", 64)])
+def test_reshape_and_cache_bit_exact(emu, dtype, d):
+    rng = np.random.default_rng(d)
+    nb, hkv, T = 19, 2, 150
+    run = np.arange(48, 80)
+    rest = np.setdiff1d(rng.permutation(nb * 16), run)
+    slots = np.concatenate([run, rng.permutation(rest)[:T - run.size]]).astype(np.int64)
+    slots[[3, 100]] = -1
+    kp, vp = empty_pools(rng, dtype, nb, hkv, d)
+    key = raw(rng.standard_normal((T, hkv, d)).astype(np.float32), dtype)
+    val = raw(rng.standard_normal((T, hkv, d)).astype(np.float32), dtype)
+    k1, v1, st = emu.reshape_and_cache(dtype, key, val, kp, vp, slots)
+    k2, v2 = cache_ops.reshape_and_cache(key, val, kp, vp, slots)
+    assert st == 0 and np.array_equal(k1, k2) and np.array_equal(v1, v2)
+
+
+def test_copy_blocks_bit_exact(emu):
+    kp, vp = empty_pools(np.random.default_rng(2), "bf16", 12, 8, 128)
+    pairs = [[3, 10], [3, 11], [7, 0]]
+    k1, v1, st = emu.copy_blocks("bf16", kp, vp, pairs)
+    k2, v2 = cache_ops.copy_blocks(kp, vp, pairs)
+    assert st == 0 and np.array_equal(k1, k2) and np.array_equal(v1, v2)
+
+
+def test_out_of_range_ids_are_flagged_and_skipped(emu):
+    kp, vp = empty_pools(np.random.default_rng(3), "f32", 4, 1, 64)
+    key = np.ones((2, 1, 64), np.float32)
+    k1, v1, st = emu.reshape_and_cache("f32", key, key, kp, vp, [3, 64])
+    assert st == 2 and np.array_equal(k1[1:], kp[1:])
+    k1, v1, st = emu.copy_blocks("f32", kp, vp, [[0, 1], [2, 4]])
+    assert st == 1
+    w = W.random_ragged(0, "f32", 2, 2, 64, [1], [20])
+    w.block_tables[0, 1] = w.num_blocks + 5
+    kp, vp = empty_pools(np.random.default_rng(4), "f32", w.num_blocks, 2, 64)
+    _, st = emu.forward(w, np.zeros((1, 2, 64), np.float32), kp, vp)
+    assert st == 1

@@ -1,0 +1,247 @@
+"""GPU parity of libpa against the fp64 CPU oracle (MI355X, through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from oracle import cache_ops
+from tests._gpu import DEV, Run, assert_close, check_tables_in_pool, host_raw, oracle_rows, say, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    import paged_kv_cache_57_amd as pa
+    assert torch.cuda.is_available()
+    return pa
+
+
+def run_and_check(pa, w, seqs=None, poison=False, label=None):
+    """Draw the workload's values, run (cache write +) forward, compare the listed sequences."""
+    label = label or w.name
+    say(f"[case] {label}: S={w.num_seqs} T={w.num_tokens} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+        f"d={w.head_dim} {w.dtype} NB={w.num_blocks} maxL={w.max_context_len}")
+    check_tables_in_pool(w)
+    r = Run(w)
+    q, kc, vc, nk, nv = W.make_values(w, DEV)
+    if poison:
+        poison_unreferenced(w, kc, vc)
+    if nk is not None:
+        r.write(nk, nv, kc, vc)
+    out = r.forward(q, kc, vc)
+    r.check_status()
+    seqs = range(w.num_seqs) if seqs is None else seqs
+    rows, ref = oracle_rows(w, q, kc, vc, seqs)
+    got = to_f64(out.index_select(0, torch.from_numpy(rows).to(DEV)))
+    assert np.isfinite(got).all()
+    assert_close(got, ref, w.dtype, label)
+    return out, (q, kc, vc), r
+
+
+def poison_unreferenced(w, kc, vc):
+    """NaN in every block no table references and in the unused tail slots of last blocks."""
+    used = np.zeros(w.num_blocks, bool)
+    for s, L in enumerate(w.context_lens):
+        n = (int(L) + 15) // 16
+        used[w.block_tables[s, :n]] = True
+        if L % 16:
+            b = int(w.block_tables[s, n - 1])
+            kc[b, :, :, L % 16:, :] = float("nan")
+            vc[b, :, :, L % 16:] = float("nan")
+    free = torch.from_numpy(np.flatnonzero(~used)).to(DEV)
+    if free.numel():
+        kc[free] = float("nan")
+        vc[free] = float("nan")
+
+
+# ---------------------------------------------------------------- cache write and copy
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128), ("bf16", 64), ("f32", 128)])
+def test_reshape_and_cache_bit_exact(pa, dtype, d):
+    say(f"[case] reshape_and_cache {dtype} d={d}")
+    rng = np.random.default_rng(d)
+    nb, hkv, T = 37, 3, 300
+    run = np.arange(160, 200)                                # a run of consecutive slots
+    rest = np.setdiff1d(rng.permutation(nb * 16), run)
+    slots = np.concatenate([run, rng.permutation(rest)[:T - run.size]]).astype(np.int64)
+    slots[[5, 77, 250]] = -1                                 # padding tokens
+    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    ks, vs = W.cache_shapes(nb, hkv, d, dtype)
+    g = torch.Generator(device=DEV).manual_seed(1)
+    kc = W.fill_normal(torch.empty(ks, dtype=td, device=DEV), g)
+    vc = W.fill_normal(torch.empty(vs, dtype=td, device=DEV), g)
+    key = W.fill_normal(torch.empty((T, hkv, d), dtype=td, device=DEV), g)
+    val = W.fill_normal(torch.empty((T, hkv, d), dtype=td, device=DEV), g)
+    k0, v0 = host_raw(kc), host_raw(vc)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pa.pa_reshape_and_cache(key, val, kc, vc, torch.from_numpy(slots).to(DEV), st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    k1, v1 = cache_ops.reshape_and_cache(host_raw(key), host_raw(val), k0, v0, slots)
+    assert np.array_equal(host_raw(kc).view(np.uint8), k1.view(np.uint8))
+    assert np.array_equal(host_raw(vc).view(np.uint8), v1.view(np.uint8))
+
+
+def test_copy_blocks_bit_exact(pa):
+    say("[case] copy_blocks bf16 d=128 Hkv=32")
+    nb, hkv, d = 24, 32, 128
+    ks, vs = W.cache_shapes(nb, hkv, d, "bf16")
+    g = torch.Generator(device=DEV).manual_seed(2)
+    kc = W.fill_normal(torch.empty(ks, dtype=torch.bfloat16, device=DEV), g)
+    vc = W.fill_normal(torch.empty(vs, dtype=torch.bfloat16, device=DEV), g)
+    pairs = np.array([[3, 10], [3, 11], [7, 0], [23, 12]], np.int32)
+    k0, v0 = host_raw(kc), host_raw(vc)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pa.pa_copy_blocks(kc, vc, torch.from_numpy(pairs).to(DEV), st)
+    torch.cuda.synchronize()
+    assert st.item() == 0
+    k1, v1 = cache_ops.copy_blocks(k0, v0, pairs)
+    assert np.array_equal(host_raw(kc), k1) and np.array_equal(host_raw(vc), v1)
+
+
+def test_out_of_range_ids_are_flagged_not_followed(pa):
+    # the kernels check ids before forming an address; the host sees the status bits
+    say("[case] out-of-range slot / pair / table entry")
+    nb, hkv, d = 4, 1, 64
+    ks, vs = W.cache_shapes(nb, hkv, d, "f32")
+    kc = torch.zeros(ks, device=DEV)
+    vc = torch.zeros(vs, device=DEV)
+    st = torch.zeros(1, dtype=torch.int32, device=DEV)
+    key = torch.ones((2, hkv, d), device=DEV)
+    pa.pa_reshape_and_cache(key, key, kc, vc, torch.tensor([3, nb * 16], device=DEV), st)
+    pa.pa_copy_blocks(kc, vc, torch.tensor([[0, 1], [2, nb]], dtype=torch.int32, device=DEV), st)
+    torch.cuda.synchronize()
+    assert st.item() == pa.PA_DEV_BAD_SLOT | pa.PA_DEV_BAD_BLOCK
+    w = W.random_ragged(0, "f32", 2, 2, 64, [1], [20])
+    w.block_tables[0, 1] = w.num_blocks + 5                 # second page points outside the pool
+    r = Run(w)
+    q, kc2, vc2, _, _ = W.make_values(w, DEV)
+    r.forward(q, kc2, vc2)
+    torch.cuda.synchronize()
+    assert r.status.item() == pa.PA_DEV_BAD_BLOCK
+
+
+# ---------------------------------------------------------------- attention parity
+
+def test_tiny_decode_fp32(pa):
+    run_and_check(pa, W.tiny_decode(0))
+
+
+# float32 with head_dim 128 faulted the GPU on its first run while every
+# address of that case checks out in the CPU emulator and in the generated
+# code; its kernel was the only one that spilled registers.  pa_forward
+# rejects that combination until the variant is reworked, and the case stays
+# off the GPU.
+FAULTED = {1: "faulted the GPU on its first run (float32, head_dim 128); that variant is switched off"}
+
+RAGGED = [
+    # dtype, Hq, Hkv, d, q_lens, ctx_lens
+    ("f32", 4, 4, 64, [1, 1, 1], [1, 16, 17]),
+    ("f32", 8, 2, 128, [1, 5, 1], [1300, 40, 513]),              # (switched off, see FAULTED)
+    ("f32", 8, 2, 64, [1, 5, 1], [1300, 40, 513]),               # VALU split contexts, GQA, fp32 prefill rows
+    ("bf16", 32, 32, 128, [1, 1, 1, 1], [1, 15, 513, 2049]),      # MHA decode, partitions + ragged tails
+    ("bf16", 8, 8, 64, [1, 1], [700, 33]),
+    ("bf16", 64, 8, 128, [1, 1, 1], [1, 255, 1000]),              # GQA decode, 256-key partitions
+    ("bf16", 16, 2, 64, [1, 1], [300, 17]),
+    ("bf16", 8, 8, 128, [37, 1, 16, 1], [37, 900, 1100, 2]),      # prefill tiles (prior 0 and 1084)
+    ("bf16", 16, 4, 128, [9, 3, 1], [2100, 3, 64]),               # GQA prefill: rows = positions x heads
+    ("bf16", 4, 4, 64, [70, 1], [1500, 5]),                       # prefill crossing partitions of 1024
+]
+
+
+@pytest.mark.parametrize("i", range(len(RAGGED)))
+def test_ragged_batches(pa, i):
+    if i in FAULTED:
+        pytest.skip(FAULTED[i])
+    dt, hq, hkv, d, ql, cl = RAGGED[i]
+    w = W.random_ragged(100 + i, dt, hq, hkv, d, ql, cl)
+    run_and_check(pa, w, label=f"ragged[{i}] {dt} Hq={hq} Hkv={hkv} d={d} q={ql} L={cl}")
+
+
+def test_nan_poison_outside_context(pa):
+    w = W.random_ragged(7, "bf16", 16, 4, 128, [1, 5, 1, 1], [37, 600, 1000, 1])
+    run_and_check(pa, w, poison=True, label="nan-poison GQA")
+    w = W.random_ragged(8, "bf16", 8, 8, 128, [1, 1, 20], [517, 33, 1025])
+    run_and_check(pa, w, poison=True, label="nan-poison MHA")
+
+
+def test_single_key_and_equal_scores(pa):
+    # one key: output is that value row exactly; q = 0: output is the mean of the values
+    for dt, hq, hkv, d in [("f32", 4, 4, 64), ("bf16", 32, 32, 128), ("bf16", 64, 8, 128)]:
+        say(f"[case] single key / equal scores {dt} Hq={hq} Hkv={hkv}")
+        w = W.random_ragged(9, dt, hq, hkv, d, [1, 1], [1, 1])
+        r = Run(w)
+        q, kc, vc, _, _ = W.make_values(w, DEV)
+        out = r.forward(q, kc, vc)
+        r.check_status()
+        for s in range(2):
+            b = int(w.block_tables[s, 0])
+            v = to_f64(vc[b, :, :, 0])                         # [Hkv, d]
+            got = to_f64(out[s]).reshape(hkv, hq // hkv, -1)
+            assert np.array_equal(got, np.repeat(v[:, None], hq // hkv, 1))
+    w = W.random_ragged(10, "bf16", 32, 32, 128, [1], [777])
+    r = Run(w)
+    q, kc, vc, _, _ = W.make_values(w, DEV)
+    q.zero_()
+    out = r.forward(q, kc, vc)
+    r.check_status()
+    rows, ref = oracle_rows(w, q, kc, vc, [0])
+    assert_close(to_f64(out), ref, "bf16", "q=0 mean of values")
+
+
+def test_block_permutation_gives_identical_bits(pa):
+    w = W.random_ragged(11, "bf16", 16, 2, 128, [1, 7, 1], [900, 300, 47])
+    say("[case] physical block permutation (bit-identical)")
+    r = Run(w)
+    q, kc, vc, _, _ = W.make_values(w, DEV)
+    base = r.forward(q, kc, vc).clone()
+    perm = np.random.default_rng(5).permutation(w.num_blocks)
+    kc2, vc2 = torch.empty_like(kc), torch.empty_like(vc)
+    pt = torch.from_numpy(perm).to(DEV)
+    kc2[pt] = kc
+    vc2[pt] = vc
+    w2 = W.Workload(**{**w.__dict__})
+    w2.block_tables = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    r2 = Run(w2)
+    out2 = r2.forward(q, kc2, vc2)
+    r2.check_status()
+    assert torch.equal(base.view(torch.int16), out2.view(torch.int16))
+
+
+def test_batch_invariance(pa):
+    # a sequence's output is bit-identical alone and inside a bigger batch
+    say("[case] batch invariance")
+    w = W.random_ragged(12, "bf16", 32, 32, 128, [1, 1, 1, 1], [2049, 100, 3000, 512])
+    r = Run(w)
+    q, kc, vc, _, _ = W.make_values(w, DEV)
+    full = r.forward(q, kc, vc).clone()
+    for s in range(w.num_seqs):
+        ws = W.Workload(**{**w.__dict__})
+        ws.context_lens = w.context_lens[s:s + 1].copy()
+        ws.block_tables = w.block_tables[s:s + 1].copy()
+        ws.query_start_loc = np.array([0, 1], np.int32)
+        rs = Run(ws)
+        one = rs.forward(q[s:s + 1].contiguous(), kc, vc)
+        rs.check_status()
+        assert torch.equal(one.view(torch.int16), full[s:s + 1].view(torch.int16)), s
+
+
+# ---------------------------------------------------------------- the benchmark workloads
+
+def test_llama7b_decode_batch64(pa):
+    run_and_check(pa, W.llama7b_decode(0), seqs=[0, 1, 2, 17, 31, 40, 63])
+
+
+def test_gqa70b_decode_batch32(pa):
+    run_and_check(pa, W.gqa70b_decode(0), seqs=[0, 5, 31])
+
+
+def test_gqa70b_decode_long_32k(pa):
+    run_and_check(pa, W.gqa70b_long_decode(0))
+
+
+def test_splitfuse_mixed_pass(pa):
+    # both prefill chunks (all 1024 rows) plus a spread of decode rows, after the cache write
+    w = W.splitfuse_mixed(0)
+    run_and_check(pa, w, seqs=[0, 1, 2, 3, 500, 1025])
