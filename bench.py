@@ -1,0 +1,287 @@
+#!/usr/bin/env python3
+"""Throughput of the paged-attention hot path on one MI355X.
+
+One step is one pass of the path over one batch of synthetic input, with all
+inputs resident in device memory before timing starts:
+
+* splitfuse (default): a Dynamic-SplitFuse forward — the cache write of all
+  2048 new tokens through their slots, then one paged-attention pass over two
+  causal 512-token prefill chunks (prior context uniform in [0, 8192]) and
+  1024 single-token decodes (context uniform in [128, 4096]); 32 heads of dim
+  128, bfloat16, 16-token pages.  value = query tokens per second.
+* llama7b / gqa70b / gqa70b_long: decode-only passes (batch 64 MHA 32x128;
+  batch 32 GQA 64/8 at 2048 keys; one GQA sequence of 32768 keys).  value =
+  KV bytes read per second.
+
+The roofline object describes the dominant kernel, timed with HIP events
+recorded on the stream it runs on (pa_set_stage_events), against MI355X's
+8 TB/s HBM.  cpu_baseline times the fp64 CPU oracle on a bounded sample of
+the same workload on this host.
+
+    python bench.py [--workload splitfuse] [--steps 20] [--warmup 3] [--gpus 1]
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn KV-read GB/s (% HBM peak); SplitFuse mixed-batch tokens/s"
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2516.6
+MALL_BYTES = 256 << 20
+STAGES = ("plan", "valu_worker", "mfma_worker", "merge")
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (the library records them on its own stream)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def new(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        self.events += out
+        return out
+
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, a, b):
+        f = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(f), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return f.value
+
+    def close(self):
+        for e in self.events:
+            self.lib.hipEventDestroy(ctypes.c_void_p(e))
+        self.events = []
+
+
+def build_workload(name):
+    import workloads as W
+    return {"splitfuse": lambda: W.splitfuse_mixed(0),
+            "llama7b": lambda: W.llama7b_decode(0),
+            "gqa70b": lambda: W.gqa70b_decode(0),
+            "gqa70b_long": lambda: W.gqa70b_long_decode(0),
+            "tiny": lambda: W.tiny_decode(0)}[name]()
+
+
+def kv_token_bytes(w):
+    return 2 * w.num_kv_heads * w.head_dim * (4 if w.dtype == "f32" else 2)
+
+
+def work_split(w):
+    """Algorithmic work of one pass, split by the worker that does it.
+
+    Decode rows of sequences with one query head per KV head run on the VALU
+    worker (as does everything in float32); GQA decode rows and prefill chunks
+    run on the MFMA worker.  Bytes are the KV pages the rows must read (each
+    context key once per KV head: 2 * Hkv * d * elem bytes per key); FLOPs
+    count QK^T and PV over the keys each prefill row may see.
+    """
+    ql = np.diff(w.query_start_loc).astype(np.int64)
+    L = w.context_lens.astype(np.int64)
+    G = w.num_q_heads // w.num_kv_heads
+    valu = (ql == 1) & (G == 1) if w.dtype == "bf16" else (ql >= 1)
+    mfma = (ql >= 1) & ~valu
+    valu_bytes = int(L[valu].sum()) * kv_token_bytes(w)
+    mfma_bytes = int(L[mfma].sum()) * kv_token_bytes(w)
+    flops = 0
+    for q, Ls in zip(ql[ql > 1], L[ql > 1]):
+        pos = Ls - q + np.arange(q)
+        flops += 4 * w.head_dim * w.num_q_heads * int((pos + 1).sum())
+    return valu_bytes, mfma_bytes, flops
+
+
+def cpu_baseline(w, q, kc, vc, budget_s):
+    """fp64 oracle on a bounded sample of the workload's decode sequences (host copies of their bytes)."""
+    import torch
+
+    from oracle import attention as oattn
+    ql = np.diff(w.query_start_loc)
+    dec = np.flatnonzero(ql == 1)
+    pool = dec if dec.size else np.arange(w.num_seqs)
+    rng = np.random.default_rng(123)
+    order = rng.permutation(pool)
+
+    def raw(t):
+        t = t.detach().cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    done_tokens = 0
+    spent = 0.0
+    kv_bytes = 0
+    n = 0
+    for s in order:
+        Ls = int(w.context_lens[s])
+        nb = (Ls + 15) // 16
+        ids = torch.from_numpy(w.block_tables[s, :nb].astype(np.int64)).to(kc.device)
+        kp, vp = raw(kc.index_select(0, ids)), raw(vc.index_select(0, ids))
+        a, b = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
+        qh = raw(q[a:b])
+        tab = np.arange(nb, dtype=np.int32)[None]
+        t0 = time.perf_counter()
+        oattn.paged_attention(qh, kp, vp, tab, np.array([Ls], np.int32), np.array([0, b - a], np.int32),
+                              w.scale, w.dtype)
+        spent += time.perf_counter() - t0
+        done_tokens += b - a
+        kv_bytes += Ls * kv_token_bytes(w)
+        n += 1
+        if spent >= budget_s:
+            break
+    threads = None
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=1)
+    except Exception:
+        pass
+    cores = threads or 1
+    return {"tokens": done_tokens, "seconds": spent, "kv_bytes": kv_bytes, "seqs": n, "cores": cores,
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="splitfuse",
+                    choices=["splitfuse", "llama7b", "gqa70b", "gqa70b_long", "tiny"])
+    ap.add_argument("--rotate", type=int, default=0, help="pool copies cycled per step (0: enough to exceed the 256 MB MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the CPU oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus})",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_57_amd as pa
+    import workloads as W
+
+    dev = torch.device("cuda:0")
+    w = build_workload(args.workload)
+    code = pa.PA_BF16 if w.dtype == "bf16" else pa.PA_F32
+    q, kc, vc, nk, nv = W.make_values(w, dev)
+    valu_bytes, mfma_bytes, pre_flops = work_split(w)
+    pass_bytes = valu_bytes + mfma_bytes
+    # cycle enough pool copies that one pass's pages cannot stay in the 256 MB Infinity Cache
+    rotate = args.rotate or (1 if pass_bytes >= 8 * MALL_BYTES else int(np.ceil(8 * MALL_BYTES / max(pass_bytes, 1))))
+    pools = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(max(1, rotate) - 1)]
+    rotate = len(pools)
+
+    tables = torch.from_numpy(w.block_tables).to(dev)
+    lens = torch.from_numpy(w.context_lens).to(dev)
+    qsl = torch.from_numpy(w.query_start_loc).to(dev)
+    slots = None if w.new_slots is None else torch.from_numpy(w.new_slots).to(dev)
+    nbytes = pa.pa_forward_workspace_bytes(w.num_seqs, w.num_tokens, w.max_q_len, w.num_q_heads, w.num_kv_heads,
+                                           w.head_dim, w.max_context_len, code)
+    workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ev = HipEvents()
+
+    def step(i, stage_events=None, write_events=None):
+        kcur, vcur = pools[i % rotate]
+        if slots is not None:
+            if write_events:
+                ev.record(write_events[0], stream)
+            pa.pa_reshape_and_cache(nk, nv, kcur, vcur, slots, status)
+            if write_events:
+                ev.record(write_events[1], stream)
+        pa.pa_set_stage_events(stage_events)
+        pa.pa_forward(out, q, kcur, vcur, tables, lens, qsl, w.max_q_len, w.max_context_len, w.scale,
+                      workspace, status)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item()):#x}")
+
+    K = args.steps
+    stage_ev = [ev.new(2 * len(STAGES)) for _ in range(K)]
+    write_ev = [ev.new(2) for _ in range(K)] if slots is not None else [None] * K
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(args.warmup + k, stage_ev[k], write_ev[k])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    pa.pa_set_stage_events(None)
+    stage_ms = {name: float(np.mean([ev.ms(e[2 * j], e[2 * j + 1]) for e in stage_ev]))
+                for j, name in enumerate(STAGES)}
+    write_ms = float(np.mean([ev.ms(e[0], e[1]) for e in write_ev])) if slots is not None else 0.0
+    ev.close()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item()):#x}")
+
+    ms_per_step = 1e3 * elapsed / K
+    # the dominant kernel is the worker with the larger share of the pass
+    dom = "valu_worker" if stage_ms["valu_worker"] >= stage_ms["mfma_worker"] else "mfma_worker"
+    dom_bytes = valu_bytes if dom == "valu_worker" else mfma_bytes
+    achieved = dom_bytes / (stage_ms[dom] * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+    }
+    if args.workload == "splitfuse":
+        result.update(value=round(w.num_tokens / (ms_per_step * 1e-3), 1), unit="tokens/s")
+    else:
+        result.update(value=round(pass_bytes / (ms_per_step * 1e-3) / 1e9, 2), unit="GB/s")
+    result["config"] = {"workload": w.name, "num_seqs": w.num_seqs, "query_tokens": w.num_tokens,
+                        "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+                        "block_size": 16, "max_context_len": w.max_context_len, "pool_blocks": w.num_blocks,
+                        "pool_copies_rotated": rotate}
+    result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                          "kernel": dom, "kernel_ms": round(stage_ms[dom], 4), "algorithmic_bytes": dom_bytes}
+    result["stages_ms"] = {k: round(v, 4) for k, v in stage_ms.items()}
+    if slots is not None:
+        result["stages_ms"]["cache_write"] = round(write_ms, 4)
+    if valu_bytes:
+        result["valu_worker_kv_GBps"] = round(valu_bytes / (stage_ms["valu_worker"] * 1e-3) / 1e9, 1)
+    if mfma_bytes and not pre_flops:
+        result["mfma_worker_kv_GBps"] = round(mfma_bytes / (stage_ms["mfma_worker"] * 1e-3) / 1e9, 1)
+    if pre_flops:
+        mfma_ms = stage_ms["mfma_worker"]
+        result["prefill"] = {"algorithmic_tflops": round(pre_flops / 1e12, 3),
+                             "achieved_tflops": round(pre_flops / (mfma_ms * 1e-3) / 1e12, 1),
+                             "frac_of_bf16_mfma_peak": round(pre_flops / (mfma_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline(w, q, kc, vc, args.cpu_seconds)
+        result["cpu_baseline"] = {
+            "value": round(cb["tokens"] / cb["seconds"], 3) if args.workload == "splitfuse"
+            else round(cb["kv_bytes"] / cb["seconds"] / 1e9, 4),
+            "unit": "tokens/s" if args.workload == "splitfuse" else "GB/s",
+            "cores": cb["cores"], "kind": "oracle",
+            "sample": f"{cb['seqs']} decode sequences of this batch (gather + fp64 attention over host copies "
+                      f"of their pages), {cb['seconds']:.1f} s on {cb['host_cpus']} host CPUs"}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

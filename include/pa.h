@@ -147,6 +147,16 @@ pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* 
                      pa_dtype dtype, void* workspace, size_t workspace_bytes,
                      int32_t* dev_status, void* stream);
 
+/* Measurement hook, for timing only (changes nothing that is computed).
+ * pa_forward runs four stages on its stream: 0 planner, 1 VALU worker, 2 MFMA
+ * worker, 3 log-sum-exp merge.  After this call, every pa_forward on the
+ * calling thread records events[2k] before and events[2k+1] after stage k
+ * (k < num_events/2) with hipEventRecord on its stream; a stage that has no
+ * work records both events back to back.  events: host array of hipEvent_t
+ * created by the caller, who keeps it alive; NULL entries are skipped.
+ * num_events 0 (events may be NULL) turns recording off. */
+pa_status pa_set_stage_events(void* const* events, int32_t num_events);
+
 /* ------------------------------------------------------------------ copy-on-write
  * pa_copy_blocks — for each pair (src, dst) = block_pairs[2i], block_pairs[2i+1],
  * copy the whole key and value page of block src (all KV heads) onto block dst,

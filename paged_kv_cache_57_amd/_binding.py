@@ -51,6 +51,7 @@ _SIGS = {
     "pa_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                           _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "pa_set_stage_events": (_i32, [_vp, _i32]),
     "pa_alloc_create": (_i32, [_i32, _i32, _f64, _vp, ctypes.POINTER(_vp)]),
     "pa_alloc_destroy": (None, [_vp]),
     "pa_alloc_num_free": (_i32, [_vp]),
@@ -175,6 +176,17 @@ def pa_copy_blocks(k_cache, v_cache, block_pairs, dev_status=None, stream=None):
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_pairs, "block_pairs", torch.int32),
         block_pairs.shape[0], nb, hkv, d, blk, _dtype_code(k_cache),
         _dev(dev_status, "dev_status", torch.int32), _stream(k_cache, stream)))
+
+
+def pa_set_stage_events(events):
+    """events: sequence of raw hipEvent_t handles (ints), or None to stop recording."""
+    if not events:
+        _check(_lib.pa_set_stage_events(None, 0))
+        pa_set_stage_events._keep = None
+        return
+    arr = (ctypes.c_void_p * len(events))(*events)
+    pa_set_stage_events._keep = arr          # the library reads the array at every pa_forward
+    _check(_lib.pa_set_stage_events(arr, len(events)))
 
 
 # ---------------------------------------------------------------- host allocator

@@ -16,7 +16,11 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa.so")
 SOURCES = ["pa_status.cpp", "pa_alloc.cpp", "pa_cache.hip", "pa_attention.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# No packed FP32 instructions; and no atomic optimizer, which wraps each atomic in a
+# branch on the first active lane (the kernels keep their work loops free of
+# lane-dependent branches).
+DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function"]
 
 

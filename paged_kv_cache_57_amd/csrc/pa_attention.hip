@@ -16,8 +16,8 @@
 //        prefill chunks, whose positions x G heads become the rows).
 //    Partition sizes depend only on the sequence's own lengths, so a
 //    sequence's result does not depend on the rest of the batch.
-//  * Persistent workers pull items from a device work queue.  Each item
-//    streams its pages with 16-byte loads and keeps the running max m, the
+//  * Persistent workers walk the items with a fixed stride (wave w takes
+//    items w, w + W, w + 2W, ...).  Each item streams its pages with 16-byte loads and keeps the running max m, the
 //    running sum l and the unnormalised output O of the tiled online softmax
 //    ("第 15 章" §15.1 "算法详解": m_new = max(m, rowmax S), α = exp(m − m_new),
 //    P = exp(S − m_new), l = αl + rowsum P, O = diag(α)O + PV), in base 2
@@ -89,7 +89,7 @@ struct AttnParams {
   int32_t Hq, Hkv, G, num_blocks;
   float scale_log2;
   int32_t is_f32;
-  int32_t* ctrl;  // [0] VALU queue, [1] MFMA queue, [2] VALU items, [3] MFMA items
+  int32_t* ctrl;  // [2] VALU items, [3] MFMA items
   int32_t* pre_v;
   int32_t* pre_m;
   float* partials;  // [T][Hq][maxparts][D + 4]: O (unnormalised), m, l, 2 pad
@@ -173,31 +173,31 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
   if (tid == 0) {
     p.pre_v[p.num_seqs] = carry_v;
     p.pre_m[p.num_seqs] = carry_m;
-    p.ctrl[0] = 0;
-    p.ctrl[1] = 0;
     p.ctrl[2] = carry_v;
     p.ctrl[3] = carry_m;
   }
 }
 
-__device__ inline int next_item(int32_t* queue, int lane) {
-  int item = 0;
-  if (lane == 0) item = atomicAdd(queue, 1);
-  return __builtin_amdgcn_readfirstlane(item);
-}
+// Work distribution and control flow in the workers: a wavefront walks the
+// items wave_id, wave_id + nwaves, ... with both numbers made uniform by
+// readfirstlane, and nothing inside an item branches on the lane index.
+// Lane-dependent branches around the loop (for example "lane 0 fetches the
+// next item, then everyone reads it back") were merged by the compiler across
+// the loop's back edge into an inner loop that only lane 0 leaves, after which
+// the other lanes ran on with a stale item and read lane values of a lane that
+// was no longer active.  So stores are unconditional (lanes holding the same
+// value write the same address) and loads use clamped, always-valid indices.
+__device__ inline int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Loads this partition's physical block ids into lanes 0..nblk-1 and checks
-// them.  Returns false (and flags) if any id lies outside the pool.
-__device__ inline bool load_block_ids(const AttnParams& p, int s, int first_blk, int nblk, int lane,
-                                      int& bid) {
-  bid = 0;
-  if (lane < nblk) bid = p.block_tables[(int64_t)s * p.mbps + first_blk + lane];
-  const bool bad = lane < nblk && (bid < 0 || bid >= p.num_blocks);
-  if (__builtin_amdgcn_ballot_w64(bad)) {
-    if (lane == 0) flag_status(p.dev_status, PA_DEV_BAD_BLOCK);
-    return false;
-  }
-  return true;
+// Physical block ids of this partition's pages: lane j holds page j (lanes
+// past the last page repeat it).  An id outside the pool is replaced by block
+// 0, which keeps every address inside the pool, and PA_DEV_BAD_BLOCK is set.
+__device__ inline int load_block_ids(const AttnParams& p, int s, int first_blk, int nblk, int lane) {
+  const int j = min(lane, nblk - 1);
+  const int bid = p.block_tables[(int64_t)s * p.mbps + first_blk + j];
+  const bool bad = bid < 0 || bid >= p.num_blocks;
+  if (__builtin_amdgcn_ballot_w64(bad)) flag_status(p.dev_status, PA_DEV_BAD_BLOCK);
+  return bad ? 0 : bid;
 }
 
 __device__ inline void wave_lds_sync() {
@@ -228,17 +228,20 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const int total = p.ctrl[2];
+  const int wave_id = wave_uniform((int)(blockIdx.x * 4 + wv));
+  const int nwaves = (int)gridDim.x * 4;
+  const int total = wave_uniform(p.ctrl[2]);
   const T* __restrict__ kc = (const T*)p.k_cache;
   const T* __restrict__ vc = (const T*)p.v_cache;
   const int64_t page_elems = (int64_t)kBlock * D;
 
-  for (;;) {
-    const int item = next_item(&p.ctrl[0], lane);
-    if (item >= total) break;
-    const int s = find_seq(p.pre_v, p.num_seqs, item);
-    const int local = item - p.pre_v[s];
-    const SeqInfo si = read_seq(p, s);
+  for (int item = wave_id; item < total; item += nwaves) {
+    const int s = wave_uniform(find_seq(p.pre_v, p.num_seqs, item));
+    const int local = item - wave_uniform(p.pre_v[s]);
+    SeqInfo si = read_seq(p, s);
+    si.a = wave_uniform(si.a);
+    si.q_len = wave_uniform(si.q_len);
+    si.L = wave_uniform(si.L);
     const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L);
     const int pidx = local % w.nparts;
     const int rh = local / w.nparts;
@@ -256,9 +259,8 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
     for (int k = 0; k < NIV; ++k) acc[k] = 0.f;
 
     if (kv_lo < kv_hi) {
-      int bidv;
       const int nblk = (kv_hi - kv_lo + kBlock - 1) / kBlock;
-      if (!load_block_ids(p, s, kv_lo / kBlock, nblk, lane, bidv)) continue;
+      const int bidv = load_block_ids(p, s, kv_lo / kBlock, nblk, lane);
 
       // q row: the 16-byte groups this lane multiplies
       const T* qrow = (const T*)p.q + ((int64_t)t * p.Hq + h) * D;
@@ -362,22 +364,17 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
       acc[k] += shfl_xor_f(acc[k], 1);
       if constexpr (LPR == 4) acc[k] += shfl_xor_f(acc[k], 2);
     }
+    // every lane of a column group holds the column's value: all of them store it
     if (w.nparts == 1) {
-      if (lane % LPR == 0) {
-        T* orow = (T*)p.out + ((int64_t)t * p.Hq + h) * D;
+      T* orow = (T*)p.out + ((int64_t)t * p.Hq + h) * D;
 #pragma unroll
-        for (int k = 0; k < NIV; ++k) orow[RPI * k + lane / LPR] = Elem<T>::from_f32(acc[k] / l);
-      }
+      for (int k = 0; k < NIV; ++k) orow[RPI * k + lane / LPR] = Elem<T>::from_f32(acc[k] / l);
     } else {
       float* slot = p.partials + (((int64_t)t * p.Hq + h) * p.maxparts + pidx) * slot_floats(D);
-      if (lane % LPR == 0) {
 #pragma unroll
-        for (int k = 0; k < NIV; ++k) slot[RPI * k + lane / LPR] = acc[k];
-      }
-      if (lane == 0) {
-        slot[D] = m;
-        slot[D + 1] = l;
-      }
+      for (int k = 0; k < NIV; ++k) slot[RPI * k + lane / LPR] = acc[k];
+      slot[D] = m;
+      slot[D + 1] = l;
     }
   }
 }
@@ -402,29 +399,34 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(AttnParams p) {
   constexpr int NJ = D / 16;  // 16-dim column blocks of the output
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g4 = lane >> 4;
-  const int total = p.ctrl[3];
+  const int wave_id = wave_uniform((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
+  const int nwaves = (int)gridDim.x * 4;
+  const int total = wave_uniform(p.ctrl[3]);
   const bf16_t* __restrict__ kc = (const bf16_t*)p.k_cache;
   const bf16_t* __restrict__ vc = (const bf16_t*)p.v_cache;
   const int64_t page_elems = (int64_t)kBlock * D;
 
-  for (;;) {
-    const int item = next_item(&p.ctrl[1], lane);
-    if (item >= total) break;
-    const int s = find_seq(p.pre_m, p.num_seqs, item);
-    const int local = item - p.pre_m[s];
-    const SeqInfo si = read_seq(p, s);
+  for (int item = wave_id; item < total; item += nwaves) {
+    const int s = wave_uniform(find_seq(p.pre_m, p.num_seqs, item));
+    const int local = item - wave_uniform(p.pre_m[s]);
+    SeqInfo si = read_seq(p, s);
+    si.a = wave_uniform(si.a);
+    si.q_len = wave_uniform(si.q_len);
+    si.L = wave_uniform(si.L);
     const SeqWork w = seq_work(false, p.G, p.Hq, p.Hkv, si.q_len, si.L);
     const int pidx = local % w.nparts;
     const int rest = local / w.nparts;
     const int kvh = rest % p.Hkv;
     const int tile = rest / p.Hkv;
     const int rows_total = si.q_len * p.G;
-    const int R = tile * kTileRows + r;
-    const bool valid_row = R < rows_total;
+    // Rows past the sequence's last row (the padding of the last tile) repeat
+    // that last row: they compute its values and store the same bytes to its
+    // address, so no lane ever needs a branch or a dummy destination.
+    const int R = min(tile * kTileRows + r, rows_total - 1);
     const int qi = R / p.G;
     const int hh = kvh * p.G + R % p.G;
     const int t = si.a + qi;
-    const int pos_r = valid_row ? si.L - si.q_len + qi : -1;
+    const int pos_r = si.L - si.q_len + qi;
     const int last_row = min(tile * kTileRows + kTileRows - 1, rows_total - 1);
     const int tile_pos_max = si.L - si.q_len + last_row / p.G;
     const int kv_lo = pidx * w.part;
@@ -436,16 +438,14 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(AttnParams p) {
     for (int j = 0; j < NJ; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     if (kv_lo < kv_hi) {
-      int bidv;
       const int nblk = (kv_hi - kv_lo + kBlock - 1) / kBlock;
-      if (!load_block_ids(p, s, kv_lo / kBlock, nblk, lane, bidv)) continue;
+      const int bidv = load_block_ids(p, s, kv_lo / kBlock, nblk, lane);
 
       bf16x8 qop[KS];
       {
         const bf16_t* qrow = (const bf16_t*)p.q + ((int64_t)t * p.Hq + hh) * D;
 #pragma unroll
-        for (int k = 0; k < KS; ++k)
-          qop[k] = __builtin_bit_cast(bf16x8, valid_row ? ld16(qrow + 32 * k + 8 * g4) : u32x4{0, 0, 0, 0});
+        for (int k = 0; k < KS; ++k) qop[k] = __builtin_bit_cast(bf16x8, ld16(qrow + 32 * k + 8 * g4));
       }
 
       for (int base = kv_lo; base < kv_hi; base += 32) {
@@ -502,13 +502,12 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(AttnParams p) {
         for (int e = 0; e < 8; e += 2) {
           const float p0 = none ? 0.f : exp2f(sc[e] - m_new);
           const float p1 = none ? 0.f : exp2f(sc[e + 1] - m_new);
-          const bf16_t h0 = Elem<bf16_t>::from_f32(p0), h1 = Elem<bf16_t>::from_f32(p1);
-          const float r0 = p0 - Elem<bf16_t>::to_f32(h0), r1 = p1 - Elem<bf16_t>::to_f32(h1);
-          const bf16_t l0 = Elem<bf16_t>::from_f32(r0), l1 = Elem<bf16_t>::from_f32(r1);
-          psum += (Elem<bf16_t>::to_f32(h0) + Elem<bf16_t>::to_f32(l0)) +
-                  (Elem<bf16_t>::to_f32(h1) + Elem<bf16_t>::to_f32(l1));
-          phw[e >> 1] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          plw[e >> 1] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+          const uint32_t hw = pack_bf16x2(p0, p1);
+          const float r0 = p0 - bf16_lo(hw), r1 = p1 - bf16_hi(hw);
+          const uint32_t lw = pack_bf16x2(r0, r1);
+          psum += (bf16_lo(hw) + bf16_lo(lw)) + (bf16_hi(hw) + bf16_hi(lw));
+          phw[e >> 1] = hw;
+          plw[e >> 1] = lw;
         }
         lsum = lsum * alpha + psum;
         m_r = m_new;
@@ -536,27 +535,19 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(AttnParams p) {
     }
     float l = lsum + shfl_xor_f(lsum, 16);
     l += shfl_xor_f(l, 32);
-    if (valid_row) {
-      if (w.nparts == 1) {
-        bf16_t* orow = (bf16_t*)p.out + ((int64_t)t * p.Hq + hh) * D;
+    if (w.nparts == 1) {
+      bf16_t* orow = (bf16_t*)p.out + ((int64_t)t * p.Hq + hh) * D;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          u32x2 pk;
-          pk[0] = (uint32_t)Elem<bf16_t>::from_f32(oacc[j][0] / l) |
-                  ((uint32_t)Elem<bf16_t>::from_f32(oacc[j][1] / l) << 16);
-          pk[1] = (uint32_t)Elem<bf16_t>::from_f32(oacc[j][2] / l) |
-                  ((uint32_t)Elem<bf16_t>::from_f32(oacc[j][3] / l) << 16);
-          *reinterpret_cast<u32x2*>(orow + 16 * j + 4 * g4) = pk;
-        }
-      } else {
-        float* slot = p.partials + (((int64_t)t * p.Hq + hh) * p.maxparts + pidx) * slot_floats(D);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) *reinterpret_cast<f32x4*>(slot + 16 * j + 4 * g4) = oacc[j];
-        if (g4 == 0) {
-          slot[D] = m_r;
-          slot[D + 1] = l;
-        }
+      for (int j = 0; j < NJ; ++j) {
+        const u32x2 pk = {pack_bf16x2(oacc[j][0] / l, oacc[j][1] / l), pack_bf16x2(oacc[j][2] / l, oacc[j][3] / l)};
+        *reinterpret_cast<u32x2*>(orow + 16 * j + 4 * g4) = pk;
       }
+    } else {
+      float* slot = p.partials + (((int64_t)t * p.Hq + hh) * p.maxparts + pidx) * slot_floats(D);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) *reinterpret_cast<f32x4*>(slot + 16 * j + 4 * g4) = oacc[j];
+      slot[D] = m_r;  // the four lanes of a row hold the same m and l
+      slot[D + 1] = l;
     }
   }
 }
@@ -566,25 +557,35 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(AttnParams p) {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
   const int lane = threadIdx.x & 63;
-  const int rh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int rh = wave_uniform((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
   if (rh >= p.T * p.Hq) return;
   const int t = rh / p.Hq, h = rh % p.Hq;
-  const int s = find_seq(p.qsl, p.num_seqs, t);
-  const SeqInfo si = read_seq(p, s);
-  if (!si.ok || t < si.a || t >= si.a + si.q_len) return;
+  const int s = wave_uniform(find_seq(p.qsl, p.num_seqs, t));
+  SeqInfo si = read_seq(p, s);
+  si.a = wave_uniform(si.a);
+  si.q_len = wave_uniform(si.q_len);
+  si.L = wave_uniform(si.L);
+  if (!wave_uniform(si.ok) || t < si.a || t >= si.a + si.q_len) return;
   const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L);
   if (w.nparts <= 1) return;
   const int pos = si.L - si.q_len + (t - si.a);
   const int np = min(w.nparts, pos / w.part + 1);  // later partitions hold no visible key
   const float* base = p.partials + ((int64_t)t * p.Hq + h) * p.maxparts * slot_floats(D);
+  // lane-strided passes with a uniform trip count; lanes past np read partition 0 and drop it
   float M = kNegInf;
-  for (int q = lane; q < np; q += 64) M = fmaxf(M, base[(int64_t)q * slot_floats(D) + D]);
+  for (int q0 = 0; q0 < np; q0 += 64) {
+    const int q = q0 + lane;
+    const float mq = base[(int64_t)(q < np ? q : 0) * slot_floats(D) + D];
+    M = fmaxf(M, q < np ? mq : kNegInf);
+  }
   M = wave_max(M);
   float lsum = 0.f;
-  for (int q = lane; q < np; q += 64) {
-    const float mq = base[(int64_t)q * slot_floats(D) + D];
-    const float lq = base[(int64_t)q * slot_floats(D) + D + 1];
-    lsum += mq == kNegInf ? 0.f : lq * exp2f(mq - M);
+  for (int q0 = 0; q0 < np; q0 += 64) {
+    const int q = q0 + lane;
+    const float* sl = base + (int64_t)(q < np ? q : 0) * slot_floats(D);
+    // M is finite, so 2^(m - M) is 0 for an empty partition (m = -inf) and for lanes past np
+    const float mq = sl[D], lq = sl[D + 1];
+    lsum += lq * exp2f(q < np ? mq - M : kNegInf);
   }
   const float l = wave_sum(lsum);
   constexpr int PER = D / 64;
@@ -593,9 +594,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
   for (int k = 0; k < PER; ++k) o[k] = 0.f;
   for (int q = 0; q < np; ++q) {
     const float* sl = base + (int64_t)q * slot_floats(D);
-    const float mq = sl[D];
-    if (mq == kNegInf) continue;
-    const float wq = exp2f(mq - M);
+    const float wq = exp2f(sl[D] - M);  // empty partition: 2^-inf = 0 and O_p = 0
 #pragma unroll
     for (int k = 0; k < PER; ++k) o[k] = fmaf(sl[lane + 64 * k], wq, o[k]);
   }
@@ -626,19 +625,37 @@ WsLayout ws_layout(int S, int T, int Hq, int Hkv, int D, int max_ctx, bool is_f3
   return l;
 }
 
+// Optional events recorded around each stage of pa_forward (see pa_set_stage_events).
+thread_local void* const* g_stage_events = nullptr;
+thread_local int32_t g_num_stage_events = 0;
+
+inline void mark(int stage, int edge, hipStream_t stream) {
+  const int k = 2 * stage + edge;
+  if (g_stage_events && k < g_num_stage_events && g_stage_events[k])
+    (void)hipEventRecord((hipEvent_t)g_stage_events[k], stream);
+}
+
 template <typename T, int D>
 void launch_attention(const AttnParams& p, bool may_valu, bool may_mfma, int grid_v, int grid_m,
                       hipStream_t stream) {
+  mark(0, 0, stream);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, p);
+  mark(0, 1, stream);
+  mark(1, 0, stream);
   if (may_valu)
     hipLaunchKernelGGL((valu_attn_kernel<T, D>), dim3(grid_v), dim3(256), 0, stream, p);
+  mark(1, 1, stream);
+  mark(2, 0, stream);
   if constexpr (sizeof(T) == 2) {
     if (may_mfma) hipLaunchKernelGGL((mfma_attn_kernel<D>), dim3(grid_m), dim3(256), 0, stream, p);
   }
+  mark(2, 1, stream);
+  mark(3, 0, stream);
   if (p.maxparts > 1) {
     const int64_t rows = (int64_t)p.T * p.Hq;
     hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
   }
+  mark(3, 1, stream);
 }
 
 }  // namespace
@@ -749,5 +766,13 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+extern "C" pa_status pa_set_stage_events(void* const* events, int32_t num_events) {
+  if (num_events < 0 || (num_events > 0 && !events))
+    return fail(PA_ERR_INVALID, "pa_set_stage_events: bad event list");
+  g_stage_events = num_events ? events : nullptr;
+  g_num_stage_events = num_events;
   return ok();
 }

@@ -34,14 +34,20 @@ template <>
 struct Elem<bf16_t> {
   static constexpr int X = 8;
   __device__ static inline float to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
-  // Round to nearest even (NaN stays NaN).
+  // Round to nearest even, NaN stays NaN (v_cvt_pk_bf16_f32 on gfx950, no branch).
   __device__ static inline bf16_t from_f32(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
+    const __bf16 b = (__bf16)f;
+    return __builtin_bit_cast(bf16_t, b);
   }
 };
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats rounded to bfloat16 and packed (low half = a), one instruction.
+__device__ inline uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2 v = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // Low / high bfloat16 of a packed pair, widened to float32 (exact).
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

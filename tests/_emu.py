@@ -91,3 +91,17 @@ def copy_blocks(dtype, kp, vp, pairs):
     raw, st = _run("copy", [hdr, kp, vp, pairs], kp.nbytes + vp.nbytes)
     return (np.frombuffer(raw[:kp.nbytes], kp.dtype).reshape(kp.shape),
             np.frombuffer(raw[kp.nbytes:], vp.dtype).reshape(vp.shape), st)
+
+
+def forward_sparse(w, q, pages_k, pages_v, used):
+    """Emulated pa_forward on a full-size zeroed pool holding only the ``used`` blocks' pages."""
+    es = 4 if w.dtype == "f32" else 2
+    hdr = np.array([dtype_code(w.dtype), w.num_seqs, w.num_tokens, w.max_q_len, w.max_context_len,
+                    w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_blocks, w.max_blocks_per_seq], np.int32)
+    blob = [hdr, np.array([w.scale], np.float32), q, np.array([len(used)], np.int32),
+            np.asarray(used, np.int32), pages_k, pages_v, w.block_tables.astype(np.int32),
+            w.context_lens.astype(np.int32), w.query_start_loc.astype(np.int32)]
+    n = w.num_tokens * w.num_q_heads * w.head_dim
+    raw, st = _run("forward_sparse", blob, n * es, timeout=3600)
+    dt = np.float32 if w.dtype == "f32" else np.uint16
+    return np.frombuffer(raw, dt).reshape(w.num_tokens, w.num_q_heads, w.head_dim), st

@@ -48,7 +48,42 @@ int main(int argc, char** argv) {
   fout = std::fopen(argv[3], "wb");
   if (!fin || !fout) return 2;
   int32_t status = 0;
-  if (!std::strcmp(argv[1], "forward")) {
+  if (!std::strcmp(argv[1], "forward_sparse")) {
+    // Same as forward, but the pools are described by the blocks the tables use:
+    // i32 nused, i32 ids[nused], then the K pages and the V pages of those blocks.
+    // The full pools are allocated zeroed at their real size (large pools test
+    // 64-bit page offsets) and only the given blocks are filled in.
+    const int dt = rd_i32(), S = rd_i32(), T = rd_i32(), mq = rd_i32(), mc = rd_i32();
+    const int Hq = rd_i32(), Hkv = rd_i32(), D = rd_i32(), NB = rd_i32(), mbps = rd_i32();
+    const float scale = rd_f32();
+    const size_t es = dt == PA_F32 ? 4 : 2;
+    const size_t page = (size_t)Hkv * 16 * D * es;
+    void* q = rd_buf((size_t)T * Hq * D * es);
+    const int nused = rd_i32();
+    auto* ids = (int32_t*)rd_buf((size_t)nused * 4);
+    auto* kc = (char*)std::calloc((size_t)NB * page, 1);
+    auto* vc = (char*)std::calloc((size_t)NB * page, 1);
+    if (!kc || !vc) return 4;
+    for (int i = 0; i < nused; ++i)
+      if (std::fread(kc + (size_t)ids[i] * page, 1, page, fin) != page) std::abort();
+    for (int i = 0; i < nused; ++i)
+      if (std::fread(vc + (size_t)ids[i] * page, 1, page, fin) != page) std::abort();
+    auto* tab = (int32_t*)rd_buf((size_t)S * mbps * 4);
+    auto* lens = (int32_t*)rd_buf((size_t)S * 4);
+    auto* qsl = (int32_t*)rd_buf((size_t)(S + 1) * 4);
+    void* out = std::malloc((size_t)T * Hq * D * es);
+    const size_t wsb = pa_forward_workspace_bytes(S, T, mq, Hq, Hkv, D, mc, (pa_dtype)dt);
+    void* ws = std::aligned_alloc(256, wsb);
+    pa_status st = pa_forward(out, q, kc, vc, tab, mbps, lens, qsl, S, T, mq, mc, Hq, Hkv, D, 16, NB,
+                              scale, (pa_dtype)dt, ws, wsb, &status, nullptr);
+    if (st != PA_OK) {
+      std::fprintf(stderr, "pa_forward: %d %s\n", st, pa_last_error());
+      return 3;
+    }
+    wr(out, (size_t)T * Hq * D * es);
+    std::free(ws); std::free(out); std::free(q); std::free(ids); std::free(kc); std::free(vc);
+    std::free(tab); std::free(lens); std::free(qsl);
+  } else if (!std::strcmp(argv[1], "forward")) {
     const int dt = rd_i32(), S = rd_i32(), T = rd_i32(), mq = rd_i32(), mc = rd_i32();
     const int Hq = rd_i32(), Hkv = rd_i32(), D = rd_i32(), NB = rd_i32(), mbps = rd_i32();
     const float scale = rd_f32();

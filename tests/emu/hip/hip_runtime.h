@@ -20,10 +20,12 @@ struct dim3 {
 };
 
 typedef struct emu_stream* hipStream_t;
+typedef struct emu_event* hipEvent_t;
 typedef int hipError_t;
 constexpr hipError_t hipSuccess = 0;
 inline hipError_t hipGetLastError() { return hipSuccess; }
 inline const char* hipGetErrorString(hipError_t) { return "emulated"; }
+inline hipError_t hipEventRecord(hipEvent_t, hipStream_t) { return hipSuccess; }
 
 #define __global__
 #define __device__

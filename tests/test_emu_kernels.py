@@ -14,7 +14,7 @@ from oracle import attention as oattn
 from oracle import cache_ops, layout
 from tests import _emu
 from tests._pools import empty_pools, raw
-from tests.test_gpu_parity import FAULTED, RAGGED
+from tests.test_gpu_parity import RAGGED, REJECTED
 
 pytestmark = pytest.mark.skipif(not _emu.available(), reason="needs the ROCm clang++ for the host build")
 TOL = {"bf16": (2e-3, 1e-2), "f32": (1e-5, 1e-5)}
@@ -35,7 +35,7 @@ def check(w, q, kp, vp, out, label):
     return ratio
 
 
-@pytest.mark.parametrize("i", [i for i in range(len(RAGGED)) if i not in FAULTED])
+@pytest.mark.parametrize("i", [i for i in range(len(RAGGED)) if i not in REJECTED])
 def test_ragged_cases_match_oracle(emu, i):
     dt, hq, hkv, d, ql, cl = RAGGED[i]
     w = W.random_ragged(100 + i, dt, hq, hkv, d, ql, cl)

@@ -1,4 +1,13 @@
-"""Every gfx950 kernel of the library fits its registers without spilling."""
+"""Properties of the compiled gfx950 kernels, checked on the CPU from hipcc output.
+
+* No kernel spills registers or uses scratch memory.
+* The attention workers and the merge contain no exec-mask regions: nothing
+  inside them branches per lane.  Their work loops call cross-lane operations
+  (readfirstlane, readlane, shuffles, MFMA); a lane-dependent branch near such
+  a loop let the compiler split the wavefront across loop iterations, which
+  left lanes running with a stale work item.
+"""
+import importlib.util
 import os
 import re
 import subprocess
@@ -10,13 +19,24 @@ from tests.conftest import ROOT
 CSRC = os.path.join(ROOT, "paged_kv_cache_57_amd", "csrc")
 
 
-@pytest.mark.parametrize("src", ["pa_attention.hip", "pa_cache.hip"])
-def test_no_register_spills(src):
-    r = subprocess.run(["/opt/rocm/bin/hipcc", "-x", "hip", "--offload-arch=gfx950", "-Xclang", "-target-feature",
-                        "-Xclang", "-packed-fp32-ops", "-O3", "-std=c++17", "--cuda-device-only", "-c",
-                        os.path.join(CSRC, src), "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"],
+def device_flags():
+    spec = importlib.util.spec_from_file_location("pa_build", os.path.join(ROOT, "paged_kv_cache_57_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.DEVICE_FLAGS
+
+
+def compile_device(src, extra):
+    r = subprocess.run(["/opt/rocm/bin/hipcc", "-x", "hip", *device_flags(), "-O3", "-std=c++17",
+                        "--cuda-device-only", os.path.join(CSRC, src), *extra],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-3000:]
+    return r
+
+
+@pytest.mark.parametrize("src", ["pa_attention.hip", "pa_cache.hip"])
+def test_no_register_spills(src):
+    r = compile_device(src, ["-c", "-o", os.devnull, "-Rpass-analysis=kernel-resource-usage"])
     names = re.findall(r"Function Name: (\S+)", r.stderr)
     spills = [int(x) for x in re.findall(r"VGPRs Spill: (\d+)", r.stderr)]
     sspills = [int(x) for x in re.findall(r"SGPRs Spill: (\d+)", r.stderr)]
@@ -25,3 +45,21 @@ def test_no_register_spills(src):
     bad = [n for n, v, s in zip(names, spills, sspills) if v or s]
     assert not bad, f"kernels with spills: {bad}"
     assert not any(scratch), "kernels using scratch memory"
+
+
+def test_workers_have_no_per_lane_branches(tmp_path):
+    asm = tmp_path / "attn.s"
+    compile_device("pa_attention.hip", ["-S", "-o", str(asm)])
+    text = asm.read_text()
+    bodies = re.findall(r"^(_Z\S+):.*?^\.Lfunc_end", text, flags=re.S | re.M)
+    funcs = re.split(r"^(?=_Z\S+:)", text, flags=re.M)
+    checked = 0
+    for f in funcs:
+        m = re.match(r"(_Z\S+):", f)
+        if not m or not re.search(r"(valu_attn|mfma_attn|merge)_kernel", m.group(1)):
+            continue
+        body = f.split(".Lfunc_end")[0]
+        n = len(re.findall(r"\bs_and_saveexec_b64|\bs_andn2_saveexec_b64|\bs_or_saveexec_b64", body))
+        assert n == 0, f"{m.group(1)} has {n} exec-mask regions"
+        checked += 1
+    assert checked >= 6 and bodies is not None
