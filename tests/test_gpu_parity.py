@@ -137,7 +137,7 @@ def test_tiny_decode_fp32(pa):
 # have no per-lane branches (checked on the compiled code by
 # test_kernel_resources).  float32 with head_dim 128 stays unsupported: its
 # kernel needed more registers than it could hold without spilling.
-REJECTED = {1: "float32 attention takes head_dim 64 only"}
+REJECTED = {1: "float32 attention supports head_dim 64 only"}
 
 RAGGED = [
     # dtype, Hq, Hkv, d, q_lens, ctx_lens
