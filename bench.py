@@ -160,13 +160,38 @@ def cpu_baseline(w, q, kc, vc, budget_s):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def copy_calibration(torch, dev, args, nbytes=4 << 30):
+    """Device-to-device copy of a 4 GiB buffer: achievable HBM bandwidth, and the
+    known-size kernel that scales the FETCH_SIZE / WRITE_SIZE counters."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    gbps = 2 * nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": "device copy GB/s (read + write)", "value": round(gbps, 1), "unit": "GB/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                      "data": "synthetic", "config": {"workload": "copy_4GiB", "bytes_read": nbytes,
+                                                      "bytes_written": nbytes},
+                      "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="splitfuse",
-                    choices=["splitfuse", "llama7b", "gqa70b", "gqa70b_long", "tiny"])
+                    choices=["splitfuse", "llama7b", "gqa70b", "gqa70b_long", "tiny", "copy"])
     ap.add_argument("--rotate", type=int, default=0, help="pool copies cycled per step (0: enough to exceed the 256 MB MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -182,6 +207,8 @@ def main():
     import workloads as W
 
     dev = torch.device("cuda:0")
+    if args.workload == "copy":
+        return copy_calibration(torch, dev, args)
     w = build_workload(args.workload)
     code = pa.PA_BF16 if w.dtype == "bf16" else pa.PA_F32
     q, kc, vc, nk, nv = W.make_values(w, dev)

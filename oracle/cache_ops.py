@@ -27,10 +27,14 @@ import numpy as np
 from .layout import BLOCK, set_key_row, set_value_row
 
 
-def reshape_and_cache(key, value, k_pool, v_pool, slot_mapping):
-    """Return new pools with token rows of ``key``/``value`` [T, Hkv, d] stored at their slots."""
-    k_pool = np.array(k_pool, copy=True)
-    v_pool = np.array(v_pool, copy=True)
+def reshape_and_cache(key, value, k_pool, v_pool, slot_mapping, inplace=False):
+    """Pools with token rows of ``key``/``value`` [T, Hkv, d] stored at their slots.
+
+    Returns new pools, or writes into the given ones when ``inplace``.
+    """
+    if not inplace:
+        k_pool = np.array(k_pool, copy=True)
+        v_pool = np.array(v_pool, copy=True)
     nb, hkv = k_pool.shape[0], k_pool.shape[1]
     slots = np.asarray(slot_mapping, dtype=np.int64)
     live = slots[slots >= 0]
@@ -48,10 +52,11 @@ def reshape_and_cache(key, value, k_pool, v_pool, slot_mapping):
     return k_pool, v_pool
 
 
-def copy_blocks(k_pool, v_pool, pairs):
-    """Return new pools where every destination block holds a copy of its source block."""
-    k_pool = np.array(k_pool, copy=True)
-    v_pool = np.array(v_pool, copy=True)
+def copy_blocks(k_pool, v_pool, pairs, inplace=False):
+    """Pools where every destination block holds a copy of its source block (new, or in place)."""
+    if not inplace:
+        k_pool = np.array(k_pool, copy=True)
+        v_pool = np.array(v_pool, copy=True)
     pairs = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
     nb = k_pool.shape[0]
     if pairs.size:

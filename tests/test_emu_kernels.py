@@ -114,3 +114,16 @@ def test_out_of_range_ids_are_flagged_and_skipped(emu):
     kp, vp = empty_pools(np.random.default_rng(4), "f32", w.num_blocks, 2, 64)
     _, st = emu.forward(w, np.zeros((1, 2, 64), np.float32), kp, vp)
     assert st == 1
+
+
+def test_parallel_sampling_workflow_emulated(emu):
+    # reduced workflow through the emulated kernels and libpa's C++ allocator
+    import workloads as W
+    from tests._lib import ensure_built
+    from tests._sampling import EmuBackend, run_workflow
+    ensure_built()
+    import paged_kv_cache_57_amd as pa
+    spec = W.parallel_sampling_spec(0, prompts=2, lo=20, hi=60, branches=3, steps=20, num_blocks=64,
+                                    heads=2, head_dim=64)
+    worst, copies = run_workflow(EmuBackend(pa, spec), spec, checkpoints={0, 1, 7, 19}, say=lambda *_: None)
+    assert worst <= 1.0 and copies > 0

@@ -255,3 +255,15 @@ def test_splitfuse_mixed_pass(pa):
     # both prefill chunks (all 1024 rows) plus a spread of decode rows, after the cache write
     w = W.splitfuse_mixed(0)
     run_and_check(pa, w, seqs=[0, 1, 2, 3, 500, 1025])
+
+
+def test_parallel_sampling_workflow(pa):
+    # 16 prompts x 4 branches sharing prompt pages, copy-on-write at step 0, 256 decode steps;
+    # slots, copy pairs and tables checked every step, pool bytes and outputs at checkpoints
+    from tests._sampling import GpuBackend, run_workflow
+    spec = W.parallel_sampling_spec(0)
+    say(f"[case] parallel sampling: prompts {list(spec.prompt_lens)} x {spec.branches} branches, "
+        f"{spec.steps} steps, NB={spec.num_blocks}")
+    worst, copies = run_workflow(GpuBackend(pa, spec), spec, checkpoints={0, 1, 15, 16, 17, 255}, say=say)
+    say(f"  copy-on-write pairs: {copies}; worst err/bound {worst:.3f}")
+    assert copies > 0

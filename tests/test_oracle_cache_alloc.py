@@ -206,3 +206,17 @@ def test_bf16_widening_matches_torch_and_known_encodings():
     bits = bits[(bits & 0x7F80) != 0x7F80]                     # skip inf / nan encodings
     ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     assert np.array_equal(layout.to_f64(bits, "bf16"), ref)
+
+
+def test_inplace_cache_ops_match_functional_ones():
+    rng = np.random.default_rng(4)
+    kp, vp = empty_pools(rng, "bf16", 5, 2, 64)
+    key = raw(rng.standard_normal((7, 2, 64)).astype(np.float32), "bf16")
+    slots = np.array([3, 17, 40, -1, 79, 0, 33])
+    k1, v1 = cache_ops.reshape_and_cache(key, key, kp, vp, slots)
+    k2, v2 = kp.copy(), vp.copy()
+    cache_ops.reshape_and_cache(key, key, k2, v2, slots, inplace=True)
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+    k3, v3 = cache_ops.copy_blocks(k1, v1, [(1, 4)])
+    cache_ops.copy_blocks(k2, v2, [(1, 4)], inplace=True)
+    assert np.array_equal(k3, k2) and np.array_equal(v3, v2)
