@@ -10,10 +10,11 @@
 //    them, and turns every sequence into work items.  An item is a key
 //    partition (a fixed range of key positions) of either
 //      - one query row and one query head (VALU class: float32 batches and
-//        bfloat16 single-row decodes with one query head per KV head), or
+//        bfloat16 single-row decodes with one query head per KV head),
 //      - a tile of 16 query rows that share one KV head (MFMA class: bfloat16
-//        GQA decodes, whose G query heads become the rows, and bfloat16
-//        prefill chunks, whose positions x G heads become the rows).
+//        sequences with at most 16 rows, where a row is one query position
+//        of one of the G query heads of a KV head, e.g. GQA decodes), or
+//      - a tile of 128 such rows (TILE class: bfloat16 prefill chunks).
 //    Partition sizes depend only on the sequence's own lengths, so a
 //    sequence's result does not depend on the rest of the batch.
 //  * Persistent workers walk the items with a fixed stride (wave w takes
@@ -28,6 +29,7 @@
 //    The pages name split-K decoding for long contexts ("大模型部署.md" §2.5
 //    item 2, TurboMind) without giving its math; this merge is the
 //    rescaling rule above.
+#include <algorithm>
 #include <cmath>
 
 #include "pa_device.h"
@@ -36,12 +38,17 @@
 namespace pa {
 namespace {
 
-enum { CLS_NONE = 0, CLS_VALU = 1, CLS_MFMA = 2 };
+enum { CLS_NONE = 0, CLS_VALU = 1, CLS_MFMA = 2, CLS_TILE = 3 };
 constexpr int kPartValu = 512;          // keys per VALU partition
 constexpr int kPartMfmaDecode = 256;    // keys per partition of a one-row GQA decode tile
-constexpr int kPartMfmaPrefill = 1024;  // keys per partition of a prefill tile
+constexpr int kPartMfmaPrefill = 1024;  // keys per partition of a small multi-row tile
+constexpr int kPartTile = 1024;         // keys per partition of a 128-row tile
 constexpr int kTileRows = 16;           // query rows per MFMA item
+constexpr int kTileWaves = 4;           // wavefronts per TILE workgroup, 32 rows each
+constexpr int kBigRows = 32 * kTileWaves;  // query rows per TILE item
 constexpr int kMaxWorkerGroups = 2048;  // persistent workgroups per worker launch
+constexpr int kMaxTileGroups = 512;     // TILE workgroups (two per compute unit)
+constexpr float kLazyRescale = 8.f;     // TILE: raise the exponent reference only past this growth (log2)
 constexpr float kNegInf = -INFINITY;
 
 // floats per partial state: O[D], m, l, padded to keep 16-byte alignment
@@ -57,14 +64,19 @@ struct SeqWork {
 __host__ __device__ inline SeqWork seq_work(bool is_f32, int G, int Hq, int Hkv, int q_len, int L) {
   SeqWork w{CLS_NONE, 1, 0, 0};
   if (q_len <= 0 || L <= 0) return w;
+  const int rows = q_len * G;  // rows of one KV head: positions x query heads of the group
   if (is_f32 || (G == 1 && q_len == 1)) {
     w.cls = CLS_VALU;
     w.part = kPartValu;
     w.groups = q_len * Hq;
-  } else {
+  } else if (rows <= kTileRows) {
     w.cls = CLS_MFMA;
     w.part = q_len == 1 ? kPartMfmaDecode : kPartMfmaPrefill;
-    w.groups = ((q_len * G + kTileRows - 1) / kTileRows) * Hkv;
+    w.groups = Hkv;
+  } else {
+    w.cls = CLS_TILE;
+    w.part = kPartTile;
+    w.groups = ((rows + kBigRows - 1) / kBigRows) * Hkv;
   }
   w.nparts = (L + w.part - 1) / w.part;
   return w;
@@ -73,7 +85,8 @@ __host__ __device__ inline SeqWork seq_work(bool is_f32, int G, int Hq, int Hkv,
 // Smallest partition any sequence of this batch can use (bounds the partial states).
 inline int min_part(bool is_f32, int G) {
   if (is_f32) return kPartValu;
-  return G == 1 ? kPartValu : kPartMfmaDecode;
+  const int m = G == 1 ? kPartValu : kPartMfmaDecode;
+  return std::min(m, std::min(kPartMfmaPrefill, kPartTile));
 }
 
 struct AttnParams {
@@ -89,9 +102,10 @@ struct AttnParams {
   int32_t Hq, Hkv, G, num_blocks;
   float scale_log2;
   int32_t is_f32;
-  int32_t* ctrl;  // [2] VALU items, [3] MFMA items
+  int32_t* ctrl;  // [2] VALU items, [3] MFMA items, [4] TILE items
   int32_t* pre_v;
   int32_t* pre_m;
+  int32_t* pre_t;
   float* partials;  // [T][Hq][maxparts][D + 4]: O (unnormalised), m, l, 2 pad
   int32_t maxparts;
   int32_t* dev_status;
@@ -126,17 +140,17 @@ __device__ inline int find_seq(const int32_t* pre, int n, int x) {
 
 // ---------------------------------------------------------------- planner
 __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
-  __shared__ int sv[1024], sm[1024];
-  __shared__ int carry_v, carry_m;
+  __shared__ int sv[1024], sm[1024], st[1024];
+  __shared__ int carry_v, carry_m, carry_t;
   const int tid = threadIdx.x;
   if (tid == 0) {
-    carry_v = carry_m = 0;
+    carry_v = carry_m = carry_t = 0;
     if (p.qsl[0] != 0 || p.qsl[p.num_seqs] != p.T) flag_status(p.dev_status, PA_DEV_BAD_LENGTH);
   }
   __syncthreads();
   for (int base = 0; base < p.num_seqs; base += 1024) {
     const int s = base + tid;
-    int iv = 0, im = 0;
+    int iv = 0, im = 0, it = 0;
     if (s < p.num_seqs) {
       const SeqInfo si = read_seq(p, s);
       if (!si.ok) {
@@ -146,35 +160,43 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
         const int items = w.groups * w.nparts;
         if (w.cls == CLS_VALU) iv = items;
         else if (w.cls == CLS_MFMA) im = items;
+        else if (w.cls == CLS_TILE) it = items;
       }
     }
     sv[tid] = iv;
     sm[tid] = im;
+    st[tid] = it;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {
       const int xv = tid >= off ? sv[tid - off] : 0;
       const int xm = tid >= off ? sm[tid - off] : 0;
+      const int xt = tid >= off ? st[tid - off] : 0;
       __syncthreads();
       sv[tid] += xv;
       sm[tid] += xm;
+      st[tid] += xt;
       __syncthreads();
     }
     if (s < p.num_seqs) {
       p.pre_v[s] = carry_v + sv[tid] - iv;
       p.pre_m[s] = carry_m + sm[tid] - im;
+      p.pre_t[s] = carry_t + st[tid] - it;
     }
     __syncthreads();
     if (tid == 1023) {
       carry_v += sv[1023];
       carry_m += sm[1023];
+      carry_t += st[1023];
     }
     __syncthreads();
   }
   if (tid == 0) {
     p.pre_v[p.num_seqs] = carry_v;
     p.pre_m[p.num_seqs] = carry_m;
+    p.pre_t[p.num_seqs] = carry_t;
     p.ctrl[2] = carry_v;
     p.ctrl[3] = carry_m;
+    p.ctrl[4] = carry_t;
   }
 }
 
@@ -552,6 +574,246 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(AttnParams p) {
   }
 }
 
+// ---------------------------------------------------------------- TILE worker
+// One workgroup per item: kBigRows query rows sharing one KV head x one key
+// partition.  Each wavefront owns 32 rows (two 16-row MFMA tiles) and the
+// products and operand layouts are those of the MFMA worker above.  Keys
+// advance 32 at a time (two pages): while the wavefronts compute on one half
+// of a double-buffered LDS area, every thread has already loaded its share of
+// the next step's two key pages and two value pages and stores them into the
+// other half afterwards, so each key and value is read from memory once per
+// item and from LDS by every wavefront.
+// The exponent reference of a row is raised only when the row's maximum grows
+// by more than kLazyRescale (base 2): all weights stay below 2^kLazyRescale,
+// O and l share the reference, and O / l is unchanged.
+// Workgroup g takes items g, g + grid, g + 2 grid, ...  (A shared counter
+// bumped once per item was tried: at one atomic per lane, 64 per item, the
+// same-address atomics serialised and made the kernel six times slower.)
+template <int D>
+__global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParams p) {
+  constexpr int KS = D / 32;                 // k-steps of the score product
+  constexpr int NJ = D / 16;                 // 16-dim column blocks of the output
+  constexpr int PAGE16 = kBlock * D / 8;     // 16-byte pieces per page
+  constexpr int STEP16 = 4 * PAGE16;         // key page 0, key page 1, value page 0, value page 1
+  constexpr int NT = 64 * kTileWaves;        // threads
+  constexpr int CPT = STEP16 / NT;           // pieces each thread copies per step
+  static_assert(STEP16 % NT == 0 && PAGE16 % 64 == 0, "a copy round stays inside one page per wavefront");
+  static_assert(kPartTile % 32 == 0 && kPartTile <= 64 * kBlock, "a partition is whole steps of at most 64 pages");
+  __shared__ u32x4 stage[2][STEP16];
+
+  const int lane = threadIdx.x & 63;
+  const int wv = wave_uniform((int)(threadIdx.x >> 6));
+  const int r = lane & 15, g4 = lane >> 4;
+  const int total = wave_uniform(p.ctrl[4]);
+  const bf16_t* __restrict__ kc = (const bf16_t*)p.k_cache;
+  const bf16_t* __restrict__ vc = (const bf16_t*)p.v_cache;
+  const int64_t page_elems = (int64_t)kBlock * D;
+
+  for (int item = (int)blockIdx.x; item < total; item += (int)gridDim.x) {
+
+    const int s = wave_uniform(find_seq(p.pre_t, p.num_seqs, item));
+    const int local = item - wave_uniform(p.pre_t[s]);
+    SeqInfo si = read_seq(p, s);
+    si.a = wave_uniform(si.a);
+    si.q_len = wave_uniform(si.q_len);
+    si.L = wave_uniform(si.L);
+    const SeqWork w = seq_work(false, p.G, p.Hq, p.Hkv, si.q_len, si.L);
+    const int pidx = local % w.nparts;
+    const int rest = local / w.nparts;
+    const int kvh = rest % p.Hkv;
+    const int tile = rest / p.Hkv;
+    const int rows_total = si.q_len * p.G;
+    const int first = si.L - si.q_len;  // position of query row 0
+    const int tile_last = min(tile * kBigRows + kBigRows - 1, rows_total - 1);
+    const int kv_lo = pidx * w.part;
+    const int kv_hi = min(kv_lo + w.part, first + tile_last / p.G + 1);
+    if (kv_lo >= kv_hi) continue;  // no row of the tile sees this partition: the merge skips it
+
+    // this wavefront's rows; padding rows repeat the last row (see the MFMA worker)
+    const int row0 = tile * kBigRows + 32 * wv;
+    const bool active = row0 < rows_total;
+    const int w_pos_lo = first + min(row0, rows_total - 1) / p.G;
+    const int w_kv_hi = min(kv_hi, first + min(row0 + 31, rows_total - 1) / p.G + 1);
+    int pos_r[2], tok[2], hh[2];
+    bf16x8 qop[2][KS];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int R = min(row0 + 16 * t + r, rows_total - 1);
+      const int qi = R / p.G;
+      hh[t] = kvh * p.G + R % p.G;
+      tok[t] = si.a + qi;
+      pos_r[t] = first + qi;
+      const bf16_t* qrow = (const bf16_t*)p.q + ((int64_t)tok[t] * p.Hq + hh[t]) * D;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) qop[t][k] = __builtin_bit_cast(bf16x8, ld16(qrow + 32 * k + 8 * g4));
+    }
+
+    const int nblk = (kv_hi - kv_lo + kBlock - 1) / kBlock;
+    const int bidv = load_block_ids(p, s, kv_lo / kBlock, nblk, lane);
+    const int nsteps = (kv_hi - kv_lo + 31) / 32;
+
+    // one step's pages: thread piece c = threadIdx.x + i * NT lies in page c / PAGE16
+    // (wave-uniform), 16 bytes at offset c % PAGE16
+    u32x4 nxt[CPT];
+    auto fetch = [&](int st) {
+      const int j0 = 2 * st;
+      const int bid0 = readlane(bidv, j0);
+      const int bid1 = j0 + 1 < nblk ? readlane(bidv, j0 + 1) : bid0;
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int c = (int)threadIdx.x + i * NT;
+        const int region = c / PAGE16;
+        const bf16_t* base = region < 2 ? kc : vc;
+        const int bid = (region & 1) ? bid1 : bid0;
+        nxt[i] = ld16(base + ((int64_t)bid * p.Hkv + kvh) * page_elems + (int64_t)(c % PAGE16) * 8);
+      }
+    };
+    auto put = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) stage[buf][threadIdx.x + i * NT] = nxt[i];
+    };
+
+    float m_used[2] = {kNegInf, kNegInf}, lsum[2] = {0.f, 0.f};
+    f32x4 oacc[2][NJ];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) oacc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    fetch(0);
+    put(0);
+    __syncthreads();
+    for (int st = 0; st < nsteps; ++st) {
+      const int kbase = kv_lo + 32 * st;
+      const bool more = st + 1 < nsteps;
+      if (more) fetch(st + 1);
+      if (active && kbase < w_kv_hi) {
+        const u32x4* ks = stage[st & 1];
+        const u32x4* vs = stage[st & 1] + 2 * PAGE16;
+        bf16x8 kop[2][KS];
+#pragma unroll
+        for (int pg = 0; pg < 2; ++pg)
+#pragma unroll
+          for (int k = 0; k < KS; ++k) kop[pg][k] = __builtin_bit_cast(bf16x8, ks[pg * PAGE16 + (4 * k + g4) * kBlock + r]);
+        f32x4 c[2][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int pg = 0; pg < 2; ++pg) {
+            c[t][pg] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < KS; ++k)
+              c[t][pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[pg][k], qop[t][k], c[t][pg], 0, 0, 0);
+          }
+        // scores of row r of tile t for keys kbase + 16 * (e >> 2) + 4 * g4 + (e & 3)
+        float sc[2][8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sc[t][e] = c[t][e >> 2][e & 3] * p.scale_log2;
+        if (kbase + 31 > w_pos_lo) {  // some key of the step lies past some row's position
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int key = kbase + (e >> 2) * kBlock + 4 * g4 + (e & 3);
+              sc[t][e] = key <= pos_r[t] ? sc[t][e] : kNegInf;
+            }
+        }
+        float mloc[2];
+        bool grow = false;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float mx = sc[t][0];
+#pragma unroll
+          for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[t][e]);
+          mx = fmaxf(mx, shfl_xor_f(mx, 16));
+          mx = fmaxf(mx, shfl_xor_f(mx, 32));
+          mloc[t] = mx;
+          grow = grow || mx > m_used[t] + kLazyRescale;
+        }
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const float m_new = fmaxf(m_used[t], mloc[t]);
+            const float alpha = m_new == kNegInf ? 1.f : exp2f(m_used[t] - m_new);
+            lsum[t] *= alpha;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) oacc[t][j] *= alpha;
+            m_used[t] = m_new;
+          }
+        }
+        bf16x8 phi[2], plo[2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const float mu = m_used[t] == kNegInf ? 0.f : m_used[t];  // a row that sees no key yet has weights 0
+          uint32_t hw4[4], lw4[4];
+          float ps = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float p0 = exp2f(sc[t][e] - mu), p1 = exp2f(sc[t][e + 1] - mu);
+            const uint32_t hw = pack_bf16x2(p0, p1);
+            hw4[e >> 1] = hw;
+            lw4[e >> 1] = pack_bf16x2(p0 - bf16_lo(hw), p1 - bf16_hi(hw));
+            ps += p0 + p1;
+          }
+          lsum[t] += ps;
+          phi[t] = __builtin_bit_cast(bf16x8, u32x4{hw4[0], hw4[1], hw4[2], hw4[3]});
+          plo[t] = __builtin_bit_cast(bf16x8, u32x4{lw4[0], lw4[1], lw4[2], lw4[3]});
+        }
+        const bool vtail = kbase + 32 > si.L;  // keys past the context may hold anything (even NaN)
+        const char* vb = (const char*)vs;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const int off = (16 * j + r) * 32 + 8 * g4;  // dim 16j + r, keys 4 * g4 .. + 3 of a value page
+          const u32x2 v0 = *reinterpret_cast<const u32x2*>(vb + off);
+          const u32x2 v1 = *reinterpret_cast<const u32x2*>(vb + PAGE16 * 16 + off);
+          uint32_t vw[4] = {v0[0], v0[1], v1[0], v1[1]};
+          if (vtail) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const int key = kbase + (e >> 2) * kBlock + 4 * g4 + (e & 3);
+              const uint32_t keep = (e & 1) ? 0x0000ffffu : 0xffff0000u;
+              vw[e >> 1] = key < si.L ? vw[e >> 1] : (vw[e >> 1] & keep);
+            }
+          }
+          const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{vw[0], vw[1], vw[2], vw[3]});
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            oacc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[t], oacc[t][j], 0, 0, 0);
+            oacc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[t], oacc[t][j], 0, 0, 0);
+          }
+        }
+      }
+      if (more) put((st + 1) & 1);
+      __syncthreads();
+    }
+
+    if (active) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float l = lsum[t] + shfl_xor_f(lsum[t], 16);
+        l += shfl_xor_f(l, 32);
+        if (w.nparts == 1) {
+          bf16_t* orow = (bf16_t*)p.out + ((int64_t)tok[t] * p.Hq + hh[t]) * D;
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const u32x2 pk = {pack_bf16x2(oacc[t][j][0] / l, oacc[t][j][1] / l),
+                              pack_bf16x2(oacc[t][j][2] / l, oacc[t][j][3] / l)};
+            *reinterpret_cast<u32x2*>(orow + 16 * j + 4 * g4) = pk;
+          }
+        } else {
+          float* slot = p.partials + (((int64_t)tok[t] * p.Hq + hh[t]) * p.maxparts + pidx) * slot_floats(D);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) *reinterpret_cast<f32x4*>(slot + 16 * j + 4 * g4) = oacc[t][j];
+          slot[D] = m_used[t];
+          slot[D + 1] = l;
+        }
+      }
+    }
+  }
+}
+
 // ---------------------------------------------------------------- merge
 // One wavefront per (query token, query head) whose context was split.
 template <typename T, int D>
@@ -605,7 +867,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
 
 // ---------------------------------------------------------------- host side
 struct WsLayout {
-  size_t ctrl, pre_v, pre_m, partials, total;
+  size_t ctrl, pre_v, pre_m, pre_t, partials, total;
   int maxparts;
 };
 
@@ -619,7 +881,8 @@ WsLayout ws_layout(int S, int T, int Hq, int Hkv, int D, int max_ctx, bool is_f3
   l.ctrl = 0;
   l.pre_v = 256;
   l.pre_m = l.pre_v + align256((size_t)(S + 1) * 4);
-  l.partials = l.pre_m + align256((size_t)(S + 1) * 4);
+  l.pre_t = l.pre_m + align256((size_t)(S + 1) * 4);
+  l.partials = l.pre_t + align256((size_t)(S + 1) * 4);
   const size_t part_bytes = l.maxparts > 1 ? (size_t)T * Hq * l.maxparts * slot_floats(D) * 4 : 0;
   l.total = l.partials + align256(part_bytes);
   return l;
@@ -636,8 +899,8 @@ inline void mark(int stage, int edge, hipStream_t stream) {
 }
 
 template <typename T, int D>
-void launch_attention(const AttnParams& p, bool may_valu, bool may_mfma, int grid_v, int grid_m,
-                      hipStream_t stream) {
+void launch_attention(const AttnParams& p, bool may_valu, bool may_mfma, bool may_tile, int grid_v,
+                      int grid_m, int grid_t, hipStream_t stream) {
   mark(0, 0, stream);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, p);
   mark(0, 1, stream);
@@ -648,6 +911,8 @@ void launch_attention(const AttnParams& p, bool may_valu, bool may_mfma, int gri
   mark(2, 0, stream);
   if constexpr (sizeof(T) == 2) {
     if (may_mfma) hipLaunchKernelGGL((mfma_attn_kernel<D>), dim3(grid_m), dim3(256), 0, stream, p);
+    if (may_tile)
+      hipLaunchKernelGGL((tile_attn_kernel<D>), dim3(grid_t), dim3(64 * kTileWaves), 0, stream, p);
   }
   mark(2, 1, stream);
   mark(3, 0, stream);
@@ -743,26 +1008,30 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
   p.ctrl = (int32_t*)(ws + wl.ctrl);
   p.pre_v = (int32_t*)(ws + wl.pre_v);
   p.pre_m = (int32_t*)(ws + wl.pre_m);
+  p.pre_t = (int32_t*)(ws + wl.pre_t);
   p.partials = (float*)(ws + wl.partials);
   p.maxparts = wl.maxparts;
   p.dev_status = dev_status;
 
   // Which worker classes can receive items (decided from host-known bounds only).
   const bool may_valu = is_f32 || p.G == 1;
-  const bool may_mfma = !is_f32 && (p.G > 1 || max_q_len > 1);
+  const bool may_mfma = !is_f32 && p.G <= kTileRows && (p.G > 1 || max_q_len > 1);
+  const bool may_tile = !is_f32 && (int64_t)max_q_len * p.G > kTileRows;
   const int64_t bound_v = (int64_t)total_q_tokens * num_q_heads * wl.maxparts;
-  const int64_t bound_m =
-      ((int64_t)total_q_tokens * p.G / kTileRows + num_seqs) * num_kv_heads * wl.maxparts;
+  const int64_t bound_m = (int64_t)num_seqs * num_kv_heads * wl.maxparts;
+  const int64_t bound_t =
+      ((int64_t)total_q_tokens * p.G / kBigRows + num_seqs) * num_kv_heads * wl.maxparts;
   const int grid_v = (int)std::min<int64_t>(kMaxWorkerGroups, (bound_v + 3) / 4);
   const int grid_m = (int)std::min<int64_t>(kMaxWorkerGroups, (bound_m + 3) / 4);
+  const int grid_t = (int)std::min<int64_t>(kMaxTileGroups, bound_t);
 
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   if (is_f32) {
-    launch_attention<float, 64>(p, may_valu, false, grid_v, grid_m, s);
+    launch_attention<float, 64>(p, may_valu, false, false, grid_v, grid_m, grid_t, s);
   } else {
-    if (head_dim == 64) launch_attention<bf16_t, 64>(p, may_valu, may_mfma, grid_v, grid_m, s);
-    else launch_attention<bf16_t, 128>(p, may_valu, may_mfma, grid_v, grid_m, s);
+    if (head_dim == 64) launch_attention<bf16_t, 64>(p, may_valu, may_mfma, may_tile, grid_v, grid_m, grid_t, s);
+    else launch_attention<bf16_t, 128>(p, may_valu, may_mfma, may_tile, grid_v, grid_m, grid_t, s);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));

@@ -151,6 +151,9 @@ RAGGED = [
     ("bf16", 8, 8, 128, [37, 1, 16, 1], [37, 900, 1100, 2]),      # prefill tiles (prior 0 and 1084)
     ("bf16", 16, 4, 128, [9, 3, 1], [2100, 3, 64]),               # GQA prefill: rows = positions x heads
     ("bf16", 4, 4, 64, [70, 1], [1500, 5]),                       # prefill crossing partitions of 1024
+    ("bf16", 8, 8, 128, [300, 1], [2500, 40]),                    # 128-row tiles: 3 tiles, last one 44 rows
+    ("bf16", 16, 2, 64, [40, 17], [40, 1100]),                    # GQA tiles: 320 and 136 rows
+    ("bf16", 4, 4, 128, [129, 128, 2], [129, 1152, 2]),           # tile edges: 129 and 128 rows, 2-row MFMA
 ]
 
 

@@ -56,10 +56,10 @@ def test_workers_have_no_per_lane_branches(tmp_path):
     checked = 0
     for f in funcs:
         m = re.match(r"(_Z\S+):", f)
-        if not m or not re.search(r"(valu_attn|mfma_attn|merge)_kernel", m.group(1)):
+        if not m or not re.search(r"(valu_attn|mfma_attn|tile_attn|merge)_kernel", m.group(1)):
             continue
         body = f.split(".Lfunc_end")[0]
         n = len(re.findall(r"\bs_and_saveexec_b64|\bs_andn2_saveexec_b64|\bs_or_saveexec_b64", body))
         assert n == 0, f"{m.group(1)} has {n} exec-mask regions"
         checked += 1
-    assert checked >= 6 and bodies is not None
+    assert checked >= 8 and bodies is not None
