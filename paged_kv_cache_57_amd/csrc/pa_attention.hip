@@ -49,6 +49,7 @@ constexpr int kBigRows = 32 * kTileWaves;  // query rows per TILE item
 constexpr int kMaxWorkerGroups = 2048;  // persistent workgroups per worker launch
 constexpr int kMaxTileGroups = 512;     // TILE workgroups (two per compute unit)
 constexpr float kLazyRescale = 8.f;     // TILE: raise the exponent reference only past this growth (log2)
+constexpr int kMergeSplitParts = 32;    // partitions per row from which four wavefronts merge a row
 constexpr float kNegInf = -INFINITY;
 
 // floats per partial state: O[D], m, l, padded to keep 16-byte alignment
@@ -102,10 +103,12 @@ struct AttnParams {
   int32_t Hq, Hkv, G, num_blocks;
   float scale_log2;
   int32_t is_f32;
-  int32_t* ctrl;  // [2] VALU items, [3] MFMA items, [4] TILE items
-  int32_t* pre_v;
-  int32_t* pre_m;
-  int32_t* pre_t;
+  int32_t* ctrl;  // [2] VALU items, [3] MFMA items, [4] TILE items, [5] rows to merge
+  int32_t* pre_v;  // exclusive prefix over sequences of VALU items, [S + 1]
+  int32_t* pre_m;  // ... of MFMA items
+  int32_t* pre_t;  // ... of TILE items
+  int32_t* pre_g;  // ... of (query token, query head) rows whose context was split
+  i32x4* seqinfo;  // per sequence: first query row, q_len, context length, 1 if valid
   float* partials;  // [T][Hq][maxparts][D + 4]: O (unnormalised), m, l, 2 pad
   int32_t maxparts;
   int32_t* dev_status;
@@ -116,6 +119,7 @@ struct SeqInfo {
   bool ok;
 };
 
+// Checks one sequence's row range and length against the host-known bounds.
 __device__ inline SeqInfo read_seq(const AttnParams& p, int s) {
   SeqInfo si;
   si.a = p.qsl[s];
@@ -127,76 +131,145 @@ __device__ inline SeqInfo read_seq(const AttnParams& p, int s) {
   return si;
 }
 
-// Largest s in [0, n) with pre[s] <= x (pre non-decreasing, pre[0] <= x < pre[n]).
-__device__ inline int find_seq(const int32_t* pre, int n, int x) {
-  int lo = 0, hi = n;
+// The planner's record of sequence s, as wave-uniform values (one 16-byte load).
+__device__ inline SeqInfo seq_record(const AttnParams& p, int s) {
+  const i32x4 v = p.seqinfo[s];
+  SeqInfo si;
+  si.a = __builtin_amdgcn_readfirstlane(v[0]);
+  si.q_len = __builtin_amdgcn_readfirstlane(v[1]);
+  si.L = __builtin_amdgcn_readfirstlane(v[2]);
+  si.ok = __builtin_amdgcn_readfirstlane(v[3]) != 0;
+  return si;
+}
+
+// Item -> sequence lookup.  Every workgroup of a worker first copies every
+// stride-th entry of the item prefix array into LDS (at most kSkip entries;
+// stride 1 for batches of fewer than kSkip sequences), so that finding the
+// sequence of an item costs LDS probes instead of a chain of dependent
+// global loads; only batches larger than kSkip sequences finish the search
+// in global memory, inside one stride.
+constexpr int kSkip = 2048;
+
+struct SkipTable {
+  int stride, count;
+};
+
+__device__ inline SkipTable stage_skip(int* sk, const int32_t* pre, int n) {
+  SkipTable t;
+  t.stride = (n + kSkip) / kSkip;  // ceil((n + 1) / kSkip)
+  t.count = n / t.stride + 1;      // entries i * stride <= n
+  for (int i0 = 0; i0 < t.count; i0 += (int)blockDim.x) {
+    const int i = min(i0 + (int)threadIdx.x, t.count - 1);  // threads past the end repeat the last entry
+    sk[i] = pre[i * t.stride];
+  }
+  __syncthreads();
+  return t;
+}
+
+struct SeqHit {
+  int s, first;  // sequence, and pre[s]: its first item
+};
+
+// Largest s in [0, n) with pre[s] <= x, for pre non-decreasing with
+// pre[0] <= x < pre[n] and x wave-uniform.
+__device__ inline SeqHit find_seq(const int* sk, SkipTable t, const int32_t* pre, int n, int x) {
+  int lo = 0, hi = t.count, vlo = 0;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (pre[mid] <= x) lo = mid;
-    else hi = mid;
+    const int v = __builtin_amdgcn_readfirstlane(sk[mid]);
+    if (v <= x) {
+      lo = mid;
+      vlo = v;
+    } else {
+      hi = mid;
+    }
   }
-  return lo;
+  vlo = __builtin_amdgcn_readfirstlane(sk[lo]);
+  int a = lo * t.stride, b = min(a + t.stride, n);
+  while (b - a > 1) {
+    const int mid = (a + b) >> 1;
+    const int v = pre[mid];
+    if (v <= x) {
+      a = mid;
+      vlo = v;
+    } else {
+      b = mid;
+    }
+  }
+  return SeqHit{a, vlo};
 }
 
 // ---------------------------------------------------------------- planner
+// One workgroup: checks every sequence, records it, and writes the exclusive
+// prefix sums of its items per worker class and of its rows to merge.
+__device__ inline i32x4 wave_incl_scan(i32x4 v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    i32x4 y;
+    y[0] = __shfl_up(v[0], o, 64);
+    y[1] = __shfl_up(v[1], o, 64);
+    y[2] = __shfl_up(v[2], o, 64);
+    y[3] = __shfl_up(v[3], o, 64);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
 __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
-  __shared__ int sv[1024], sm[1024], st[1024];
-  __shared__ int carry_v, carry_m, carry_t;
-  const int tid = threadIdx.x;
+  __shared__ i32x4 wsum[16];
+  __shared__ i32x4 carry;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (tid == 0) {
-    carry_v = carry_m = carry_t = 0;
+    carry = i32x4{0, 0, 0, 0};
     if (p.qsl[0] != 0 || p.qsl[p.num_seqs] != p.T) flag_status(p.dev_status, PA_DEV_BAD_LENGTH);
   }
   __syncthreads();
   for (int base = 0; base < p.num_seqs; base += 1024) {
     const int s = base + tid;
-    int iv = 0, im = 0, it = 0;
+    i32x4 cnt = {0, 0, 0, 0};  // VALU, MFMA, TILE items, rows to merge
     if (s < p.num_seqs) {
       const SeqInfo si = read_seq(p, s);
+      p.seqinfo[s] = i32x4{si.a, si.q_len, si.L, si.ok ? 1 : 0};
       if (!si.ok) {
         flag_status(p.dev_status, PA_DEV_BAD_LENGTH);
       } else {
         const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L);
         const int items = w.groups * w.nparts;
-        if (w.cls == CLS_VALU) iv = items;
-        else if (w.cls == CLS_MFMA) im = items;
-        else if (w.cls == CLS_TILE) it = items;
+        if (w.cls == CLS_VALU) cnt[0] = items;
+        else if (w.cls == CLS_MFMA) cnt[1] = items;
+        else if (w.cls == CLS_TILE) cnt[2] = items;
+        if (w.nparts > 1) cnt[3] = si.q_len * p.Hq;
       }
     }
-    sv[tid] = iv;
-    sm[tid] = im;
-    st[tid] = it;
+    const i32x4 inc = wave_incl_scan(cnt, lane);
+    if (lane == 63) wsum[wv] = inc;
     __syncthreads();
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int xv = tid >= off ? sv[tid - off] : 0;
-      const int xm = tid >= off ? sm[tid - off] : 0;
-      const int xt = tid >= off ? st[tid - off] : 0;
-      __syncthreads();
-      sv[tid] += xv;
-      sm[tid] += xm;
-      st[tid] += xt;
-      __syncthreads();
-    }
+    i32x4 before = carry;
+    for (int k = 0; k < wv; ++k) before += wsum[k];
     if (s < p.num_seqs) {
-      p.pre_v[s] = carry_v + sv[tid] - iv;
-      p.pre_m[s] = carry_m + sm[tid] - im;
-      p.pre_t[s] = carry_t + st[tid] - it;
+      const i32x4 ex = before + inc - cnt;
+      p.pre_v[s] = ex[0];
+      p.pre_m[s] = ex[1];
+      p.pre_t[s] = ex[2];
+      p.pre_g[s] = ex[3];
     }
     __syncthreads();
-    if (tid == 1023) {
-      carry_v += sv[1023];
-      carry_m += sm[1023];
-      carry_t += st[1023];
+    if (tid == 0) {
+      i32x4 tot = carry;
+      for (int k = 0; k < 16; ++k) tot += wsum[k];
+      carry = tot;
     }
     __syncthreads();
   }
   if (tid == 0) {
-    p.pre_v[p.num_seqs] = carry_v;
-    p.pre_m[p.num_seqs] = carry_m;
-    p.pre_t[p.num_seqs] = carry_t;
-    p.ctrl[2] = carry_v;
-    p.ctrl[3] = carry_m;
-    p.ctrl[4] = carry_t;
+    p.pre_v[p.num_seqs] = carry[0];
+    p.pre_m[p.num_seqs] = carry[1];
+    p.pre_t[p.num_seqs] = carry[2];
+    p.pre_g[p.num_seqs] = carry[3];
+    p.ctrl[2] = carry[0];
+    p.ctrl[3] = carry[1];
+    p.ctrl[4] = carry[2];
+    p.ctrl[5] = carry[3];
   }
 }
 
@@ -247,23 +320,23 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
   constexpr int NIV = D / RPI;   // value loads per page
   constexpr bool kBf16 = sizeof(T) == 2;
   __shared__ float lds_p[4][64];
+  __shared__ int skip[kSkip];
 
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
   const int wave_id = wave_uniform((int)(blockIdx.x * 4 + wv));
   const int nwaves = (int)gridDim.x * 4;
   const int total = wave_uniform(p.ctrl[2]);
+  const SkipTable tab = stage_skip(skip, p.pre_v, p.num_seqs);
   const T* __restrict__ kc = (const T*)p.k_cache;
   const T* __restrict__ vc = (const T*)p.v_cache;
   const int64_t page_elems = (int64_t)kBlock * D;
 
   for (int item = wave_id; item < total; item += nwaves) {
-    const int s = wave_uniform(find_seq(p.pre_v, p.num_seqs, item));
-    const int local = item - wave_uniform(p.pre_v[s]);
-    SeqInfo si = read_seq(p, s);
-    si.a = wave_uniform(si.a);
-    si.q_len = wave_uniform(si.q_len);
-    si.L = wave_uniform(si.L);
+    const SeqHit hit = find_seq(skip, tab, p.pre_v, p.num_seqs, item);
+    const int s = hit.s;
+    const int local = item - hit.first;
+    const SeqInfo si = seq_record(p, s);
     const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L);
     const int pidx = local % w.nparts;
     const int rh = local / w.nparts;
@@ -340,8 +413,8 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
         sc = (base + lane < kv_hi) ? sc * p.scale_log2 : kNegInf;
 
         const float m_new = fmaxf(m, wave_max(sc));  // finite: key `base` is visible
-        const float alpha = exp2f(m - m_new);
-        const float pr = exp2f(sc - m_new);
+        const float alpha = fast_exp2(m - m_new);
+        const float pr = fast_exp2(sc - m_new);
         lsum = lsum * alpha + pr;
         m = m_new;
 #pragma unroll
@@ -416,7 +489,7 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
 //  running sum adds exactly those parts, so the result stays a convex
 //  combination of the value rows with weights accurate to ~2^-16.
 template <int D>
-__global__ __launch_bounds__(256) void mfma_attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
   constexpr int KS = D / 32;  // k-steps of the score product
   constexpr int NJ = D / 16;  // 16-dim column blocks of the output
   const int lane = threadIdx.x & 63;
@@ -427,14 +500,14 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(AttnParams p) {
   const bf16_t* __restrict__ kc = (const bf16_t*)p.k_cache;
   const bf16_t* __restrict__ vc = (const bf16_t*)p.v_cache;
   const int64_t page_elems = (int64_t)kBlock * D;
+  __shared__ int skip[kSkip];
+  const SkipTable tab = stage_skip(skip, p.pre_m, p.num_seqs);
 
   for (int item = wave_id; item < total; item += nwaves) {
-    const int s = wave_uniform(find_seq(p.pre_m, p.num_seqs, item));
-    const int local = item - wave_uniform(p.pre_m[s]);
-    SeqInfo si = read_seq(p, s);
-    si.a = wave_uniform(si.a);
-    si.q_len = wave_uniform(si.q_len);
-    si.L = wave_uniform(si.L);
+    const SeqHit hit = find_seq(skip, tab, p.pre_m, p.num_seqs, item);
+    const int s = hit.s;
+    const int local = item - hit.first;
+    const SeqInfo si = seq_record(p, s);
     const SeqWork w = seq_work(false, p.G, p.Hq, p.Hkv, si.q_len, si.L);
     const int pidx = local % w.nparts;
     const int rest = local / w.nparts;
@@ -470,36 +543,50 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(AttnParams p) {
         for (int k = 0; k < KS; ++k) qop[k] = __builtin_bit_cast(bf16x8, ld16(qrow + 32 * k + 8 * g4));
       }
 
-      for (int base = kv_lo; base < kv_hi; base += 32) {
+      // A step covers two pages.  A missing second page (odd page count)
+      // reads the first page again: its scores are masked and its values
+      // zeroed below, and the address stays inside the pool.  Key pages are
+      // loaded one step ahead; a step's value pages load while its scores
+      // and weights are computed.
+      struct KeyOps {
+        bf16x8 k0[KS], k1[KS];
+      };
+      auto page_offsets = [&](int base, int64_t& pg0, int64_t& pg1) {
         const int jb = (base - kv_lo) >> 4;
-        const bool has1 = base + kBlock < kv_hi;
-        const int bid0 = readlane(bidv, jb);
-        const int bid1 = has1 ? readlane(bidv, jb + 1) : bid0;
-        const int64_t pg0 = ((int64_t)bid0 * p.Hkv + kvh) * page_elems;
-        const int64_t pg1 = ((int64_t)bid1 * p.Hkv + kvh) * page_elems;
-        bf16x8 kop0[KS], kop1[KS];
+        pg0 = ((int64_t)readlane(bidv, jb) * p.Hkv + kvh) * page_elems;
+        pg1 = ((int64_t)readlane(bidv, min(jb + 1, nblk - 1)) * p.Hkv + kvh) * page_elems;
+      };
+      auto load_keys = [&](int base, KeyOps& o) {
+        int64_t pg0, pg1;
+        page_offsets(base, pg0, pg1);
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
           const int off = ((4 * k + g4) * kBlock + r) * 8;
-          kop0[k] = __builtin_bit_cast(bf16x8, ld16(kc + pg0 + off));
-          kop1[k] = __builtin_bit_cast(bf16x8, has1 ? ld16(kc + pg1 + off) : u32x4{0, 0, 0, 0});
+          o.k0[k] = __builtin_bit_cast(bf16x8, ld16(kc + pg0 + off));
+          o.k1[k] = __builtin_bit_cast(bf16x8, ld16(kc + pg1 + off));
         }
+      };
+      auto step = [&](int base, const KeyOps& ko) {
         uint32_t vw[NJ][4];  // value operand words: keys 4*g4 + 0..3 of page 0, then of page 1
+        {
+          int64_t pg0, pg1;
+          page_offsets(base, pg0, pg1);
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int off = (16 * j + r) * kBlock + 4 * g4;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vc + pg0 + off);
-          const u32x2 hi = has1 ? *reinterpret_cast<const u32x2*>(vc + pg1 + off) : u32x2{0, 0};
-          vw[j][0] = lo[0];
-          vw[j][1] = lo[1];
-          vw[j][2] = hi[0];
-          vw[j][3] = hi[1];
+          for (int j = 0; j < NJ; ++j) {
+            const int off = (16 * j + r) * kBlock + 4 * g4;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vc + pg0 + off);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vc + pg1 + off);
+            vw[j][0] = lo[0];
+            vw[j][1] = lo[1];
+            vw[j][2] = hi[0];
+            vw[j][3] = hi[1];
+          }
         }
         f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-          c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop0[k], qop[k], c0, 0, 0, 0);
-          c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop1[k], qop[k], c1, 0, 0, 0);
+          c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ko.k0[k], qop[k], c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ko.k1[k], qop[k], c1, 0, 0, 0);
         }
         // scores of row r for keys base + 16a + 4*g4 + e
         float sc[8];
@@ -515,15 +602,15 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(AttnParams p) {
         mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
         const float m_new = fmaxf(m_r, mloc);
         const bool none = m_new == kNegInf;  // the row sees no key yet
-        const float alpha = none ? 1.f : exp2f(m_r - m_new);
+        const float alpha = none ? 1.f : fast_exp2(m_r - m_new);
         // P enters the product as hi + lo bfloat16 parts (two MFMAs), so each
         // weight keeps about 16 mantissa bits instead of 8.
         uint32_t phw[4], plw[4];
         float psum = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const float p0 = none ? 0.f : exp2f(sc[e] - m_new);
-          const float p1 = none ? 0.f : exp2f(sc[e + 1] - m_new);
+          const float p0 = none ? 0.f : fast_exp2(sc[e] - m_new);
+          const float p1 = none ? 0.f : fast_exp2(sc[e + 1] - m_new);
           const uint32_t hw = pack_bf16x2(p0, p1);
           const float r0 = p0 - bf16_lo(hw), r1 = p1 - bf16_hi(hw);
           const uint32_t lw = pack_bf16x2(r0, r1);
@@ -551,8 +638,25 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(AttnParams p) {
           oacc[j] *= alpha;
           const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{vw[j][0], vw[j][1], vw[j][2], vw[j][3]});
           oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_hi, oacc[j], 0, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{vw[j][0], vw[j][1], vw[j][2], vw[j][3]});
           oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo, oacc[j], 0, 0, 0);
         }
+      };
+      // two key register sets, swapped every step
+      KeyOps ka, kb;
+      load_keys(kv_lo, ka);
+      for (int base = kv_lo;;) {
+        if (base + 32 < kv_hi) load_keys(base + 32, kb);
+        step(base, ka);
+        base += 32;
+        if (base >= kv_hi) break;
+        if (base + 32 < kv_hi) load_keys(base + 32, ka);
+        step(base, kb);
+        base += 32;
+        if (base >= kv_hi) break;
       }
     }
     float l = lsum + shfl_xor_f(lsum, 16);
@@ -576,16 +680,27 @@ __global__ __launch_bounds__(256) void mfma_attn_kernel(AttnParams p) {
 
 // ---------------------------------------------------------------- TILE worker
 // One workgroup per item: kBigRows query rows sharing one KV head x one key
-// partition.  Each wavefront owns 32 rows (two 16-row MFMA tiles) and the
-// products and operand layouts are those of the MFMA worker above.  Keys
-// advance 32 at a time (two pages): while the wavefronts compute on one half
-// of a double-buffered LDS area, every thread has already loaded its share of
-// the next step's two key pages and two value pages and stores them into the
+// partition.  Each wavefront owns 32 rows (two 16-row MFMA tiles); the score
+// and output products are those of the MFMA worker above.  Keys advance 32 at
+// a time (two pages): while the wavefronts compute on one half of a
+// double-buffered LDS area, every thread has already loaded its share of the
+// next step's two key pages and two value pages and stores them into the
 // other half afterwards, so each key and value is read from memory once per
 // item and from LDS by every wavefront.
-// The exponent reference of a row is raised only when the row's maximum grows
-// by more than kLazyRescale (base 2): all weights stay below 2^kLazyRescale,
-// O and l share the reference, and O / l is unchanged.
+//  LDS layout of one step: the two key pages as they are in memory, then the
+//  values rearranged so that lane l = r + 16 g of a wavefront finds its MFMA
+//  operand for output columns 16j..16j+15 — value column 16j + r at keys
+//  4g..4g+3 of page 0 followed by the same keys of page 1 — as the 16-byte
+//  piece (4j + g) * 16 + r.  Both operand reads are then 64 consecutive
+//  16-byte pieces in lane order, free of bank conflicts.  Values of keys at
+//  or past the item's last visible key are stored as zero, so key pages past
+//  the context (which may hold anything, even NaN) never reach the output.
+// Scores stay unscaled until the exponent: p = 2^(s·c − m) with
+// c = |scale|·log2 e is one FMA per score (a negative scale flips the sign
+// bits of q instead, which is exact).  The exponent reference m of a row is
+// raised only when the row's maximum grows past it by more than kLazyRescale:
+// all weights stay below 2^kLazyRescale, O and l share the reference, and
+// O / l is unchanged.
 // Workgroup g takes items g, g + grid, g + 2 grid, ...  (A shared counter
 // bumped once per item was tried: at one atomic per lane, 64 per item, the
 // same-address atomics serialised and made the kernel six times slower.)
@@ -594,7 +709,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
   constexpr int KS = D / 32;                 // k-steps of the score product
   constexpr int NJ = D / 16;                 // 16-dim column blocks of the output
   constexpr int PAGE16 = kBlock * D / 8;     // 16-byte pieces per page
-  constexpr int STEP16 = 4 * PAGE16;         // key page 0, key page 1, value page 0, value page 1
+  constexpr int STEP16 = 4 * PAGE16;         // key page 0, key page 1, values of both pages
   constexpr int NT = 64 * kTileWaves;        // threads
   constexpr int CPT = STEP16 / NT;           // pieces each thread copies per step
   static_assert(STEP16 % NT == 0 && PAGE16 % 64 == 0, "a copy round stays inside one page per wavefront");
@@ -608,15 +723,16 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
   const bf16_t* __restrict__ kc = (const bf16_t*)p.k_cache;
   const bf16_t* __restrict__ vc = (const bf16_t*)p.v_cache;
   const int64_t page_elems = (int64_t)kBlock * D;
+  const float csc = fmaxf(fabsf(p.scale_log2), 1e-30f);  // scale 0 gives equal weights, as it should
+  const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+  __shared__ int skip[kSkip];
+  const SkipTable tab = stage_skip(skip, p.pre_t, p.num_seqs);
 
   for (int item = (int)blockIdx.x; item < total; item += (int)gridDim.x) {
-
-    const int s = wave_uniform(find_seq(p.pre_t, p.num_seqs, item));
-    const int local = item - wave_uniform(p.pre_t[s]);
-    SeqInfo si = read_seq(p, s);
-    si.a = wave_uniform(si.a);
-    si.q_len = wave_uniform(si.q_len);
-    si.L = wave_uniform(si.L);
+    const SeqHit hit = find_seq(skip, tab, p.pre_t, p.num_seqs, item);
+    const int s = hit.s;
+    const int local = item - hit.first;
+    const SeqInfo si = seq_record(p, s);
     const SeqWork w = seq_work(false, p.G, p.Hq, p.Hkv, si.q_len, si.L);
     const int pidx = local % w.nparts;
     const int rest = local / w.nparts;
@@ -645,15 +761,19 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
       pos_r[t] = first + qi;
       const bf16_t* qrow = (const bf16_t*)p.q + ((int64_t)tok[t] * p.Hq + hh[t]) * D;
 #pragma unroll
-      for (int k = 0; k < KS; ++k) qop[t][k] = __builtin_bit_cast(bf16x8, ld16(qrow + 32 * k + 8 * g4));
+      for (int k = 0; k < KS; ++k) {
+        const u32x4 qw = ld16(qrow + 32 * k + 8 * g4);
+        qop[t][k] = __builtin_bit_cast(bf16x8, u32x4{qw[0] ^ qflip, qw[1] ^ qflip, qw[2] ^ qflip, qw[3] ^ qflip});
+      }
     }
 
     const int nblk = (kv_hi - kv_lo + kBlock - 1) / kBlock;
     const int bidv = load_block_ids(p, s, kv_lo / kBlock, nblk, lane);
     const int nsteps = (kv_hi - kv_lo + 31) / 32;
 
-    // one step's pages: thread piece c = threadIdx.x + i * NT lies in page c / PAGE16
-    // (wave-uniform), 16 bytes at offset c % PAGE16
+    // Piece i of this thread is c = 64 wv + lane + i NT: region c / PAGE16
+    // (wave-uniform: key page 0, key page 1, value page 0, value page 1) at
+    // 16-byte offset c % PAGE16 inside the page.
     u32x4 nxt[CPT];
     auto fetch = [&](int st) {
       const int j0 = 2 * st;
@@ -661,16 +781,41 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
       const int bid1 = j0 + 1 < nblk ? readlane(bidv, j0 + 1) : bid0;
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const int c = (int)threadIdx.x + i * NT;
-        const int region = c / PAGE16;
+        const int region = (64 * wv + i * NT) / PAGE16;
+        const int q16 = (64 * wv + i * NT) % PAGE16 + lane;
         const bf16_t* base = region < 2 ? kc : vc;
         const int bid = (region & 1) ? bid1 : bid0;
-        nxt[i] = ld16(base + ((int64_t)bid * p.Hkv + kvh) * page_elems + (int64_t)(c % PAGE16) * 8);
+        nxt[i] = ld16(base + ((int64_t)bid * p.Hkv + kvh) * page_elems + (int64_t)q16 * 8);
       }
     };
-    auto put = [&](int buf) {
+    auto put = [&](int buf, int st) {
+      const int kb = kv_lo + 32 * st;
+      const bool vtail = kb + 32 > kv_hi;  // workgroup-uniform
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) stage[buf][threadIdx.x + i * NT] = nxt[i];
+      for (int i = 0; i < CPT; ++i) {
+        const int region = (64 * wv + i * NT) / PAGE16;
+        const int q16 = (64 * wv + i * NT) % PAGE16 + lane;
+        if (region < 2) {
+          stage[buf][region * PAGE16 + q16] = nxt[i];
+        } else {
+          // value page piece: column d = q16 / 2, keys 8h .. 8h + 7 of the page
+          const int pg = region - 2, d = q16 >> 1, h = q16 & 1;
+          u32x4 v = nxt[i];
+          if (vtail) {
+            const int k0 = kb + kBlock * pg + 8 * h;  // key of element 0
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t lo = k0 + 2 * e < kv_hi ? 0x0000ffffu : 0u;
+              const uint32_t hi = k0 + 2 * e + 1 < kv_hi ? 0xffff0000u : 0u;
+              v[e] &= lo | hi;
+            }
+          }
+          char* vb = (char*)&stage[buf][2 * PAGE16];
+          const int p0 = ((d >> 4) * 4 + 2 * h) * 16 + (d & 15);
+          *reinterpret_cast<u32x2*>(vb + p0 * 16 + pg * 8) = u32x2{v[0], v[1]};
+          *reinterpret_cast<u32x2*>(vb + (p0 + 16) * 16 + pg * 8) = u32x2{v[2], v[3]};
+        }
+      }
     };
 
     float m_used[2] = {kNegInf, kNegInf}, lsum[2] = {0.f, 0.f};
@@ -681,7 +826,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
       for (int j = 0; j < NJ; ++j) oacc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     fetch(0);
-    put(0);
+    put(0, 0);
     __syncthreads();
     for (int st = 0; st < nsteps; ++st) {
       const int kbase = kv_lo + 32 * st;
@@ -690,27 +835,26 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
       if (active && kbase < w_kv_hi) {
         const u32x4* ks = stage[st & 1];
         const u32x4* vs = stage[st & 1] + 2 * PAGE16;
-        bf16x8 kop[2][KS];
-#pragma unroll
-        for (int pg = 0; pg < 2; ++pg)
-#pragma unroll
-          for (int k = 0; k < KS; ++k) kop[pg][k] = __builtin_bit_cast(bf16x8, ks[pg * PAGE16 + (4 * k + g4) * kBlock + r]);
         f32x4 c[2][2];
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int pg = 0; pg < 2; ++pg) {
+          bf16x8 kop[KS];
 #pragma unroll
-          for (int pg = 0; pg < 2; ++pg) {
+          for (int k = 0; k < KS; ++k) kop[k] = __builtin_bit_cast(bf16x8, ks[pg * PAGE16 + (4 * k + g4) * kBlock + r]);
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
             c[t][pg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k = 0; k < KS; ++k)
-              c[t][pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[pg][k], qop[t][k], c[t][pg], 0, 0, 0);
+              c[t][pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[k], qop[t][k], c[t][pg], 0, 0, 0);
           }
-        // scores of row r of tile t for keys kbase + 16 * (e >> 2) + 4 * g4 + (e & 3)
+        }
+        // unscaled scores of row r of tile t for keys kbase + 16 * (e >> 2) + 4 * g4 + (e & 3)
         float sc[2][8];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sc[t][e] = c[t][e >> 2][e & 3] * p.scale_log2;
+          for (int e = 0; e < 8; ++e) sc[t][e] = c[t][e >> 2][e & 3];
         if (kbase + 31 > w_pos_lo) {  // some key of the step lies past some row's position
 #pragma unroll
           for (int t = 0; t < 2; ++t)
@@ -724,19 +868,18 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
         bool grow = false;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          float mx = sc[t][0];
-#pragma unroll
-          for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sc[t][e]);
+          float mx = fmaxf(fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])),
+                           fmaxf(fmaxf(sc[t][4], sc[t][5]), fmaxf(sc[t][6], sc[t][7])));
           mx = fmaxf(mx, shfl_xor_f(mx, 16));
           mx = fmaxf(mx, shfl_xor_f(mx, 32));
-          mloc[t] = mx;
-          grow = grow || mx > m_used[t] + kLazyRescale;
+          mloc[t] = mx * csc;  // -inf stays -inf (csc > 0)
+          grow = grow || mloc[t] > m_used[t] + kLazyRescale;
         }
         if (__builtin_amdgcn_ballot_w64(grow)) {
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             const float m_new = fmaxf(m_used[t], mloc[t]);
-            const float alpha = m_new == kNegInf ? 1.f : exp2f(m_used[t] - m_new);
+            const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_used[t] - m_new);
             lsum[t] *= alpha;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) oacc[t][j] *= alpha;
@@ -746,12 +889,13 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
         bf16x8 phi[2], plo[2];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const float mu = m_used[t] == kNegInf ? 0.f : m_used[t];  // a row that sees no key yet has weights 0
+          const float nmu = m_used[t] == kNegInf ? 0.f : -m_used[t];  // a row that sees no key yet has weights 0
           uint32_t hw4[4], lw4[4];
           float ps = 0.f;
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
-            const float p0 = exp2f(sc[t][e] - mu), p1 = exp2f(sc[t][e + 1] - mu);
+            const float p0 = fast_exp2(fmaf(sc[t][e], csc, nmu));
+            const float p1 = fast_exp2(fmaf(sc[t][e + 1], csc, nmu));
             const uint32_t hw = pack_bf16x2(p0, p1);
             hw4[e >> 1] = hw;
             lw4[e >> 1] = pack_bf16x2(p0 - bf16_lo(hw), p1 - bf16_hi(hw));
@@ -761,31 +905,22 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
           phi[t] = __builtin_bit_cast(bf16x8, u32x4{hw4[0], hw4[1], hw4[2], hw4[3]});
           plo[t] = __builtin_bit_cast(bf16x8, u32x4{lw4[0], lw4[1], lw4[2], lw4[3]});
         }
-        const bool vtail = kbase + 32 > si.L;  // keys past the context may hold anything (even NaN)
-        const char* vb = (const char*)vs;
+        bf16x8 va[NJ];
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int off = (16 * j + r) * 32 + 8 * g4;  // dim 16j + r, keys 4 * g4 .. + 3 of a value page
-          const u32x2 v0 = *reinterpret_cast<const u32x2*>(vb + off);
-          const u32x2 v1 = *reinterpret_cast<const u32x2*>(vb + PAGE16 * 16 + off);
-          uint32_t vw[4] = {v0[0], v0[1], v1[0], v1[1]};
-          if (vtail) {
+        for (int j = 0; j < NJ; ++j) va[j] = __builtin_bit_cast(bf16x8, vs[(4 * j + g4) * 16 + r]);
+        // the high parts first, then the low parts: no MFMA waits on the one before it
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int key = kbase + (e >> 2) * kBlock + 4 * g4 + (e & 3);
-              const uint32_t keep = (e & 1) ? 0x0000ffffu : 0xffff0000u;
-              vw[e >> 1] = key < si.L ? vw[e >> 1] : (vw[e >> 1] & keep);
-            }
-          }
-          const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{vw[0], vw[1], vw[2], vw[3]});
+        for (int j = 0; j < NJ; ++j)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            oacc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[t], oacc[t][j], 0, 0, 0);
-            oacc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[t], oacc[t][j], 0, 0, 0);
-          }
-        }
+          for (int t = 0; t < 2; ++t)
+            oacc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], phi[t], oacc[t][j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int t = 0; t < 2; ++t)
+            oacc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], plo[t], oacc[t][j], 0, 0, 0);
       }
-      if (more) put((st + 1) & 1);
+      if (more) put((st + 1) & 1, st + 1);
       __syncthreads();
     }
 
@@ -815,59 +950,100 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
 }
 
 // ---------------------------------------------------------------- merge
-// One wavefront per (query token, query head) whose context was split.
-template <typename T, int D>
+// Persistent workgroups walk the planner's list of (query token, query head)
+// rows whose context was split, WPR wavefronts per row.  A
+// lane covers four output columns of one partition, so one 16-byte load per
+// lane reads 64 / (D / 4) partitions at once, and each lane keeps U loads in
+// flight; the WPR wavefronts of a workgroup take interleaved shares of the
+// partitions and add their sums through LDS.  Weights: M = max_p m_p,
+// l = Σ_p l_p 2^(m_p − M), out = Σ_p O_p 2^(m_p − M) / l.
+template <typename T, int D, int WPR>
 __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
+  constexpr int LPP = D / 4;     // lanes per partition
+  constexpr int PPI = 64 / LPP;  // partitions per wavefront load
+  constexpr int U = 4;           // loads in flight per lane
+  constexpr int RPB = 4 / WPR;   // rows merged at once per workgroup
+  constexpr int SF = slot_floats(D);
+  __shared__ f32x4 red[4][64];
+  __shared__ int skip[kSkip];
   const int lane = threadIdx.x & 63;
-  const int rh = wave_uniform((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
-  if (rh >= p.T * p.Hq) return;
-  const int t = rh / p.Hq, h = rh % p.Hq;
-  const int s = wave_uniform(find_seq(p.qsl, p.num_seqs, t));
-  SeqInfo si = read_seq(p, s);
-  si.a = wave_uniform(si.a);
-  si.q_len = wave_uniform(si.q_len);
-  si.L = wave_uniform(si.L);
-  if (!wave_uniform(si.ok) || t < si.a || t >= si.a + si.q_len) return;
-  const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L);
-  if (w.nparts <= 1) return;
-  const int pos = si.L - si.q_len + (t - si.a);
-  const int np = min(w.nparts, pos / w.part + 1);  // later partitions hold no visible key
-  const float* base = p.partials + ((int64_t)t * p.Hq + h) * p.maxparts * slot_floats(D);
-  // lane-strided passes with a uniform trip count; lanes past np read partition 0 and drop it
-  float M = kNegInf;
-  for (int q0 = 0; q0 < np; q0 += 64) {
-    const int q = q0 + lane;
-    const float mq = base[(int64_t)(q < np ? q : 0) * slot_floats(D) + D];
-    M = fmaxf(M, q < np ? mq : kNegInf);
-  }
-  M = wave_max(M);
-  float lsum = 0.f;
-  for (int q0 = 0; q0 < np; q0 += 64) {
-    const int q = q0 + lane;
-    const float* sl = base + (int64_t)(q < np ? q : 0) * slot_floats(D);
-    // M is finite, so 2^(m - M) is 0 for an empty partition (m = -inf) and for lanes past np
-    const float mq = sl[D], lq = sl[D + 1];
-    lsum += lq * exp2f(q < np ? mq - M : kNegInf);
-  }
-  const float l = wave_sum(lsum);
-  constexpr int PER = D / 64;
-  float o[PER];
+  const int wv = wave_uniform((int)(threadIdx.x >> 6));
+  const int sub = wv % WPR;
+  const int total = wave_uniform(p.ctrl[5]);
+  const SkipTable tab = stage_skip(skip, p.pre_g, p.num_seqs);
+  // row g of the merge list; the WPR wavefronts sharing a row see the same g
+  for (int g = (int)blockIdx.x * RPB + wv / WPR; g < total; g += (int)gridDim.x * RPB) {
+    const SeqHit hit = find_seq(skip, tab, p.pre_g, p.num_seqs, g);
+    const SeqInfo si = seq_record(p, hit.s);
+    const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L);
+    const int local = g - hit.first;
+    const int i = local / p.Hq, h = local % p.Hq;
+    const int t = si.a + i;
+    const int pos = si.L - si.q_len + i;
+    const int np = min(w.nparts, pos / w.part + 1);  // later partitions hold no visible key
+    const float* base = p.partials + ((int64_t)t * p.Hq + h) * p.maxparts * SF;
+    // M and l over all partitions; lanes past np read partition 0 and drop it
+    float M = kNegInf;
+    for (int q0 = 0; q0 < np; q0 += 64) {
+      const int q = q0 + lane;
+      const float mq = base[(int64_t)(q < np ? q : 0) * SF + D];
+      M = fmaxf(M, q < np ? mq : kNegInf);
+    }
+    M = wave_max(M);
+    float lsum = 0.f;
+    for (int q0 = 0; q0 < np; q0 += 64) {
+      const int q = q0 + lane;
+      const float* sl = base + (int64_t)(q < np ? q : 0) * SF;
+      // M is finite, so 2^(m - M) is 0 for an empty partition (m = -inf) and for lanes past np
+      const float mq = sl[D], lq = sl[D + 1];
+      lsum += lq * fast_exp2(q < np ? mq - M : kNegInf);
+    }
+    const float l = wave_sum(lsum);
+    // this lane: columns 4c .. 4c + 3 of partitions qo + sub * PPI + k * WPR * PPI
+    const int c = lane % LPP, qo = lane / LPP;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int q0 = sub * PPI; q0 < np; q0 += WPR * PPI * U) {
+      f32x4 o[U];
+      float mq[U];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) o[k] = 0.f;
-  for (int q = 0; q < np; ++q) {
-    const float* sl = base + (int64_t)q * slot_floats(D);
-    const float wq = exp2f(sl[D] - M);  // empty partition: 2^-inf = 0 and O_p = 0
+      for (int u = 0; u < U; ++u) {
+        const int q = q0 + qo + u * WPR * PPI;
+        const float* sl = base + (int64_t)(q < np ? q : 0) * SF;
+        o[u] = *reinterpret_cast<const f32x4*>(sl + 4 * c);
+        mq[u] = sl[D];
+      }
 #pragma unroll
-    for (int k = 0; k < PER; ++k) o[k] = fmaf(sl[lane + 64 * k], wq, o[k]);
+      for (int u = 0; u < U; ++u) {
+        const int q = q0 + qo + u * WPR * PPI;
+        const float wq = fast_exp2(q < np ? mq[u] - M : kNegInf);  // empty partition: weight 0, O_p = 0
+        acc += wq * o[u];
+      }
+    }
+#pragma unroll
+    for (int off = LPP; off < 64; off <<= 1) {
+      acc[0] += shfl_xor_f(acc[0], off);
+      acc[1] += shfl_xor_f(acc[1], off);
+      acc[2] += shfl_xor_f(acc[2], off);
+      acc[3] += shfl_xor_f(acc[3], off);
+    }
+    if constexpr (WPR > 1) {
+      red[wv][lane] = acc;
+      __syncthreads();
+      acc = red[wv - sub][lane];
+#pragma unroll
+      for (int k = 1; k < WPR; ++k) acc += red[wv - sub + k][lane];
+      __syncthreads();  // red is rewritten for the next row
+    }
+    // lanes holding the same columns store the same values
+    T* orow = (T*)p.out + ((int64_t)t * p.Hq + h) * D + 4 * c;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) orow[k] = Elem<T>::from_f32(acc[k] / l);
   }
-  T* orow = (T*)p.out + ((int64_t)t * p.Hq + h) * D;
-#pragma unroll
-  for (int k = 0; k < PER; ++k) orow[lane + 64 * k] = Elem<T>::from_f32(o[k] / l);
 }
 
 // ---------------------------------------------------------------- host side
 struct WsLayout {
-  size_t ctrl, pre_v, pre_m, pre_t, partials, total;
+  size_t ctrl, pre_v, pre_m, pre_t, pre_g, seqinfo, partials, total;
   int maxparts;
 };
 
@@ -882,7 +1058,9 @@ WsLayout ws_layout(int S, int T, int Hq, int Hkv, int D, int max_ctx, bool is_f3
   l.pre_v = 256;
   l.pre_m = l.pre_v + align256((size_t)(S + 1) * 4);
   l.pre_t = l.pre_m + align256((size_t)(S + 1) * 4);
-  l.partials = l.pre_t + align256((size_t)(S + 1) * 4);
+  l.pre_g = l.pre_t + align256((size_t)(S + 1) * 4);
+  l.seqinfo = l.pre_g + align256((size_t)(S + 1) * 4);
+  l.partials = l.seqinfo + align256((size_t)S * 16);
   const size_t part_bytes = l.maxparts > 1 ? (size_t)T * Hq * l.maxparts * slot_floats(D) * 4 : 0;
   l.total = l.partials + align256(part_bytes);
   return l;
@@ -917,8 +1095,14 @@ void launch_attention(const AttnParams& p, bool may_valu, bool may_mfma, bool ma
   mark(2, 1, stream);
   mark(3, 0, stream);
   if (p.maxparts > 1) {
-    const int64_t rows = (int64_t)p.T * p.Hq;
-    hipLaunchKernelGGL((merge_kernel<T, D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, p);
+    // many partitions per row (long contexts): four wavefronts share a row
+    const int64_t rows = (int64_t)p.T * p.Hq;  // bound on the rows to merge
+    if (p.maxparts >= kMergeSplitParts)
+      hipLaunchKernelGGL((merge_kernel<T, D, 4>), dim3((unsigned)std::min<int64_t>(kMaxWorkerGroups, rows)),
+                         dim3(256), 0, stream, p);
+    else
+      hipLaunchKernelGGL((merge_kernel<T, D, 1>), dim3((unsigned)std::min<int64_t>(kMaxWorkerGroups, (rows + 3) / 4)),
+                         dim3(256), 0, stream, p);
   }
   mark(3, 1, stream);
 }
@@ -1009,6 +1193,8 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
   p.pre_v = (int32_t*)(ws + wl.pre_v);
   p.pre_m = (int32_t*)(ws + wl.pre_m);
   p.pre_t = (int32_t*)(ws + wl.pre_t);
+  p.pre_g = (int32_t*)(ws + wl.pre_g);
+  p.seqinfo = (i32x4*)(ws + wl.seqinfo);
   p.partials = (float*)(ws + wl.partials);
   p.maxparts = wl.maxparts;
   p.dev_status = dev_status;

@@ -14,6 +14,7 @@ constexpr int kWave = 64;   // CDNA wavefront width
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -72,6 +73,12 @@ __device__ inline T readlane(T v, int lane) {
 }
 
 __device__ inline float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }
+
+// 2^x with one v_exp_f32.  Results below 2^-126 come out as 0 (exp2f spends
+// five more instructions to produce them as denormals); softmax weights that
+// small relative to the running maximum contribute nothing measurable.
+// 2^-inf = 0, 2^NaN = NaN.
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 __device__ inline float wave_max(float v) {
 #pragma unroll

@@ -9,6 +9,7 @@
 // are still waiting, a barrier was reached by only part of its lanes (a
 // cross-lane operation in divergent code): the emulator aborts and says so.
 #include <sanitizer/common_interface_defs.h>
+#include <setjmp.h>
 #include <ucontext.h>
 
 #include <cstdio>
@@ -41,8 +42,10 @@ struct Wave {
 };
 
 struct Fiber {
-  ucontext_t ctx;
-  std::unique_ptr<char[]> stack;
+  ucontext_t ctx;      // first entry only
+  jmp_buf env;         // where the fiber resumes after it has started
+  bool started = false;
+  char* stack = nullptr;  // from g_stacks, reused by every workgroup
   dim3 tid;
   int wave = 0;
   bool done = false;
@@ -55,6 +58,7 @@ struct Block {
   std::vector<Wave> waves;
   Barrier bar;
   ucontext_t sched;
+  jmp_buf sched_env;  // the scheduler's resumption point (switches use _setjmp/_longjmp: no signal-mask syscall)
   void (*body)(void*) = nullptr;
   void* ctx = nullptr;
   int current = -1;
@@ -63,11 +67,14 @@ struct Block {
 };
 
 Block* g_block = nullptr;
+std::vector<std::unique_ptr<char[]>> g_stacks;  // one per thread slot, kept for the next workgroup
 
 void switch_to_sched(Fiber& f) {
   void* fake = nullptr;
-  __sanitizer_start_switch_fiber(&fake, g_block->sched_stack_bottom, g_block->sched_stack_size);
-  swapcontext(&f.ctx, &g_block->sched);
+  if (_setjmp(f.env) == 0) {
+    __sanitizer_start_switch_fiber(&fake, g_block->sched_stack_bottom, g_block->sched_stack_size);
+    _longjmp(g_block->sched_env, 1);
+  }
   __sanitizer_finish_switch_fiber(fake, nullptr, nullptr);
 }
 
@@ -112,7 +119,7 @@ void fiber_main(unsigned lo, unsigned hi) {
   leave(blk.waves[me.wave].bar);
   leave(blk.bar);
   __sanitizer_start_switch_fiber(nullptr, blk.sched_stack_bottom, blk.sched_stack_size);
-  setcontext(&blk.sched);
+  _longjmp(blk.sched_env, 1);
 }
 
 Wave& my_wave() { return g_block->waves[g_block->fibers[g_block->current].wave]; }
@@ -194,9 +201,10 @@ void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* ctx) {
           Fiber& f = blk.fibers[t];
           f.tid = dim3(t % block.x, (t / block.x) % block.y, t / (block.x * block.y));
           f.wave = t / 64;
-          f.stack.reset(new char[kStack]);
+          if ((int)g_stacks.size() <= t) g_stacks.emplace_back(new char[kStack]);
+          f.stack = g_stacks[t].get();
           getcontext(&f.ctx);
-          f.ctx.uc_stack.ss_sp = f.stack.get();
+          f.ctx.uc_stack.ss_sp = f.stack;
           f.ctx.uc_stack.ss_size = kStack;
           f.ctx.uc_link = nullptr;
           makecontext(&f.ctx, (void (*)())fiber_main, 2, 0u, 0u);
@@ -211,8 +219,15 @@ void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* ctx) {
             if (f.waiting_on && f.waiting_on->phase == f.waiting_phase) continue;
             blk.current = t;
             void* fake = nullptr;
-            __sanitizer_start_switch_fiber(&fake, f.stack.get(), kStack);
-            swapcontext(&blk.sched, &f.ctx);
+            if (_setjmp(blk.sched_env) == 0) {
+              __sanitizer_start_switch_fiber(&fake, f.stack, kStack);
+              if (f.started) {
+                _longjmp(f.env, 1);
+              } else {
+                f.started = true;
+                swapcontext(&blk.sched, &f.ctx);  // first entry; the fiber comes back by _longjmp
+              }
+            }
             __sanitizer_finish_switch_fiber(fake, nullptr, nullptr);
             progressed = true;
           }

@@ -99,6 +99,13 @@ inline T __shfl_xor(T v, int mask, int width = 64) {
   return emu::from_bits<T>(emu::exchange(emu::to_bits(v), emu::tl_lane ^ mask));
 }
 
+template <typename T>
+inline T __shfl_up(T v, unsigned delta, int width = 64) {
+  (void)width;
+  const int src = emu::tl_lane - (int)delta;
+  return emu::from_bits<T>(emu::exchange(emu::to_bits(v), src < 0 ? emu::tl_lane : src));
+}
+
 inline int atomicAdd(int* p, int v) { return __atomic_fetch_add(p, v, __ATOMIC_SEQ_CST); }
 inline int atomicOr(int* p, int v) { return __atomic_fetch_or(p, v, __ATOMIC_SEQ_CST); }
 
@@ -135,5 +142,11 @@ inline F4 emu_mfma(V8 a, V8 b, F4 c, int, int, int) {
 #define __builtin_amdgcn_ballot_w64(p) emu_ballot((p))
 #define __builtin_amdgcn_fdot2_f32_bf16(a, b, c, cl) emu_fdot2((a), (b), (c), (cl))
 #define __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, x, y, z) emu_mfma((a), (b), (c), (x), (y), (z))
+// v_exp_f32: 2^x with results below the smallest normal float flushed to 0
+inline float emu_exp2(float x) {
+  const float r = std::exp2(x);
+  return std::fabs(r) < 1.17549435e-38f ? 0.f : r;
+}
+#define __builtin_amdgcn_exp2f(x) emu_exp2((x))
 #define __builtin_amdgcn_fence(...) ((void)0)
 #define __builtin_amdgcn_wave_barrier() emu::wave_sync()

@@ -14,7 +14,7 @@ from oracle import attention as oattn
 from oracle import cache_ops, layout
 from tests import _emu
 from tests._pools import empty_pools, raw
-from tests.test_gpu_parity import RAGGED, REJECTED
+from tests.test_gpu_parity import RAGGED, REJECTED, many_sequences_batch
 
 pytestmark = pytest.mark.skipif(not _emu.available(), reason="needs the ROCm clang++ for the host build")
 TOL = {"bf16": (2e-3, 1e-2), "f32": (1e-5, 1e-5)}
@@ -45,6 +45,29 @@ def test_ragged_cases_match_oracle(emu, i):
     out, st = emu.forward(w, q, kp, vp)
     assert st == 0
     check(w, q, kp, vp, out, f"ragged[{i}]")
+
+
+@pytest.mark.parametrize("scale", [-0.0625, 0.0, 0.75])
+def test_scale_sign_and_size(emu, scale):
+    w = W.random_ragged(20, "bf16", 8, 2, 64, [1, 40, 1], [300, 170, 45])
+    w.scale = float(np.float32(scale))
+    rng = np.random.default_rng(4)
+    kp, vp = empty_pools(rng, "bf16", w.num_blocks, 2, 64)
+    q = raw(rng.standard_normal((w.num_tokens, 8, 64)).astype(np.float32), "bf16")
+    out, st = emu.forward(w, q, kp, vp)
+    assert st == 0
+    check(w, q, kp, vp, out, f"scale {scale}")
+
+
+def test_many_sequences(emu):
+    # the LDS lookup table holds every second prefix entry; the rest is searched in memory
+    w = many_sequences_batch(2100)
+    rng = np.random.default_rng(5)
+    kp, vp = empty_pools(rng, "bf16", w.num_blocks, 2, 64)
+    q = raw(rng.standard_normal((w.num_tokens, 2, 64)).astype(np.float32), "bf16")
+    out, st = emu.forward(w, q, kp, vp)
+    assert st == 0
+    check(w, q, kp, vp, out, "5000 sequences")
 
 
 def test_float32_head_dim_128_is_rejected(emu):

@@ -154,6 +154,8 @@ RAGGED = [
     ("bf16", 8, 8, 128, [300, 1], [2500, 40]),                    # 128-row tiles: 3 tiles, last one 44 rows
     ("bf16", 16, 2, 64, [40, 17], [40, 1100]),                    # GQA tiles: 320 and 136 rows
     ("bf16", 4, 4, 128, [129, 128, 2], [129, 1152, 2]),           # tile edges: 129 and 128 rows, 2-row MFMA
+    ("bf16", 4, 1, 64, [1, 3], [9000, 8500]),                     # >= 32 partitions: four waves merge a row
+    ("f32", 2, 2, 64, [1, 2], [17000, 40]),                       # the same for float32 (512-key partitions)
 ]
 
 
@@ -172,11 +174,43 @@ def test_ragged_batches(pa, i):
     run_and_check(pa, w, label=f"ragged[{i}] {dt} Hq={hq} Hkv={hkv} d={d} q={ql} L={cl}")
 
 
+def many_sequences_batch(n=5000):
+    """n sequences (more than the 2,047 the workers' LDS lookup table holds one by one):
+    MHA decodes, some split into partitions, plus short prefill rows and empty-query sequences."""
+    rng = np.random.default_rng(31)
+    ql = np.ones(n, np.int64)
+    ql[rng.choice(n, 40, replace=False)] = 0                  # sequences with no query rows this pass
+    ql[rng.choice(n, 20, replace=False)] = 3                  # short prefill rows (MFMA class)
+    cl = rng.integers(1, 90, size=n)
+    cl[rng.choice(n, 12, replace=False)] = rng.integers(600, 1500, size=12)   # split contexts
+    cl = np.maximum(cl, ql)
+    return W.random_ragged(32, "bf16", 2, 2, 64, ql, cl)
+
+
+def test_many_sequences(pa):
+    w = many_sequences_batch()
+    run_and_check(pa, w, label="5000 sequences")
+
+
 def test_nan_poison_outside_context(pa):
     w = W.random_ragged(7, "bf16", 16, 4, 128, [1, 5, 1, 1], [37, 600, 1000, 1])
     run_and_check(pa, w, poison=True, label="nan-poison GQA")
     w = W.random_ragged(8, "bf16", 8, 8, 128, [1, 1, 20], [517, 33, 1025])
     run_and_check(pa, w, poison=True, label="nan-poison MHA")
+
+
+# Scales other than 1/sqrt(d): negative (the tile worker flips the sign of q),
+# zero (every visible key weighs the same) and large (sharp weights).
+SCALES = [-0.0625, 0.0, 0.75]
+
+
+@pytest.mark.parametrize("scale", SCALES)
+def test_scale_sign_and_size(pa, scale):
+    # decode rows (VALU), GQA rows (MFMA) and a 128-row prefill tile (TILE) in two batches
+    for hq, hkv, ql, cl in [(8, 8, [1, 150, 1], [700, 1200, 40]), (16, 4, [1, 40], [300, 1100])]:
+        w = W.random_ragged(20, "bf16", hq, hkv, 128, ql, cl)
+        w.scale = float(np.float32(scale))
+        run_and_check(pa, w, label=f"scale {scale} Hq={hq} Hkv={hkv} q={ql} L={cl}")
 
 
 def test_single_key_and_equal_scores(pa):
