@@ -76,6 +76,37 @@ class HipEvents:
         self.events = []
 
 
+# rocprofv3 kernel names of each worker, for looking up counter results
+DOMINANT_KERNEL = {("valu_worker", "bf16", 128): "valu_attn_kernel<unsigned short, 128>",
+                   ("valu_worker", "bf16", 64): "valu_attn_kernel<unsigned short, 64>",
+                   ("valu_worker", "f32", 64): "valu_attn_kernel<float, 64>",
+                   ("mfma_worker", "bf16", 128): "mfma_attn_kernel<128>",
+                   ("mfma_worker", "bf16", 64): "mfma_attn_kernel<64>",
+                   ("mfma_worker", "f32", 64): "mfma_attn_kernel<64>"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_57_amd", "csrc", "pa_attention.hip")
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from the committed counter runs
+    (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for a copy of known size),
+    or None when there is none or the kernel source changed since it was taken."""
+    import hashlib
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(KERNEL_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    for e in rec.get("entries", []):
+        if e["workload"] == workload and e["kernel"] == kernel:
+            return round(e["fetch_kib"] * 1024 * rec["fetch_scale"] + e["write_kib"] * 1024 * rec["write_scale"])
+    return None
+
+
 def build_workload(name):
     import workloads as W
     return {"splitfuse": lambda: W.splitfuse_mixed(0),
@@ -249,14 +280,20 @@ def main():
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item()):#x}")
 
+    # timed steps: nothing but the path itself on the stream
     K = args.steps
-    stage_ev = [ev.new(2 * len(STAGES)) for _ in range(K)]
-    write_ev = [ev.new(2) for _ in range(K)] if slots is not None else [None] * K
     t0 = time.perf_counter()
     for k in range(K):
-        step(args.warmup + k, stage_ev[k], write_ev[k])
+        step(args.warmup + k)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+
+    # the same steps again with HIP events around every stage (kernel durations)
+    stage_ev = [ev.new(2 * len(STAGES)) for _ in range(K)]
+    write_ev = [ev.new(2) for _ in range(K)] if slots is not None else [None] * K
+    for k in range(K):
+        step(args.warmup + K + k, stage_ev[k], write_ev[k])
+    torch.cuda.synchronize()
     pa.pa_set_stage_events(None)
     stage_ms = {name: float(np.mean([ev.ms(e[2 * j], e[2 * j + 1]) for e in stage_ev]))
                 for j, name in enumerate(STAGES)}
@@ -284,11 +321,13 @@ def main():
                         "block_size": 16, "max_context_len": w.max_context_len, "pool_blocks": w.num_blocks,
                         "pool_copies_rotated": rotate}
     result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                          "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                          "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                          "traffic": measured_traffic(w.name, DOMINANT_KERNEL[(dom, w.dtype, w.head_dim)]),
                           "kernel": dom, "kernel_ms": round(stage_ms[dom], 4), "algorithmic_bytes": dom_bytes}
     result["stages_ms"] = {k: round(v, 4) for k, v in stage_ms.items()}
     if slots is not None:
         result["stages_ms"]["cache_write"] = round(write_ms, 4)
+    result["kv_read_GBps"] = round(pass_bytes / ((stage_ms["valu_worker"] + stage_ms["mfma_worker"]) * 1e-3) / 1e9, 1)
     if valu_bytes:
         result["valu_worker_kv_GBps"] = round(valu_bytes / (stage_ms["valu_worker"] * 1e-3) / 1e9, 1)
     if mfma_bytes and not pre_flops:

@@ -476,7 +476,8 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
 
 // ---------------------------------------------------------------- MFMA worker
 // One wavefront per item: 16 query rows sharing one KV head x one key
-// partition, 32 keys (two pages) per step on v_mfma_f32_16x16x32_bf16.
+// partition, 64 keys (four pages) per step on v_mfma_f32_16x16x32_bf16; all
+// four key and value pages of a step are requested before it computes.
 //  Scores, transposed: Sᵀ[key][row] = K · Qᵀ with K as the A operand (lane l:
 //  key l%16 of the page, 8 head dims per lane, straight from the key page)
 //  and Q as the B operand (lane l: row l%16).  The result gives lane l the
@@ -488,6 +489,10 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
 //  P enters as a bf16 hi part plus a bf16 lo part (two MFMAs), and the
 //  running sum adds exactly those parts, so the result stays a convex
 //  combination of the value rows with weights accurate to ~2^-16.
+// As in the TILE worker, scores stay unscaled until the exponent (one FMA
+// per weight), masks are applied only on steps that reach past the context
+// or past a row's position, and a row's exponent reference is raised only
+// when its maximum grows by more than kLazyRescale.
 template <int D>
 __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
   constexpr int KS = D / 32;  // k-steps of the score product
@@ -500,6 +505,8 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
   const bf16_t* __restrict__ kc = (const bf16_t*)p.k_cache;
   const bf16_t* __restrict__ vc = (const bf16_t*)p.v_cache;
   const int64_t page_elems = (int64_t)kBlock * D;
+  const float csc = fmaxf(fabsf(p.scale_log2), 1e-30f);  // scale 0 gives equal weights, as it should
+  const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
   __shared__ int skip[kSkip];
   const SkipTable tab = stage_skip(skip, p.pre_m, p.num_seqs);
 
@@ -540,123 +547,130 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
       {
         const bf16_t* qrow = (const bf16_t*)p.q + ((int64_t)t * p.Hq + hh) * D;
 #pragma unroll
-        for (int k = 0; k < KS; ++k) qop[k] = __builtin_bit_cast(bf16x8, ld16(qrow + 32 * k + 8 * g4));
+        for (int k = 0; k < KS; ++k) {
+          const u32x4 qw = ld16(qrow + 32 * k + 8 * g4);
+          qop[k] = __builtin_bit_cast(bf16x8, u32x4{qw[0] ^ qflip, qw[1] ^ qflip, qw[2] ^ qflip, qw[3] ^ qflip});
+        }
       }
 
-      // A step covers two pages.  A missing second page (odd page count)
-      // reads the first page again: its scores are masked and its values
-      // zeroed below, and the address stays inside the pool.  Key pages are
-      // loaded one step ahead; a step's value pages load while its scores
-      // and weights are computed.
-      struct KeyOps {
-        bf16x8 k0[KS], k1[KS];
-      };
-      auto page_offsets = [&](int base, int64_t& pg0, int64_t& pg1) {
-        const int jb = (base - kv_lo) >> 4;
-        pg0 = ((int64_t)readlane(bidv, jb) * p.Hkv + kvh) * page_elems;
-        pg1 = ((int64_t)readlane(bidv, min(jb + 1, nblk - 1)) * p.Hkv + kvh) * page_elems;
-      };
-      auto load_keys = [&](int base, KeyOps& o) {
-        int64_t pg0, pg1;
-        page_offsets(base, pg0, pg1);
+      // Pages past the last one (odd counts, the tail) read the last page
+      // again: their scores are masked and their values zeroed, and every
+      // address stays inside the pool.
+      constexpr int NH = 2;  // 32-key halves per step
+      const int pos_lo = si.L - si.q_len + (tile * kTileRows) / p.G;  // lowest row position of the tile
+      for (int base = kv_lo; base < kv_hi; base += 32 * NH) {
+        bf16x8 k0[NH][KS], k1[NH][KS];
+        uint32_t vw[NH][NJ][4];  // value operand words: keys 4*g4 + 0..3 of the half's page 0, then of its page 1
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          const int off = ((4 * k + g4) * kBlock + r) * 8;
-          o.k0[k] = __builtin_bit_cast(bf16x8, ld16(kc + pg0 + off));
-          o.k1[k] = __builtin_bit_cast(bf16x8, ld16(kc + pg1 + off));
-        }
-      };
-      auto step = [&](int base, const KeyOps& ko) {
-        uint32_t vw[NJ][4];  // value operand words: keys 4*g4 + 0..3 of page 0, then of page 1
-        {
-          int64_t pg0, pg1;
-          page_offsets(base, pg0, pg1);
+        for (int hp = 0; hp < NH; ++hp) {
+          const int jb = (base - kv_lo) / kBlock + 2 * hp;
+          const int64_t pg0 = ((int64_t)readlane(bidv, min(jb, nblk - 1)) * p.Hkv + kvh) * page_elems;
+          const int64_t pg1 = ((int64_t)readlane(bidv, min(jb + 1, nblk - 1)) * p.Hkv + kvh) * page_elems;
+#pragma unroll
+          for (int k = 0; k < KS; ++k) {
+            const int off = ((4 * k + g4) * kBlock + r) * 8;
+            k0[hp][k] = __builtin_bit_cast(bf16x8, ld16(kc + pg0 + off));
+            k1[hp][k] = __builtin_bit_cast(bf16x8, ld16(kc + pg1 + off));
+          }
 #pragma unroll
           for (int j = 0; j < NJ; ++j) {
             const int off = (16 * j + r) * kBlock + 4 * g4;
             const u32x2 lo = *reinterpret_cast<const u32x2*>(vc + pg0 + off);
             const u32x2 hi = *reinterpret_cast<const u32x2*>(vc + pg1 + off);
-            vw[j][0] = lo[0];
-            vw[j][1] = lo[1];
-            vw[j][2] = hi[0];
-            vw[j][3] = hi[1];
+            vw[hp][j][0] = lo[0];
+            vw[hp][j][1] = lo[1];
+            vw[hp][j][2] = hi[0];
+            vw[hp][j][3] = hi[1];
           }
         }
-        f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+        // unscaled scores of row r for keys base + 32 hp + 16 (e >> 2) + 4 g4 + (e & 3)
+        float sc[NH][8];
 #pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ko.k0[k], qop[k], c0, 0, 0, 0);
-          c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ko.k1[k], qop[k], c1, 0, 0, 0);
+        for (int hp = 0; hp < NH; ++hp) {
+          f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k = 0; k < KS; ++k) {
+            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[hp][k], qop[k], c0, 0, 0, 0);
+            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[hp][k], qop[k], c1, 0, 0, 0);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sc[hp][e] = c0[e];
+            sc[hp][4 + e] = c1[e];
+          }
         }
-        // scores of row r for keys base + 16a + 4*g4 + e
-        float sc[8];
-        float mloc = kNegInf;
+        const bool edge = base + 32 * NH > kv_hi || base + 32 * NH - 1 > pos_lo;  // wave-uniform
+        if (edge) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int key = base + (e >> 2) * kBlock + 4 * g4 + (e & 3);
-          const float v = (e >> 2) ? c1[e & 3] : c0[e & 3];
-          sc[e] = (key < kv_hi && key <= pos_r) ? v * p.scale_log2 : kNegInf;
-          mloc = fmaxf(mloc, sc[e]);
-        }
-        mloc = fmaxf(mloc, shfl_xor_f(mloc, 16));
-        mloc = fmaxf(mloc, shfl_xor_f(mloc, 32));
-        const float m_new = fmaxf(m_r, mloc);
-        const bool none = m_new == kNegInf;  // the row sees no key yet
-        const float alpha = none ? 1.f : fast_exp2(m_r - m_new);
-        // P enters the product as hi + lo bfloat16 parts (two MFMAs), so each
-        // weight keeps about 16 mantissa bits instead of 8.
-        uint32_t phw[4], plw[4];
-        float psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = none ? 0.f : fast_exp2(sc[e] - m_new);
-          const float p1 = none ? 0.f : fast_exp2(sc[e + 1] - m_new);
-          const uint32_t hw = pack_bf16x2(p0, p1);
-          const float r0 = p0 - bf16_lo(hw), r1 = p1 - bf16_hi(hw);
-          const uint32_t lw = pack_bf16x2(r0, r1);
-          psum += (bf16_lo(hw) + bf16_lo(lw)) + (bf16_hi(hw) + bf16_hi(lw));
-          phw[e >> 1] = hw;
-          plw[e >> 1] = lw;
-        }
-        lsum = lsum * alpha + psum;
-        m_r = m_new;
-        const bf16x8 pop_hi = __builtin_bit_cast(bf16x8, u32x4{phw[0], phw[1], phw[2], phw[3]});
-        const bf16x8 pop_lo = __builtin_bit_cast(bf16x8, u32x4{plw[0], plw[1], plw[2], plw[3]});
-        if (base + 32 > kv_hi) {
-          // keys past kv_hi may hold anything (even NaN): zero them in the value operand
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) {
+          for (int hp = 0; hp < NH; ++hp)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              const int key = base + (e >> 2) * kBlock + 4 * g4 + (e & 3);
-              if (key >= kv_hi) vw[j][e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+              const int key = base + 32 * hp + (e >> 2) * kBlock + 4 * g4 + (e & 3);
+              sc[hp][e] = (key < kv_hi && key <= pos_r) ? sc[hp][e] : kNegInf;
             }
+        }
+        float mx = kNegInf;
+#pragma unroll
+        for (int hp = 0; hp < NH; ++hp)
+          mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sc[hp][0], sc[hp][1]), fmaxf(sc[hp][2], sc[hp][3])),
+                               fmaxf(fmaxf(sc[hp][4], sc[hp][5]), fmaxf(sc[hp][6], sc[hp][7]))));
+        mx = fmaxf(mx, shfl_xor_f(mx, 16));
+        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        const float mloc = mx * csc;  // -inf stays -inf (csc > 0)
+        if (__builtin_amdgcn_ballot_w64(mloc > m_r + kLazyRescale)) {
+          const float m_new = fmaxf(m_r, mloc);
+          const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_r - m_new);
+          lsum *= alpha;
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) oacc[j] *= alpha;
+          m_r = m_new;
+        }
+        const float nmu = m_r == kNegInf ? 0.f : -m_r;  // a row that sees no key yet has weights 0
+        bf16x8 pop_hi[NH], pop_lo[NH];
+        float psum = 0.f;
+#pragma unroll
+        for (int hp = 0; hp < NH; ++hp) {
+          uint32_t phw[4], plw[4];
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const float p0 = fast_exp2(fmaf(sc[hp][e], csc, nmu));
+            const float p1 = fast_exp2(fmaf(sc[hp][e + 1], csc, nmu));
+            const uint32_t hw = pack_bf16x2(p0, p1);
+            phw[e >> 1] = hw;
+            plw[e >> 1] = pack_bf16x2(p0 - bf16_lo(hw), p1 - bf16_hi(hw));
+            psum += p0 + p1;
           }
+          pop_hi[hp] = __builtin_bit_cast(bf16x8, u32x4{phw[0], phw[1], phw[2], phw[3]});
+          pop_lo[hp] = __builtin_bit_cast(bf16x8, u32x4{plw[0], plw[1], plw[2], plw[3]});
         }
+        lsum += psum;
+        if (base + 32 * NH > kv_hi) {
+          // keys past kv_hi may hold anything (even NaN): zero them in the value operand
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          oacc[j] *= alpha;
-          const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{vw[j][0], vw[j][1], vw[j][2], vw[j][3]});
-          oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_hi, oacc[j], 0, 0, 0);
-        }
+          for (int hp = 0; hp < NH; ++hp)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{vw[j][0], vw[j][1], vw[j][2], vw[j][3]});
-          oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo, oacc[j], 0, 0, 0);
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const int key = base + 32 * hp + (e >> 2) * kBlock + 4 * g4 + (e & 3);
+                if (key >= kv_hi) vw[hp][j][e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
+              }
         }
-      };
-      // two key register sets, swapped every step
-      KeyOps ka, kb;
-      load_keys(kv_lo, ka);
-      for (int base = kv_lo;;) {
-        if (base + 32 < kv_hi) load_keys(base + 32, kb);
-        step(base, ka);
-        base += 32;
-        if (base >= kv_hi) break;
-        if (base + 32 < kv_hi) load_keys(base + 32, ka);
-        step(base, kb);
-        base += 32;
-        if (base >= kv_hi) break;
+        // the high parts first, then the low parts: no MFMA waits on the one before it
+#pragma unroll
+        for (int hp = 0; hp < NH; ++hp)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{vw[hp][j][0], vw[hp][j][1], vw[hp][j][2], vw[hp][j][3]});
+            oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_hi[hp], oacc[j], 0, 0, 0);
+          }
+#pragma unroll
+        for (int hp = 0; hp < NH; ++hp)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) {
+            const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{vw[hp][j][0], vw[hp][j][1], vw[hp][j][2], vw[hp][j][3]});
+            oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo[hp], oacc[j], 0, 0, 0);
+          }
       }
     }
     float l = lsum + shfl_xor_f(lsum, 16);
