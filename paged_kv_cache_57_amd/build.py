@@ -19,8 +19,10 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # No packed FP32 instructions; and no atomic optimizer, which wraps each atomic in a
 # branch on the first active lane (the kernels keep their work loops free of
 # lane-dependent branches).
+# -fno-honor-nans: maxima need no NaN quieting first (masked keys are removed by
+# integer compares, selects and bit masks, never by float comparisons).
 DEVICE_FLAGS = ["--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-                "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
+                "-mllvm", "-amdgpu-atomic-optimizer-strategy=None", "-fno-honor-nans"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function"]
 
 

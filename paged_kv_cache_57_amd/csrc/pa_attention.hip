@@ -45,12 +45,15 @@ constexpr int kPartMfmaPrefill = 1024;  // keys per partition of a small multi-r
 constexpr int kPartTile = 1024;         // keys per partition of a 128-row tile
 constexpr int kTileRows = 16;           // query rows per MFMA item
 constexpr int kTileWaves = 4;           // wavefronts per TILE workgroup, 32 rows each
+constexpr int kTileStages = 3;          // LDS stages of the TILE worker's load pipeline
 constexpr int kBigRows = 32 * kTileWaves;  // query rows per TILE item
 constexpr int kMaxWorkerGroups = 2048;  // persistent workgroups per worker launch
 constexpr int kMaxTileGroups = 512;     // TILE workgroups (two per compute unit)
-constexpr float kLazyRescale = 8.f;     // TILE: raise the exponent reference only past this growth (log2)
+constexpr float kLazyRescale = 8.f;     // MFMA worker: raise the exponent reference only past this growth (log2)
+constexpr float kTileLazyRescale = 7.f; // TILE worker: the same, bounded so that 2^8 p stays below the half maximum
 constexpr int kMergeSplitParts = 32;    // partitions per row from which four wavefronts merge a row
 constexpr float kNegInf = -INFINITY;
+
 
 // floats per partial state: O[D], m, l, padded to keep 16-byte alignment
 __host__ __device__ constexpr int slot_floats(int D) { return D + 4; }
@@ -614,8 +617,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
         for (int hp = 0; hp < NH; ++hp)
           mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sc[hp][0], sc[hp][1]), fmaxf(sc[hp][2], sc[hp][3])),
                                fmaxf(fmaxf(sc[hp][4], sc[hp][5]), fmaxf(sc[hp][6], sc[hp][7]))));
-        mx = fmaxf(mx, shfl_xor_f(mx, 16));
-        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+        mx = max_over_rows(mx);
         const float mloc = mx * csc;  // -inf stays -inf (csc > 0)
         if (__builtin_amdgcn_ballot_w64(mloc > m_r + kLazyRescale)) {
           const float m_new = fmaxf(m_r, mloc);
@@ -673,8 +675,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
           }
       }
     }
-    float l = lsum + shfl_xor_f(lsum, 16);
-    l += shfl_xor_f(l, 32);
+    const float l = sum_over_rows(lsum);
     if (w.nparts == 1) {
       bf16_t* orow = (bf16_t*)p.out + ((int64_t)t * p.Hq + hh) * D;
 #pragma unroll
@@ -694,41 +695,44 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
 
 // ---------------------------------------------------------------- TILE worker
 // One workgroup per item: kBigRows query rows sharing one KV head x one key
-// partition.  Each wavefront owns 32 rows (two 16-row MFMA tiles); the score
-// and output products are those of the MFMA worker above.  Keys advance 32 at
-// a time (two pages): while the wavefronts compute on one half of a
-// double-buffered LDS area, every thread has already loaded its share of the
-// next step's two key pages and two value pages and stores them into the
-// other half afterwards, so each key and value is read from memory once per
-// item and from LDS by every wavefront.
-//  LDS layout of one step: the two key pages as they are in memory, then the
-//  values rearranged so that lane l = r + 16 g of a wavefront finds its MFMA
-//  operand for output columns 16j..16j+15 — value column 16j + r at keys
-//  4g..4g+3 of page 0 followed by the same keys of page 1 — as the 16-byte
-//  piece (4j + g) * 16 + r.  Both operand reads are then 64 consecutive
-//  16-byte pieces in lane order, free of bank conflicts.  Values of keys at
-//  or past the item's last visible key are stored as zero, so key pages past
-//  the context (which may hold anything, even NaN) never reach the output.
+// partition.  Each wavefront owns 32 rows (two 16-row MFMA tiles); the
+// products and lane layouts are those of the MFMA worker: lane l = r + 16g
+// holds the scores of its row for keys 8g .. 8g+7 of a 32-key step, key
+// operands come with the permuted row order that gives that layout, and the
+// value operand of lane l is one 16-byte piece of one page.
+// Memory: every thread loads its 16-byte pieces of a step two steps before
+// the step is computed (two register sets) and stores them into a
+// three-stage LDS ring one step before; the LDS image of a step holds the
+// operands in the order the lanes read them (piece 64 i + l is lane l's
+// operand i), so every operand read is 64 consecutive 16-byte pieces and
+// every wavefront reads the same image.  One barrier per step publishes the
+// stored stage and frees the stage read two steps earlier.
 // Scores stay unscaled until the exponent: p = 2^(s·c − m) with
 // c = |scale|·log2 e is one FMA per score (a negative scale flips the sign
 // bits of q instead, which is exact).  The exponent reference m of a row is
-// raised only when the row's maximum grows past it by more than kLazyRescale:
-// all weights stay below 2^kLazyRescale, O and l share the reference, and
-// O / l is unchanged.
+// raised only when the row's maximum grows past it by more than
+// kTileLazyRescale: all weights stay below 2^kTileLazyRescale, O and l share
+// the reference, and O / l is unchanged.
+// P·V runs on the half-precision MFMA: the weights enter as p·2^8 rounded to
+// half (below 2^15; relative error 2^-11, as accurate as splitting p into two
+// bfloat16 parts, with one MFMA instead of two), the values as v·2^-8 in half,
+// converted once per workgroup when a step is stored to LDS (exact for
+// |v| < 2^24 up to an absolute 2^-16 on tiny magnitudes), so the products are
+// p·v.  The row sum l comes from the same MFMA with an all-ones value
+// operand: it adds exactly the rounded weights that P·V used.
 // Workgroup g takes items g, g + grid, g + 2 grid, ...  (A shared counter
 // bumped once per item was tried: at one atomic per lane, 64 per item, the
 // same-address atomics serialised and made the kernel six times slower.)
 template <int D>
 __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParams p) {
-  constexpr int KS = D / 32;                 // k-steps of the score product
-  constexpr int NJ = D / 16;                 // 16-dim column blocks of the output
-  constexpr int PAGE16 = kBlock * D / 8;     // 16-byte pieces per page
-  constexpr int STEP16 = 4 * PAGE16;         // key page 0, key page 1, values of both pages
-  constexpr int NT = 64 * kTileWaves;        // threads
-  constexpr int CPT = STEP16 / NT;           // pieces each thread copies per step
-  static_assert(STEP16 % NT == 0 && PAGE16 % 64 == 0, "a copy round stays inside one page per wavefront");
+  constexpr int KS = D / 32;              // k-steps of the score product
+  constexpr int NJ = D / 16;              // 16-dim column blocks of the output
+  constexpr int NI = 2 * KS + NJ;         // 1 KiB operand blocks per step: keys (2 chains x KS), then values
+  constexpr int IPW = NI / kTileWaves;    // blocks each wavefront loads per step
+  static_assert(NI % kTileWaves == 0, "the blocks of a step split evenly over the wavefronts");
   static_assert(kPartTile % 32 == 0 && kPartTile <= 64 * kBlock, "a partition is whole steps of at most 64 pages");
-  __shared__ u32x4 stage[2][STEP16];
+  __shared__ u32x4 stage[kTileStages][NI * 64];
+  __shared__ int skip[kSkip];
 
   const int lane = threadIdx.x & 63;
   const int wv = wave_uniform((int)(threadIdx.x >> 6));
@@ -737,10 +741,15 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
   const bf16_t* __restrict__ kc = (const bf16_t*)p.k_cache;
   const bf16_t* __restrict__ vc = (const bf16_t*)p.v_cache;
   const int64_t page_elems = (int64_t)kBlock * D;
+  const int64_t blk_elems = (int64_t)p.Hkv * page_elems;
   const float csc = fmaxf(fabsf(p.scale_log2), 1e-30f);  // scale 0 gives equal weights, as it should
   const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
-  __shared__ int skip[kSkip];
+  const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
   const SkipTable tab = stage_skip(skip, p.pre_t, p.num_seqs);
+  // this lane's key operand: page r/8, key 8((r/4)%2) + 4mm + r%4; value piece: page g/2, keys 8(g%2) ..
+  const int krow = 8 * ((r >> 2) & 1) + (r & 3);
+  const int kpage = r >> 3;
+  const int vpage = g4 >> 1, vhalf = g4 & 1;
 
   for (int item = (int)blockIdx.x; item < total; item += (int)gridDim.x) {
     const SeqHit hit = find_seq(skip, tab, p.pre_t, p.num_seqs, item);
@@ -785,164 +794,155 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
     const int bidv = load_block_ids(p, s, kv_lo / kBlock, nblk, lane);
     const int nsteps = (kv_hi - kv_lo + 31) / 32;
 
-    // Piece i of this thread is c = 64 wv + lane + i NT: region c / PAGE16
-    // (wave-uniform: key page 0, key page 1, value page 0, value page 1) at
-    // 16-byte offset c % PAGE16 inside the page.
-    u32x4 nxt[CPT];
-    auto fetch = [&](int st) {
-      const int j0 = 2 * st;
-      const int bid0 = readlane(bidv, j0);
-      const int bid1 = j0 + 1 < nblk ? readlane(bidv, j0 + 1) : bid0;
+    // This lane's pieces of step st (blocks wv, wv + 4, ...): key block
+    // (mm, k) holds key 8((r/4)%2) + 4mm + r%4 of page r/8, dims 32k + 8g ..;
+    // value block j holds column 16j + r, keys 8(g%2) .. of page g/2.  Pages
+    // past the last one (odd counts) read the last page again: their scores
+    // are masked, their values zeroed, and every address stays inside the
+    // pool.  Only the two page offsets change from step to step.
+    const bf16_t* klane = kc + (int64_t)kvh * page_elems + (g4 * kBlock + krow) * 8;
+    const bf16_t* vlane = vc + (int64_t)kvh * page_elems + r * kBlock + 8 * vhalf;
+    auto fetch = [&](int st, u32x4 (&reg)[IPW]) {
+      const int64_t pg0 = (int64_t)readlane(bidv, min(2 * st, nblk - 1)) * blk_elems;
+      const int64_t pg1 = (int64_t)readlane(bidv, min(2 * st + 1, nblk - 1)) * blk_elems;
+      const bf16_t* kb = klane + (kpage ? pg1 : pg0);
+      const bf16_t* vb = vlane + (vpage ? pg1 : pg0);
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int region = (64 * wv + i * NT) / PAGE16;
-        const int q16 = (64 * wv + i * NT) % PAGE16 + lane;
-        const bf16_t* base = region < 2 ? kc : vc;
-        const int bid = (region & 1) ? bid1 : bid0;
-        nxt[i] = ld16(base + ((int64_t)bid * p.Hkv + kvh) * page_elems + (int64_t)q16 * 8);
+      for (int u = 0; u < IPW; ++u) {
+        const int ii = wv + kTileWaves * u;  // wave-uniform
+        if (ii < 2 * KS) reg[u] = ld16(kb + ((ii % KS) * 4 * kBlock + 4 * (ii / KS)) * 8);
+        else reg[u] = ld16(vb + (ii - 2 * KS) * 16 * kBlock);
       }
     };
-    auto put = [&](int buf, int st) {
-      const int kb = kv_lo + 32 * st;
-      const bool vtail = kb + 32 > kv_hi;  // workgroup-uniform
+    // values enter LDS already as half x 2^-8 (each converted once per workgroup)
+    auto put = [&](const u32x4 (&reg)[IPW], int stg) {
 #pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int region = (64 * wv + i * NT) / PAGE16;
-        const int q16 = (64 * wv + i * NT) % PAGE16 + lane;
-        if (region < 2) {
-          stage[buf][region * PAGE16 + q16] = nxt[i];
-        } else {
-          // value page piece: column d = q16 / 2, keys 8h .. 8h + 7 of the page
-          const int pg = region - 2, d = q16 >> 1, h = q16 & 1;
-          u32x4 v = nxt[i];
-          if (vtail) {
-            const int k0 = kb + kBlock * pg + 8 * h;  // key of element 0
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const uint32_t lo = k0 + 2 * e < kv_hi ? 0x0000ffffu : 0u;
-              const uint32_t hi = k0 + 2 * e + 1 < kv_hi ? 0xffff0000u : 0u;
-              v[e] &= lo | hi;
-            }
-          }
-          char* vb = (char*)&stage[buf][2 * PAGE16];
-          const int p0 = ((d >> 4) * 4 + 2 * h) * 16 + (d & 15);
-          *reinterpret_cast<u32x2*>(vb + p0 * 16 + pg * 8) = u32x2{v[0], v[1]};
-          *reinterpret_cast<u32x2*>(vb + (p0 + 16) * 16 + pg * 8) = u32x2{v[2], v[3]};
-        }
+      for (int u = 0; u < IPW; ++u) {
+        const int ii = wv + kTileWaves * u;
+        stage[stg][ii * 64 + lane] = ii < 2 * KS ? reg[u] : bf16x8_to_f16x8_scaled(reg[u]);
       }
     };
 
-    float m_used[2] = {kNegInf, kNegInf}, lsum[2] = {0.f, 0.f};
-    f32x4 oacc[2][NJ];
+    float m_used[2] = {kNegInf, kNegInf};
+    f32x4 oacc[2][NJ], lacc[2];  // lacc: row sums of the weights x 2^8, four equal copies
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t) {
+      lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < NJ; ++j) oacc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
-    fetch(0);
-    put(0, 0);
-    __syncthreads();
-    for (int st = 0; st < nsteps; ++st) {
+    auto compute_step = [&](int st) {
       const int kbase = kv_lo + 32 * st;
-      const bool more = st + 1 < nsteps;
-      if (more) fetch(st + 1);
-      if (active && kbase < w_kv_hi) {
-        const u32x4* ks = stage[st & 1];
-        const u32x4* vs = stage[st & 1] + 2 * PAGE16;
-        f32x4 c[2][2];
+      if (!active || kbase >= w_kv_hi) return;  // wave-uniform: this wavefront's rows see no key of the step
+      const u32x4* img = stage[st % kTileStages];
+      f32x4 c[2][2];  // [tile][chain]
 #pragma unroll
-        for (int pg = 0; pg < 2; ++pg) {
-          bf16x8 kop[KS];
+      for (int mm = 0; mm < 2; ++mm) {
+        bf16x8 kop[KS];
 #pragma unroll
-          for (int k = 0; k < KS; ++k) kop[k] = __builtin_bit_cast(bf16x8, ks[pg * PAGE16 + (4 * k + g4) * kBlock + r]);
+        for (int k = 0; k < KS; ++k) kop[k] = __builtin_bit_cast(bf16x8, img[(mm * KS + k) * 64 + lane]);
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            c[t][pg] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 2; ++t) {
+          c[t][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int k = 0; k < KS; ++k)
-              c[t][pg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[k], qop[t][k], c[t][pg], 0, 0, 0);
-          }
+          for (int k = 0; k < KS; ++k)
+            c[t][mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[k], qop[t][k], c[t][mm], 0, 0, 0);
         }
-        // unscaled scores of row r of tile t for keys kbase + 16 * (e >> 2) + 4 * g4 + (e & 3)
-        float sc[2][8];
+      }
+      // unscaled scores of row r of tile t for keys kbase + 8 g4 + e
+      float sc[2][8];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sc[t][e] = c[t][e >> 2][e & 3];
+      if (kbase + 31 > w_pos_lo) {  // some key of the step lies past some row's position
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) sc[t][e] = c[t][e >> 2][e & 3];
-        if (kbase + 31 > w_pos_lo) {  // some key of the step lies past some row's position
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int key = kbase + (e >> 2) * kBlock + 4 * g4 + (e & 3);
-              sc[t][e] = key <= pos_r[t] ? sc[t][e] : kNegInf;
-            }
-        }
-        float mloc[2];
-        bool grow = false;
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float mx = fmaxf(fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])),
-                           fmaxf(fmaxf(sc[t][4], sc[t][5]), fmaxf(sc[t][6], sc[t][7])));
-          mx = fmaxf(mx, shfl_xor_f(mx, 16));
-          mx = fmaxf(mx, shfl_xor_f(mx, 32));
-          mloc[t] = mx * csc;  // -inf stays -inf (csc > 0)
-          grow = grow || mloc[t] > m_used[t] + kLazyRescale;
-        }
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const float m_new = fmaxf(m_used[t], mloc[t]);
-            const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_used[t] - m_new);
-            lsum[t] *= alpha;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) oacc[t][j] *= alpha;
-            m_used[t] = m_new;
-          }
-        }
-        bf16x8 phi[2], plo[2];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const float nmu = m_used[t] == kNegInf ? 0.f : -m_used[t];  // a row that sees no key yet has weights 0
-          uint32_t hw4[4], lw4[4];
-          float ps = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float p0 = fast_exp2(fmaf(sc[t][e], csc, nmu));
-            const float p1 = fast_exp2(fmaf(sc[t][e + 1], csc, nmu));
-            const uint32_t hw = pack_bf16x2(p0, p1);
-            hw4[e >> 1] = hw;
-            lw4[e >> 1] = pack_bf16x2(p0 - bf16_lo(hw), p1 - bf16_hi(hw));
-            ps += p0 + p1;
-          }
-          lsum[t] += ps;
-          phi[t] = __builtin_bit_cast(bf16x8, u32x4{hw4[0], hw4[1], hw4[2], hw4[3]});
-          plo[t] = __builtin_bit_cast(bf16x8, u32x4{lw4[0], lw4[1], lw4[2], lw4[3]});
-        }
-        bf16x8 va[NJ];
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) va[j] = __builtin_bit_cast(bf16x8, vs[(4 * j + g4) * 16 + r]);
-        // the high parts first, then the low parts: no MFMA waits on the one before it
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            oacc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], phi[t], oacc[t][j], 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            oacc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[j], plo[t], oacc[t][j], 0, 0, 0);
+          for (int e = 0; e < 8; ++e) sc[t][e] = kbase + 8 * g4 + e <= pos_r[t] ? sc[t][e] : kNegInf;
       }
-      if (more) put((st + 1) & 1, st + 1);
+      float mloc[2];
+      bool grow = false;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        float mx = fmaxf(fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])),
+                         fmaxf(fmaxf(sc[t][4], sc[t][5]), fmaxf(sc[t][6], sc[t][7])));
+        mx = max_over_rows(mx);
+        mloc[t] = mx * csc;  // -inf stays -inf (csc > 0)
+        grow = grow || mloc[t] > m_used[t] + kTileLazyRescale;
+      }
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const float m_new = fmaxf(m_used[t], mloc[t]);
+          const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_used[t] - m_new);
+          lacc[t] *= alpha;
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) oacc[t][j] *= alpha;
+          m_used[t] = m_new;
+        }
+      }
+      f16x8 pw[2];  // weights x 2^8 in half, keys 8 g4 + e of the lane's row
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float nmu = (m_used[t] == kNegInf ? 0.f : -m_used[t]) + 8.f;  // a row that sees no key yet has weights 0
+        uint32_t w4[4];
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+          w4[e >> 1] = pack_f16x2(fast_exp2(fmaf(sc[t][e], csc, nmu)), fast_exp2(fmaf(sc[t][e + 1], csc, nmu)));
+        pw[t] = __builtin_bit_cast(f16x8, u32x4{w4[0], w4[1], w4[2], w4[3]});
+      }
+      u32x4 vraw[NJ];
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) vraw[j] = img[(2 * KS + j) * 64 + lane];
+      if (kbase + 32 > kv_hi) {
+        // keys at or past kv_hi may hold anything (even NaN): zero them in the value operand
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const int key = kbase + 8 * g4 + e;
+          const uint32_t keep = (key < kv_hi ? 0x0000ffffu : 0u) | (key + 1 < kv_hi ? 0xffff0000u : 0u);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) vraw[j][e >> 1] &= keep;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+          oacc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vraw[j]), pw[t], oacc[t][j], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pw[t], lacc[t], 0, 0, 0);
+    };
+
+    // The loop is unrolled by two so that each register set stays in fixed
+    // registers, and every half requests one step (past the last step it
+    // requests the last one again): the number of loads in flight is then
+    // the same on every path, and the compiler waits for exactly the set
+    // being stored.
+    u32x4 rset0[IPW], rset1[IPW];
+    __syncthreads();  // every wavefront is done with the stages of the previous item
+    fetch(0, rset0);
+    fetch(min(1, nsteps - 1), rset1);
+    put(rset0, 0);
+    __syncthreads();
+    for (int st = 0;; st += 2) {
+      fetch(min(st + 2, nsteps - 1), rset0);
+      compute_step(st);
+      if (st + 1 >= nsteps) break;
+      put(rset1, (st + 1) % kTileStages);
+      __syncthreads();
+      fetch(min(st + 3, nsteps - 1), rset1);
+      compute_step(st + 1);
+      if (st + 2 >= nsteps) break;
+      put(rset0, (st + 2) % kTileStages);
       __syncthreads();
     }
 
     if (active) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        float l = lsum[t] + shfl_xor_f(lsum[t], 16);
-        l += shfl_xor_f(l, 32);
+        const float l = lacc[t][0] * 0.00390625f;  // undo the 2^8 of the weights
         if (w.nparts == 1) {
           bf16_t* orow = (bf16_t*)p.out + ((int64_t)tok[t] * p.Hq + hh[t]) * D;
 #pragma unroll

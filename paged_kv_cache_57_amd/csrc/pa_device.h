@@ -18,6 +18,9 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
 typedef uint16_t bf16_t;  // storage type of one bfloat16
 
 // Element traits: storage type, 16-byte group width X, load/convert helpers.
@@ -50,9 +53,29 @@ __device__ inline uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Two floats rounded to IEEE half (to nearest even) and packed (low half = a).
+__device__ inline uint32_t pack_f16x2(float a, float b) {
+  const f16x2 v = __builtin_convertvector(f32x2{a, b}, f16x2);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Low / high bfloat16 of a packed pair, widened to float32 (exact).
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Eight bfloat16 values (one 16-byte piece) as IEEE half, each multiplied by
+// 2^-8 first: the power-of-two factor is exact, so every |v| below 2^24 keeps
+// its bfloat16 value up to the half rounding of tiny magnitudes (absolute
+// error below 2^-16); larger magnitudes overflow to infinity.
+__device__ inline u32x4 bf16x8_to_f16x8_scaled(u32x4 w) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t wi = w[i];
+    r[i] = pack_f16x2(bf16_lo(wi) * 0.00390625f, bf16_hi(wi) * 0.00390625f);
+  }
+  return r;
+}
 
 // a.lo*b.lo + a.hi*b.hi + c on two packed bfloat16 pairs (v_dot2_f32_bf16).
 // The pairs arrive as 32-bit words copied into locals: a bit cast applied
@@ -88,6 +111,27 @@ __device__ inline float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mas
 // small relative to the running maximum contribute nothing measurable.
 // 2^-inf = 0, 2^NaN = NaN.
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Max / sum over the four 16-lane rows of a wavefront: every lane gets the
+// result for lanes l%16, l%16 + 16, l%16 + 32, l%16 + 48.  Two VALU lane
+// swaps (v_permlane16_swap: rows 0,1 and 2,3; v_permlane32_swap: halves)
+// instead of two exchanges through LDS.  Called with the same value in both
+// operands, a swap returns the two partners' values in its two results, so
+// every lane combines the same two values in the same order.
+__device__ inline float max_over_rows(float v) {
+  typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+  u32x2v s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+  s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ inline float sum_over_rows(float v) {
+  typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+  u32x2v s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(s[0]) + __uint_as_float(s[1]);
+  s = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
 
 __device__ inline float wave_max(float v) {
 #pragma unroll

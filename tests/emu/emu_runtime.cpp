@@ -181,6 +181,30 @@ void mfma_16x16x32_bf16(const uint16_t a[8], const uint16_t b[8], const float c[
   arrive(w.bar);
 }
 
+static float hf(uint16_t u) {
+  _Float16 h;
+  std::memcpy(&h, &u, 2);
+  return (float)h;
+}
+
+// The same product for IEEE half operands (v_mfma_f32_16x16x32_f16).
+void mfma_16x16x32_f16(const uint16_t a[8], const uint16_t b[8], const float c[4], float d[4]) {
+  Wave& w = my_wave();
+  const int l = tl_lane;
+  std::memcpy(w.a[l], a, 16);
+  std::memcpy(w.b[l], b, 16);
+  std::memcpy(w.c[l], c, 16);
+  arrive(w.bar);
+  const int n = l % 16;
+  for (int i = 0; i < 4; ++i) {
+    const int m = 4 * (l / 16) + i;
+    double acc = 0;
+    for (int k = 0; k < 32; ++k) acc += (double)hf(w.a[m + 16 * (k / 8)][k % 8]) * hf(w.b[n + 16 * (k / 8)][k % 8]);
+    d[i] = (float)(acc + w.c[l][i]);
+  }
+  arrive(w.bar);
+}
+
 void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* ctx) {
   const int n = (int)(block.x * block.y * block.z);
   for (unsigned bz = 0; bz < grid.z; ++bz)

@@ -42,6 +42,7 @@ void block_sync();
 uint64_t exchange(uint64_t mine, int src_lane);          // value of src_lane
 uint64_t ballot(bool pred);
 void mfma_16x16x32_bf16(const uint16_t a[8], const uint16_t b[8], const float c[4], float d[4]);
+void mfma_16x16x32_f16(const uint16_t a[8], const uint16_t b[8], const float c[4], float d[4]);
 void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* ctx);
 
 template <typename T>
@@ -119,6 +120,23 @@ inline T emu_readfirstlane(T v) {
 }
 inline uint64_t emu_ballot(bool p) { return emu::ballot(p); }
 
+// v_permlane16_swap / v_permlane32_swap with old = a, src = b: returns
+// {first, second} = ([a.R0, b.R0, a.R2, b.R2], [a.R1, b.R1, a.R3, b.R3]) for
+// 16-lane rows R, and ([a.lo, b.lo], [a.hi, b.hi]) for 32-lane halves.
+typedef uint32_t emu_u32x2 __attribute__((ext_vector_type(2)));
+inline emu_u32x2 emu_permlane_swap(uint32_t a, uint32_t b, int width) {
+  const int l = emu::tl_lane;
+  const bool upper = (l / width) & 1;
+  const uint64_t a_src = emu::exchange(a, upper ? l : l + width);   // partner for the second result
+  const uint64_t b_src = emu::exchange(b, upper ? l - width : l);   // partner for the first result
+  emu_u32x2 r;
+  r[0] = upper ? (uint32_t)b_src : a;
+  r[1] = upper ? b : (uint32_t)a_src;
+  return r;
+}
+#define __builtin_amdgcn_permlane16_swap(a, b, fi, bc) emu_permlane_swap((a), (b), 16)
+#define __builtin_amdgcn_permlane32_swap(a, b, fi, bc) emu_permlane_swap((a), (b), 32)
+
 template <typename V2>
 inline float emu_fdot2(V2 a, V2 b, float c, bool) {
   return (float)a[0] * (float)b[0] + (float)a[1] * (float)b[1] + c;
@@ -137,6 +155,20 @@ inline F4 emu_mfma(V8 a, V8 b, F4 c, int, int, int) {
   return d;
 }
 
+template <typename V8, typename F4>
+inline F4 emu_mfma_f16(V8 a, V8 b, F4 c, int, int, int) {
+  uint16_t ua[8], ub[8];
+  float fc[4], fd[4];
+  std::memcpy(ua, &a, 16);
+  std::memcpy(ub, &b, 16);
+  for (int i = 0; i < 4; ++i) fc[i] = c[i];
+  emu::mfma_16x16x32_f16(ua, ub, fc, fd);
+  F4 d;
+  for (int i = 0; i < 4; ++i) d[i] = fd[i];
+  return d;
+}
+
+#define __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, x, y, z) emu_mfma_f16((a), (b), (c), (x), (y), (z))
 #define __builtin_amdgcn_readlane(v, l) emu_readlane((v), (l))
 #define __builtin_amdgcn_readfirstlane(v) emu_readfirstlane((v))
 #define __builtin_amdgcn_ballot_w64(p) emu_ballot((p))
