@@ -12,6 +12,9 @@ inputs resident in device memory before timing starts:
 * llama7b / gqa70b / gqa70b_long: decode-only passes (batch 64 MHA 32x128;
   batch 32 GQA 64/8 at 2048 keys; one GQA sequence of 32768 keys).  value =
   KV bytes read per second.
+* copy / read: calibration lines, not the path — a 4 GiB device copy, and
+  every 4 KiB page of a 4 GiB pool read once in random order (pa_read_pages),
+  the attainable HBM rates the kernels' fractions are set against.
 
 The roofline object describes the dominant kernel, timed with HIP events
 recorded on the stream it runs on (pa_set_stage_events), against MI355X's
@@ -216,13 +219,44 @@ def copy_calibration(torch, dev, args, nbytes=4 << 30):
                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}), flush=True)
 
 
+def read_calibration(torch, pa, dev, args, nbytes=4 << 30, grid=2048):
+    """Every 4 KiB page of a 4 GiB pool read once per step in a seeded random order,
+    16-byte loads, two pages per wavefront in flight: the rate the decode workers'
+    page reads could reach if they did no arithmetic."""
+    pool = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(7)
+    npages = nbytes // 4096
+    order = torch.from_numpy(np.random.default_rng(5).permutation(npages).astype(np.int32)).to(dev)
+    sink = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    for _ in range(args.warmup):
+        pa.pa_read_pages(pool, order, sink, grid, status)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(args.steps):
+        pa.pa_read_pages(pool, order, sink, grid, status)
+    t1.record()
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"pa_read_pages flagged status {int(status.item())}")
+    ms = t0.elapsed_time(t1) / args.steps
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": "random 4 KiB page reads GB/s", "value": round(gbps, 1), "unit": "GB/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
+                      "data": "synthetic", "config": {"workload": "read_pages_4GiB", "pages": npages,
+                                                      "grid": grid},
+                      "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="splitfuse",
-                    choices=["splitfuse", "llama7b", "gqa70b", "gqa70b_long", "tiny", "copy"])
+                    choices=["splitfuse", "llama7b", "gqa70b", "gqa70b_long", "tiny", "copy", "read"])
     ap.add_argument("--rotate", type=int, default=0, help="pool copies cycled per step (0: enough to exceed the 256 MB MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -240,6 +274,8 @@ def main():
     dev = torch.device("cuda:0")
     if args.workload == "copy":
         return copy_calibration(torch, dev, args)
+    if args.workload == "read":
+        return read_calibration(torch, pa, dev, args)
     w = build_workload(args.workload)
     code = pa.PA_BF16 if w.dtype == "bf16" else pa.PA_F32
     q, kc, vc, nk, nv = W.make_values(w, dev)

@@ -106,7 +106,7 @@ struct AttnParams {
   int32_t Hq, Hkv, G, num_blocks;
   float scale_log2;
   int32_t is_f32;
-  int32_t* ctrl;  // [2] VALU items, [3] MFMA items, [4] TILE items, [5] rows to merge
+  int32_t* ctrl;  // [2] VALU items, [3] MFMA items, [4] TILE items, [5] rows to merge, [6] TILE tickets
   int32_t* pre_v;  // exclusive prefix over sequences of VALU items, [S + 1]
   int32_t* pre_m;  // ... of MFMA items
   int32_t* pre_t;  // ... of TILE items
@@ -273,6 +273,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
     p.ctrl[3] = carry[1];
     p.ctrl[4] = carry[2];
     p.ctrl[5] = carry[3];
+    p.ctrl[6] = 0;  // TILE work tickets handed out so far
   }
 }
 
@@ -720,9 +721,12 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
 // |v| < 2^24 up to an absolute 2^-16 on tiny magnitudes), so the products are
 // p·v.  The row sum l comes from the same MFMA with an all-ones value
 // operand: it adds exactly the rounded weights that P·V used.
-// Workgroup g takes items g, g + grid, g + 2 grid, ...  (A shared counter
-// bumped once per item was tried: at one atomic per lane, 64 per item, the
-// same-address atomics serialised and made the kernel six times slower.)
+// Workgroup g starts with item g and then takes tickets from a counter the
+// planner zeroes: one atomic per item, by one lane, with barriers on both
+// sides of the shared ticket (items differ in length near the diagonal, and
+// a fixed stride left the slowest workgroup with a whole item more than the
+// mean).  The lane-0 region is the only per-lane branch of the worker; the
+// barriers keep the compiler from moving anything of the work across it.
 template <int D>
 __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParams p) {
   constexpr int KS = D / 32;              // k-steps of the score product
@@ -751,7 +755,14 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
   const int kpage = r >> 3;
   const int vpage = g4 >> 1, vhalf = g4 & 1;
 
-  for (int item = (int)blockIdx.x; item < total; item += (int)gridDim.x) {
+  __shared__ int ticket;
+  auto next_item = [&]() {
+    __syncthreads();  // every thread has read the previous ticket
+    if (threadIdx.x == 0) ticket = atomicAdd(p.ctrl + 6, 1);
+    __syncthreads();
+    return wave_uniform(ticket) + (int)gridDim.x;
+  };
+  for (int item = (int)blockIdx.x; item < total; item = next_item()) {
     const SeqHit hit = find_seq(skip, tab, p.pre_t, p.num_seqs, item);
     const int s = hit.s;
     const int local = item - hit.first;

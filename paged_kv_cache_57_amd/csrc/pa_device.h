@@ -89,14 +89,6 @@ __device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// Asynchronous copy of 16 bytes per lane from global memory into LDS
-// (global_load_lds_dwordx4): lane l's bytes land at lds_base + 16 l, where
-// lds_base is the same for the whole wavefront.  No register holds the data
-// while it is in flight; the compiler makes later LDS reads of that area wait
-// for it (vmcnt).
-__device__ inline void lds_dma16(const void* src, void* lds_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
-}
 __device__ inline void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 template <typename T>

@@ -93,6 +93,15 @@ def copy_blocks(dtype, kp, vp, pairs):
             np.frombuffer(raw[kp.nbytes:], vp.dtype).reshape(vp.shape), st)
 
 
+def read_pages(words, ids, grid):
+    """Emulated pa_read_pages over int32 `words` (a whole number of 4 KiB pages)."""
+    words = np.ascontiguousarray(words, np.int32)
+    ids = np.ascontiguousarray(ids, np.int32)
+    hdr = np.array([words.size // 1024, ids.size, grid], np.int32)
+    raw, st = _run("read", [hdr, words, ids], grid * 256 * 4)
+    return np.frombuffer(raw, np.uint32).copy(), st
+
+
 def forward_sparse(w, q, pages_k, pages_v, used):
     """Emulated pa_forward on a full-size zeroed pool holding only the ``used`` blocks' pages."""
     es = 4 if w.dtype == "f32" else 2

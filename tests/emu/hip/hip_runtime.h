@@ -180,13 +180,5 @@ inline float emu_exp2(float x) {
   return std::fabs(r) < 1.17549435e-38f ? 0.f : r;
 }
 #define __builtin_amdgcn_exp2f(x) emu_exp2((x))
-// global_load_lds: lane l copies `size` bytes from its source to lds_base + offset + size * l
-inline void emu_lds_dma(const void* src, void* lds_base, int size, int offset) {
-  std::memcpy(static_cast<char*>(lds_base) + offset + size * emu::tl_lane, src, (size_t)size);
-}
-#define __builtin_amdgcn_global_load_lds(src, dst, size, off, aux) \
-  emu_lds_dma((const void*)(src), (void*)(dst), (size), (off))
 #define __builtin_amdgcn_fence(...) ((void)0)
-#define __builtin_amdgcn_sched_barrier(m) ((void)0)
-#define __builtin_amdgcn_s_waitcnt(m) ((void)0)
 #define __builtin_amdgcn_wave_barrier() emu::wave_sync()

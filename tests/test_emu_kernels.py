@@ -14,7 +14,7 @@ from oracle import attention as oattn
 from oracle import cache_ops, layout
 from tests import _emu
 from tests._pools import empty_pools, raw
-from tests.test_gpu_parity import RAGGED, REJECTED, many_sequences_batch
+from tests.test_gpu_parity import RAGGED, REJECTED, many_sequences_batch, read_probe_case
 
 pytestmark = pytest.mark.skipif(not _emu.available(), reason="needs the ROCm clang++ for the host build")
 TOL = {"bf16": (2e-3, 1e-2), "f32": (1e-5, 1e-5)}
@@ -68,6 +68,23 @@ def test_many_sequences(emu):
     out, st = emu.forward(w, q, kp, vp)
     assert st == 0
     check(w, q, kp, vp, out, "5000 sequences")
+
+
+def test_large_value_magnitudes(emu):
+    # values near 2^20: the prefill tile stages them as half x 2^-8, exact below 2^24
+    w = W.random_ragged(21, "bf16", 8, 2, 64, [1, 40, 1], [300, 170, 45])
+    rng = np.random.default_rng(6)
+    kp, vp = empty_pools(rng, "bf16", w.num_blocks, 2, 64)
+    big = raw(layout.to_f64(vp, "bf16").astype(np.float32) * np.float32(2.0 ** 20), "bf16")
+    q = raw(rng.standard_normal((w.num_tokens, 8, 64)).astype(np.float32), "bf16")
+    out, st = emu.forward(w, q, kp, big)
+    assert st == 0
+    # the output scales with the values (an exact power of two): compare at the scale of N(0, 1) values
+    ref = oattn.paged_attention(q, kp, big, w.block_tables, w.context_lens, w.query_start_loc, w.scale, "bf16")
+    got = layout.to_f64(out, "bf16")
+    a, r = TOL["bf16"]
+    ratio = (np.abs(got - ref) / 2.0 ** 20 / (a + r * np.abs(ref) / 2.0 ** 20)).max()
+    assert np.isfinite(got).all() and ratio <= 1.0, f"large values: worst err/bound {ratio:.3f}"
 
 
 def test_float32_head_dim_128_is_rejected(emu):
@@ -150,3 +167,10 @@ def test_parallel_sampling_workflow_emulated(emu):
                                     heads=2, head_dim=64)
     worst, copies = run_workflow(EmuBackend(pa, spec), spec, checkpoints={0, 1, 7, 19}, say=lambda *_: None)
     assert worst <= 1.0 and copies > 0
+
+
+def test_read_pages_probe_emulated(emu):
+    words, ids, grid, want = read_probe_case()
+    got, st = emu.read_pages(words, ids, grid)
+    assert st == 1  # PA_DEV_BAD_BLOCK for the id outside the pool
+    assert np.array_equal(got, want)

@@ -213,6 +213,23 @@ def test_scale_sign_and_size(pa, scale):
         run_and_check(pa, w, label=f"scale {scale} Hq={hq} Hkv={hkv} q={ql} L={cl}")
 
 
+def test_large_value_magnitudes(pa):
+    # values near 2^20 in magnitude: the prefill tile stages them as half x 2^-8 (exact below 2^24)
+    w = W.random_ragged(21, "bf16", 8, 8, 128, [1, 150, 1], [700, 1200, 40])
+    say("[case] large value magnitudes (V x 2^20, K x 4)")
+    r = Run(w)
+    q, kc, vc, _, _ = W.make_values(w, DEV)
+    vc.mul_(2.0 ** 20)
+    kc.mul_(4.0)
+    out = r.forward(q, kc, vc)
+    r.check_status()
+    rows, ref = oracle_rows(w, q, kc, vc, range(w.num_seqs))
+    got = to_f64(out.index_select(0, torch.from_numpy(rows).to(DEV)))
+    assert np.isfinite(got).all()
+    # the output scales with the values (an exact power of two): compare at the scale of N(0, 1) values
+    assert_close(got / 2.0 ** 20, ref / 2.0 ** 20, "bf16", "large value magnitudes (/2^20)")
+
+
 def test_single_key_and_equal_scores(pa):
     # one key: output is that value row exactly; q = 0: output is the mean of the values
     for dt, hq, hkv, d in [("f32", 4, 4, 64), ("bf16", 32, 32, 128), ("bf16", 64, 8, 128)]:
@@ -304,3 +321,35 @@ def test_parallel_sampling_workflow(pa):
     worst, copies = run_workflow(GpuBackend(pa, spec), spec, checkpoints={0, 1, 15, 16, 17, 255}, say=say)
     say(f"  copy-on-write pairs: {copies}; worst err/bound {worst:.3f}")
     assert copies > 0
+
+
+def read_probe_case():
+    """Pages, a page list with one id outside the pool, and the sink the documented
+    thread assignment gives: wavefront w XORs piece l, l+64, l+128, l+192 of its
+    pages 2w, 2w+1, 2w+2W, ... into lane l."""
+    rng = np.random.default_rng(11)
+    npool, n, grid = 300, 257, 3
+    words = rng.integers(0, 2**31 - 1, size=npool * 1024, dtype=np.int64).astype(np.int32)
+    ids = rng.integers(0, npool, size=n).astype(np.int32)
+    ids[5] = npool + 4
+    pages = words.view(np.uint32).reshape(npool, 4, 64, 4)  # [page][k][lane][component]
+    want = np.zeros(grid * 256, dtype=np.uint32)
+    nwaves = grid * 4
+    for i, pid in enumerate(ids):
+        wave = (i // 2) % nwaves
+        page = pid if pid < npool else 0
+        want[wave * 64:(wave + 1) * 64] ^= np.bitwise_xor.reduce(
+            pages[page].transpose(1, 0, 2).reshape(64, 16), axis=1)
+    return words, ids, grid, want
+
+
+def test_read_pages_probe(pa):
+    """The measurement-only page reader visits each listed page once, in the documented assignment."""
+    words, ids, grid, want = read_probe_case()
+    pool = torch.from_numpy(words).to(DEV)
+    sink = torch.full((grid * 256,), -1, dtype=torch.int32, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    pa.pa_read_pages(pool, torch.from_numpy(ids).to(DEV), sink, grid, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == pa.PA_DEV_BAD_BLOCK
+    assert np.array_equal(sink.cpu().numpy().view(np.uint32), want)

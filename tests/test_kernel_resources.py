@@ -2,7 +2,8 @@
 
 * No kernel spills registers or uses scratch memory.
 * The attention workers and the merge contain no exec-mask regions: nothing
-  inside them branches per lane.  Their work loops call cross-lane operations
+  inside them branches per lane (the one exception is the TILE worker's work
+  ticket, taken by lane 0 between two barriers).  Their work loops call cross-lane operations
   (readfirstlane, readlane, shuffles, MFMA); a lane-dependent branch near such
   a loop let the compiler split the wavefront across loop iterations, which
   left lanes running with a stale work item.
@@ -60,6 +61,11 @@ def test_workers_have_no_per_lane_branches(tmp_path):
             continue
         body = f.split(".Lfunc_end")[0]
         n = len(re.findall(r"\bs_and_saveexec_b64|\bs_andn2_saveexec_b64|\bs_or_saveexec_b64", body))
-        assert n == 0, f"{m.group(1)} has {n} exec-mask regions"
+        if "tile_attn" in m.group(1):
+            # the single exception: lane 0 takes the workgroup's next work ticket, between two barriers
+            assert n <= 1, f"{m.group(1)} has {n} exec-mask regions"
+            assert n == 0 or re.search(r"global_atomic_add", body), "the one region must be the ticket atomic"
+        else:
+            assert n == 0, f"{m.group(1)} has {n} exec-mask regions"
         checked += 1
     assert checked >= 8 and bodies is not None
