@@ -39,7 +39,8 @@ METRIC = "paged decode attn KV-read GB/s (% HBM peak); SplitFuse mixed-batch tok
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2516.6
 MALL_BYTES = 256 << 20
-STAGES = ("plan", "valu_worker", "mfma_worker", "merge")
+STAGES = ("plan", "valu_worker", "mfma_worker", "tile_worker", "merge")
+WORKERS = ("valu_worker", "mfma_worker", "tile_worker")
 
 
 class HipEvents:
@@ -85,7 +86,10 @@ DOMINANT_KERNEL = {("valu_worker", "bf16", 128): "valu_attn_kernel<unsigned shor
                    ("valu_worker", "f32", 64): "valu_attn_kernel<float, 64>",
                    ("mfma_worker", "bf16", 128): "mfma_attn_kernel<128>",
                    ("mfma_worker", "bf16", 64): "mfma_attn_kernel<64>",
-                   ("mfma_worker", "f32", 64): "mfma_attn_kernel<64>"}
+                   ("mfma_worker", "f32", 64): "mfma_attn_kernel<64>",
+                   ("tile_worker", "bf16", 128): "tile_attn_kernel<128>",
+                   ("tile_worker", "bf16", 64): "tile_attn_kernel<64>",
+                   ("tile_worker", "f32", 64): "tile_attn_kernel<64>"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCE = os.path.join(ROOT, "paged_kv_cache_57_amd", "csrc", "pa_attention.hip")
 
@@ -126,24 +130,29 @@ def kv_token_bytes(w):
 def work_split(w):
     """Algorithmic work of one pass, split by the worker that does it.
 
-    Decode rows of sequences with one query head per KV head run on the VALU
-    worker (as does everything in float32); GQA decode rows and prefill chunks
-    run on the MFMA worker.  Bytes are the KV pages the rows must read (each
-    context key once per KV head: 2 * Hkv * d * elem bytes per key); FLOPs
-    count QK^T and PV over the keys each prefill row may see.
+    A sequence goes where the library's planner sends it: decode rows with one
+    query head per KV head (and everything in float32) to the VALU worker;
+    sequences with at most 16 rows per KV head (q_len x group size: GQA decode,
+    short chunks) to the MFMA worker; longer prefill chunks to the tile worker.
+    Bytes are the KV pages a worker's rows must read (each context key once
+    per KV head: 2 * Hkv * d * elem bytes per key); FLOPs count QK^T and PV
+    over the keys each row of a multi-row chunk may see (4 d Hq (pos + 1)).
     """
     ql = np.diff(w.query_start_loc).astype(np.int64)
     L = w.context_lens.astype(np.int64)
     G = w.num_q_heads // w.num_kv_heads
-    valu = (ql == 1) & (G == 1) if w.dtype == "bf16" else (ql >= 1)
-    mfma = (ql >= 1) & ~valu
-    valu_bytes = int(L[valu].sum()) * kv_token_bytes(w)
-    mfma_bytes = int(L[mfma].sum()) * kv_token_bytes(w)
-    flops = 0
-    for q, Ls in zip(ql[ql > 1], L[ql > 1]):
-        pos = Ls - q + np.arange(q)
-        flops += 4 * w.head_dim * w.num_q_heads * int((pos + 1).sum())
-    return valu_bytes, mfma_bytes, flops
+    live = (ql >= 1) & (L >= 1)
+    valu = live & (((ql == 1) & (G == 1)) if w.dtype == "bf16" else True)
+    mfma = live & ~valu & (ql * G <= 16)
+    tile = live & ~valu & ~mfma
+    work = {}
+    for name, sel in (("valu_worker", valu), ("mfma_worker", mfma), ("tile_worker", tile)):
+        flops = 0
+        for q, Ls in zip(ql[sel & (ql > 1)], L[sel & (ql > 1)]):
+            pos = Ls - q + np.arange(q)
+            flops += 4 * w.head_dim * w.num_q_heads * int((pos + 1).sum())
+        work[name] = {"bytes": int(L[sel].sum()) * kv_token_bytes(w), "flops": flops}
+    return work
 
 
 def cpu_baseline(w, q, kc, vc, budget_s):
@@ -279,8 +288,8 @@ def main():
     w = build_workload(args.workload)
     code = pa.PA_BF16 if w.dtype == "bf16" else pa.PA_F32
     q, kc, vc, nk, nv = W.make_values(w, dev)
-    valu_bytes, mfma_bytes, pre_flops = work_split(w)
-    pass_bytes = valu_bytes + mfma_bytes
+    work = work_split(w)
+    pass_bytes = sum(v["bytes"] for v in work.values())
     # cycle enough pool copies that one pass's pages cannot stay in the 256 MB Infinity Cache
     rotate = args.rotate or (1 if pass_bytes >= 8 * MALL_BYTES else int(np.ceil(8 * MALL_BYTES / max(pass_bytes, 1))))
     pools = [(kc, vc)] + [(kc.clone(), vc.clone()) for _ in range(max(1, rotate) - 1)]
@@ -339,10 +348,9 @@ def main():
         raise RuntimeError(f"device status {int(status.item()):#x}")
 
     ms_per_step = 1e3 * elapsed / K
-    # the dominant kernel is the worker with the larger share of the pass
-    dom = "valu_worker" if stage_ms["valu_worker"] >= stage_ms["mfma_worker"] else "mfma_worker"
-    dom_bytes = valu_bytes if dom == "valu_worker" else mfma_bytes
-    achieved = dom_bytes / (stage_ms[dom] * 1e-3) / 1e9
+    # the dominant kernel is the worker with the largest share of the pass: a
+    # prefill tile worker is priced against bf16 MFMA, the decode workers against HBM
+    dom = max(WORKERS, key=lambda k: stage_ms[k])
     result = {
         "metric": METRIC,
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
@@ -356,23 +364,34 @@ def main():
                         "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                         "block_size": 16, "max_context_len": w.max_context_len, "pool_blocks": w.num_blocks,
                         "pool_copies_rotated": rotate}
-    result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                          "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                          "traffic": measured_traffic(w.name, DOMINANT_KERNEL[(dom, w.dtype, w.head_dim)]),
-                          "kernel": dom, "kernel_ms": round(stage_ms[dom], 4), "algorithmic_bytes": dom_bytes}
+    traffic = measured_traffic(w.name, DOMINANT_KERNEL[(dom, w.dtype, w.head_dim)])
+    if dom == "tile_worker":
+        achieved = work[dom]["flops"] / (stage_ms[dom] * 1e-3) / 1e12
+        result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "traffic": traffic, "kernel": dom, "kernel_ms": round(stage_ms[dom], 4),
+                              "algorithmic_flops": work[dom]["flops"]}
+    else:
+        achieved = work[dom]["bytes"] / (stage_ms[dom] * 1e-3) / 1e9
+        result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                              "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom,
+                              "kernel_ms": round(stage_ms[dom], 4), "algorithmic_bytes": work[dom]["bytes"]}
     result["stages_ms"] = {k: round(v, 4) for k, v in stage_ms.items()}
     if slots is not None:
         result["stages_ms"]["cache_write"] = round(write_ms, 4)
-    result["kv_read_GBps"] = round(pass_bytes / ((stage_ms["valu_worker"] + stage_ms["mfma_worker"]) * 1e-3) / 1e9, 1)
-    if valu_bytes:
-        result["valu_worker_kv_GBps"] = round(valu_bytes / (stage_ms["valu_worker"] * 1e-3) / 1e9, 1)
-    if mfma_bytes and not pre_flops:
-        result["mfma_worker_kv_GBps"] = round(mfma_bytes / (stage_ms["mfma_worker"] * 1e-3) / 1e9, 1)
-    if pre_flops:
-        mfma_ms = stage_ms["mfma_worker"]
-        result["prefill"] = {"algorithmic_tflops": round(pre_flops / 1e12, 3),
-                             "achieved_tflops": round(pre_flops / (mfma_ms * 1e-3) / 1e12, 1),
-                             "frac_of_bf16_mfma_peak": round(pre_flops / (mfma_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    result["kv_read_GBps"] = round(pass_bytes / (sum(stage_ms[k] for k in WORKERS) * 1e-3) / 1e9, 1)
+    for k in ("valu_worker", "mfma_worker"):
+        if work[k]["bytes"] and not work[k]["flops"]:
+            result[f"{k}_kv_GBps"] = round(work[k]["bytes"] / (stage_ms[k] * 1e-3) / 1e9, 1)
+    if work["tile_worker"]["flops"]:
+        t_ms = stage_ms["tile_worker"]
+        f = work["tile_worker"]["flops"]
+        result["prefill"] = {"kernel": "tile_worker", "kernel_ms": round(t_ms, 4),
+                             "algorithmic_tflops": round(f / 1e12, 3),
+                             "achieved_tflops": round(f / (t_ms * 1e-3) / 1e12, 1),
+                             "frac_of_bf16_mfma_peak": round(f / (t_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "traffic": measured_traffic(w.name, DOMINANT_KERNEL[("tile_worker", w.dtype,
+                                                                                   w.head_dim)])}
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, q, kc, vc, args.cpu_seconds)
         result["cpu_baseline"] = {

@@ -148,8 +148,10 @@ pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* 
                      int32_t* dev_status, void* stream);
 
 /* Measurement hook, for timing only (changes nothing that is computed).
- * pa_forward runs four stages on its stream: 0 planner, 1 VALU worker, 2 MFMA
- * worker, 3 log-sum-exp merge.  After this call, every pa_forward on the
+ * pa_forward runs five stages on its stream: 0 planner, 1 VALU worker (decode
+ * rows with one query head per KV head), 2 MFMA worker (GQA decode rows and
+ * short prefill chunks), 3 tile worker (prefill chunks of more than 16 rows
+ * per KV head), 4 log-sum-exp merge.  After this call, every pa_forward on the
  * calling thread records events[2k] before and events[2k+1] after stage k
  * (k < num_events/2) with hipEventRecord on its stream; a stage that has no
  * work records both events back to back.  events: host array of hipEvent_t

@@ -1112,13 +1112,15 @@ void launch_attention(const AttnParams& p, bool may_valu, bool may_mfma, bool ma
     hipLaunchKernelGGL((valu_attn_kernel<T, D>), dim3(grid_v), dim3(256), 0, stream, p);
   mark(1, 1, stream);
   mark(2, 0, stream);
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (sizeof(T) == 2)
     if (may_mfma) hipLaunchKernelGGL((mfma_attn_kernel<D>), dim3(grid_m), dim3(256), 0, stream, p);
-    if (may_tile)
-      hipLaunchKernelGGL((tile_attn_kernel<D>), dim3(grid_t), dim3(64 * kTileWaves), 0, stream, p);
-  }
   mark(2, 1, stream);
   mark(3, 0, stream);
+  if constexpr (sizeof(T) == 2)
+    if (may_tile)
+      hipLaunchKernelGGL((tile_attn_kernel<D>), dim3(grid_t), dim3(64 * kTileWaves), 0, stream, p);
+  mark(3, 1, stream);
+  mark(4, 0, stream);
   if (p.maxparts > 1) {
     // many partitions per row (long contexts): four wavefronts share a row
     const int64_t rows = (int64_t)p.T * p.Hq;  // bound on the rows to merge
@@ -1129,7 +1131,7 @@ void launch_attention(const AttnParams& p, bool may_valu, bool may_mfma, bool ma
       hipLaunchKernelGGL((merge_kernel<T, D, 1>), dim3((unsigned)std::min<int64_t>(kMaxWorkerGroups, (rows + 3) / 4)),
                          dim3(256), 0, stream, p);
   }
-  mark(3, 1, stream);
+  mark(4, 1, stream);
 }
 
 }  // namespace
