@@ -12,6 +12,9 @@ inputs resident in device memory before timing starts:
 * llama7b / gqa70b / gqa70b_long: decode-only passes (batch 64 MHA 32x128;
   batch 32 GQA 64/8 at 2048 keys; one GQA sequence of 32768 keys).  value =
   KV bytes read per second.
+* sampling: the parallel-sampling workflow (16 prompts x 4 branches sharing
+  prompt pages, copy-on-write, 64 decode rows per step); value = decode
+  tokens per second over the timed steps, allocator and uploads included.
 * copy / read: calibration lines, not the path — a 4 GiB device copy, and
   every 4 KiB page of a 4 GiB pool read once in random order (pa_read_pages),
   the attainable HBM rates the kernels' fractions are set against.
@@ -259,13 +262,119 @@ def read_calibration(torch, pa, dev, args, nbytes=4 << 30, grid=2048):
                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}), flush=True)
 
 
+def sampling_workflow(torch, pa, W, dev, args):
+    """Parallel sampling with shared prompt pages: 16 prompts (lengths uniform in
+    [1000, 4000]) written once and forked into 4 branches each; every decode step
+    appends one token per branch in the host allocator, copies the pages it
+    reports (copy-on-write of a shared partial page), writes the 64 new K/V
+    through their slots and runs attention for the 64 rows.  warmup + steps
+    decode steps in all (256 by default), the last `steps` timed, host allocator
+    work and the per-step uploads of slots and tables included."""
+    spec = W.parallel_sampling_spec(0)
+    P, B, NB, H, d = len(spec.prompt_lens), spec.branches, spec.num_blocks, spec.heads, spec.head_dim
+    total = args.warmup + args.steps
+    n = P * B
+    ks, vs = W.cache_shapes(NB, H, d, "bf16")
+    gen = torch.Generator(device=dev).manual_seed(0)
+    kc = W.fill_normal(torch.empty(ks, dtype=torch.bfloat16, device=dev), gen)
+    vc = W.fill_normal(torch.empty(vs, dtype=torch.bfloat16, device=dev), gen)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    alloc = pa.Allocator(NB, 16, 0.0, spec.initial_free_order)
+    ids = [p * B + b for p in range(P) for b in range(B)]
+    for p, L in enumerate(spec.prompt_lens):
+        alloc.create(p * B, int(L))
+    slots = np.concatenate([alloc.slots(p * B, 0, int(L)) for p, L in enumerate(spec.prompt_lens)])
+    knew = W.fill_normal(torch.empty((len(slots), H, d), dtype=torch.bfloat16, device=dev), gen)
+    vnew = W.fill_normal(torch.empty((len(slots), H, d), dtype=torch.bfloat16, device=dev), gen)
+    pa.pa_reshape_and_cache(knew, vnew, kc, vc, torch.from_numpy(slots.astype(np.int64)).to(dev), status)
+    for p in range(P):
+        for b in range(1, B):
+            alloc.fork(p * B, p * B + b)
+    del knew, vnew
+    qs = W.fill_normal(torch.empty((total, n, H, d), dtype=torch.bfloat16, device=dev), gen)
+    kst = W.fill_normal(torch.empty((total, n, H, d), dtype=torch.bfloat16, device=dev), gen)
+    vst = W.fill_normal(torch.empty((total, n, H, d), dtype=torch.bfloat16, device=dev), gen)
+    lens = np.repeat(spec.prompt_lens.astype(np.int32), B)
+    max_ctx = int(lens.max()) + total
+    cap_max = (max_ctx + 15) // 16
+    qsl = torch.arange(n + 1, dtype=torch.int32, device=dev)
+    nbytes = pa.pa_forward_workspace_bytes(n, n, 1, H, H, d, max_ctx, pa.PA_BF16)
+    ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((n, H, d), dtype=torch.bfloat16, device=dev)
+    # pinned upload buffers, one set per step, so no copy waits for the device
+    up_slots = torch.empty((total, n), dtype=torch.int64).pin_memory()
+    up_tab = torch.empty((total, n * cap_max), dtype=torch.int32).pin_memory()
+    up_lens = torch.empty((total, n), dtype=torch.int32).pin_memory()
+    up_pairs = torch.empty((total, 2 * n), dtype=torch.int32).pin_memory()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    ev = HipEvents()
+    fwd_ev = ev.new(2 * total)
+    logical = []
+    torch.cuda.synchronize()
+
+    def decode_step(i, record):
+        sl, pairs = alloc.append_slots(ids)
+        lens[:] += 1
+        cap = (int(lens.max()) + 15) // 16
+        tab = alloc.block_tables(ids, cap)
+        up_slots[i].numpy()[:] = sl
+        up_lens[i].numpy()[:] = lens
+        up_tab[i].numpy()[:n * cap] = tab.reshape(-1)
+        if len(pairs):
+            pr = up_pairs[i, :2 * len(pairs)]
+            pr.numpy()[:] = np.asarray(pairs, np.int32).reshape(-1)
+            pa.pa_copy_blocks(kc, vc, pr.to(dev, non_blocking=True).view(-1, 2), status)
+        pa.pa_reshape_and_cache(kst[i], vst[i], kc, vc, up_slots[i].to(dev, non_blocking=True), status)
+        tables = up_tab[i, :n * cap].to(dev, non_blocking=True).view(n, cap)
+        if record:
+            ev.record(fwd_ev[2 * i], stream)
+        pa.pa_forward(out, qs[i], kc, vc, tables, up_lens[i].to(dev, non_blocking=True), qsl, 1, max_ctx,
+                      1.0 / np.sqrt(d), ws, status)
+        if record:
+            ev.record(fwd_ev[2 * i + 1], stream)
+            logical.append(int(lens.sum()))
+
+    for i in range(args.warmup):
+        decode_step(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.warmup, total):
+        decode_step(i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    if int(status.item()) != 0:
+        raise RuntimeError(f"device status {int(status.item()):#x}")
+    fwd_ms = [ev.ms(fwd_ev[2 * i], fwd_ev[2 * i + 1]) for i in range(args.warmup, total)]
+    ev.close()
+    tok_bytes = 2 * H * d * 2
+    logical_bytes = sum(logical) * tok_bytes
+    # unique pages: every prompt token once, plus each branch's own decode tokens
+    unique_bytes = sum((int(spec.prompt_lens.sum()) + n * (i + 1)) * tok_bytes for i in range(args.warmup, total))
+    fwd_s = sum(fwd_ms) * 1e-3
+    ms_per_step = 1e3 * elapsed / args.steps
+    achieved = unique_bytes / fwd_s / 1e9
+    print(json.dumps({
+        "metric": "parallel sampling decode tokens/s (shared prompt pages, copy-on-write)",
+        "value": round(n * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "parallel_sampling_16x4", "prompts": P, "branches": B, "q_heads": H, "kv_heads": H,
+                   "head_dim": d, "block_size": 16, "pool_blocks": NB, "decode_steps": total},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "pa_forward",
+                     "kernel_ms": round(1e3 * fwd_s / args.steps, 4), "algorithmic_bytes": "unique KV pages per step"},
+        "forward_logical_kv_GBps": round(logical_bytes / fwd_s / 1e9, 1),
+        "forward_unique_kv_GBps": round(achieved, 1),
+        "forward_share_of_step": round(1e3 * fwd_s / args.steps / ms_per_step, 4)}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="splitfuse",
-                    choices=["splitfuse", "llama7b", "gqa70b", "gqa70b_long", "tiny", "copy", "read"])
+                    choices=["splitfuse", "llama7b", "gqa70b", "gqa70b_long", "tiny", "copy", "read", "sampling"])
     ap.add_argument("--rotate", type=int, default=0, help="pool copies cycled per step (0: enough to exceed the 256 MB MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -285,6 +394,11 @@ def main():
         return copy_calibration(torch, dev, args)
     if args.workload == "read":
         return read_calibration(torch, pa, dev, args)
+    if args.workload == "sampling":
+        if args.warmup + args.steps > 256:
+            print("the sampling workflow runs at most 256 decode steps (warmup + steps)", file=sys.stderr)
+            sys.exit(2)
+        return sampling_workflow(torch, pa, W, dev, args)
     w = build_workload(args.workload)
     code = pa.PA_BF16 if w.dtype == "bf16" else pa.PA_F32
     q, kc, vc, nk, nv = W.make_values(w, dev)
