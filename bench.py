@@ -328,7 +328,7 @@ def sampling_workflow(torch, pa, W, dev, args):
         tables = up_tab[i, :n * cap].to(dev, non_blocking=True).view(n, cap)
         if record:
             ev.record(fwd_ev[2 * i], stream)
-        pa.pa_forward(out, qs[i], kc, vc, tables, up_lens[i].to(dev, non_blocking=True), qsl, 1, max_ctx,
+        pa.pa_forward(out, qs[i], kc, vc, tables, up_lens[i].to(dev, non_blocking=True), qsl, 1, int(lens.max()),
                       1.0 / np.sqrt(d), ws, status)
         if record:
             ev.record(fwd_ev[2 * i + 1], stream)
