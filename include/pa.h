@@ -205,6 +205,7 @@ typedef struct pa_allocator pa_allocator;
 pa_status pa_alloc_create(int32_t num_blocks, int32_t block_size, double watermark,
                           const int32_t* initial_free_order, pa_allocator** out);
 void pa_alloc_destroy(pa_allocator* a);
+/* Free blocks (with prefix caching: free stack + evictor). */
 int32_t pa_alloc_num_free(const pa_allocator* a);
 /* Reference count of a block, or -1 for an id outside the pool. */
 int32_t pa_alloc_ref_count(const pa_allocator* a, int32_t block);
@@ -246,8 +247,47 @@ pa_status pa_seq_block_table(const pa_allocator* a, int64_t seq_id, int32_t* out
 pa_status pa_seq_block_tables(const pa_allocator* a, int32_t n, const int64_t* seq_ids,
                               int32_t* out, int32_t cap);
 /* Drop the sequence: one reference less on each block in logical order;
- * blocks reaching zero return to the free stack in that order. */
+ * blocks reaching zero return to the free stack in that order (with prefix
+ * caching, a block carrying a hash goes to the evictor instead). */
 pa_status pa_seq_free(pa_allocator* a, int64_t seq_id);
+
+/* ------------------------------------------------------------------ prefix caching
+ * Reuse of the pages of equal prompt prefixes ("大模型部署.md" §2.1 item 3,
+ * CachedBlockAllocator and LRUEvictor; "【自用】AI infra相关" part 二.4(2)).
+ * Every full block of a sequence made from token ids gets a 64-bit hash of
+ * the previous block's hash and its own 16 token ids (a hit also compares the
+ * tokens and the parent hash, so a collision costs a miss, never a wrong
+ * page).  A block whose hash is cached — in use, or released and waiting in
+ * the evictor — is shared instead of allocated.  Released hashed blocks wait
+ * in the evictor and still count as free: a new block comes from the free
+ * stack, and only when that is empty from the evictor, which gives up the
+ * block released longest ago (an allocator clock advances once per mutating
+ * call), among blocks released by the same call the one whose hash covers the
+ * most tokens.  Sequences made with pa_seq_create never carry hashes; those
+ * made from token ids must append with pa_seq_append_tokens.
+ *
+ * Switch prefix caching on; the allocator must not be in use yet
+ * (PA_ERR_INVALID otherwise). */
+pa_status pa_alloc_enable_prefix_caching(pa_allocator* a);
+/* Blocks waiting in the evictor (included in pa_alloc_num_free). */
+int32_t pa_alloc_num_evictable(const pa_allocator* a);
+/* New sequence from host token_ids[num_tokens]: every full block whose hash is
+ * cached is shared (these are taken first, in logical order), the other
+ * blocks are new (a new full block is registered under its hash).  All or
+ * nothing.  *num_cached_tokens = 16 x the number of leading full blocks that
+ * were shared: the prefix whose K/V the pool already holds once the sequence
+ * that made those pages has written them; the caller writes tokens from there
+ * on (a remainder past the last full block is always new). */
+pa_status pa_seq_create_tokens(pa_allocator* a, int64_t seq_id, const int32_t* token_ids,
+                               int32_t num_tokens, int32_t* num_cached_tokens);
+/* pa_seq_append_slots for sequences made from token ids, with the new token of
+ * each (token_ids: host int32 [n]).  When a token fills the last block and an
+ * equal block is cached, the sequence switches to that block (one more
+ * reference; the filled block is released, or, when it was shared, keeps its
+ * other users and no copy is reported); otherwise the filled block (the copy,
+ * when it was shared) is registered under its hash. */
+pa_status pa_seq_append_tokens(pa_allocator* a, int32_t n, const int64_t* seq_ids, const int32_t* token_ids,
+                               int64_t* slots_out, int32_t* cow_pairs_out, int32_t* num_cow_out);
 
 #ifdef __cplusplus
 }

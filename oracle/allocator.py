@@ -144,3 +144,259 @@ class Allocator:
             self.ref[b] -= 1
             if self.ref[b] == 0:
                 self.free.append(b)
+
+
+class PrefixCachingAllocator(Allocator):
+    """The allocator with prefix caching ("大模型部署.md" §2.1 item 3,
+    CachedBlockAllocator and LRUEvictor; "【自用】AI infra相关" part 二.4(2),
+    prefix caching by block hashes).
+
+    Rules, with where they come from and the readings taken:
+
+    * Only full blocks are hashed.  The identity of full block j of a
+      sequence is its whole token prefix (tokens 0 .. P(j+1)−1): the pages
+      chain each block's hash with the previous block's, so two blocks match
+      only when everything before them matches too.  The mirror uses that
+      prefix itself as the key (no hash function, no collisions); the
+      library uses a 64-bit chained hash and compares the block's own tokens
+      and its parent's hash on a hit.
+    * ``create_tokens(seq, tokens)``: every full block whose key is cached
+      (in use by another sequence, or waiting in the evictor) is reused — one
+      more reference, and a block in the evictor leaves it; every other
+      block is new and a new full block is registered under its key.  Reused
+      blocks are taken first, in logical order, then the new ones in logical
+      order (reading: so that making room for a new block can never evict a
+      block this same call reuses).  Returns the cached prefix length: P
+      times the number of leading full blocks that were reused (the tokens
+      the caller need not recompute; a non-aligned remainder is always
+      recomputed, part 二.4(2)).  All or nothing.
+    * A new block comes from the free stack; when that is empty, one block is
+      evicted: in the evictor's insertion order, the first block, replaced by
+      a later one with more hashed tokens while their access times are equal
+      (LRUEvictor.evict).  Its key is forgotten.
+    * ``free(seq)``: blocks whose count reaches zero go to the evictor when
+      they carry a key (access time = the allocator's clock at that call;
+      reading: the pages use the last access time, and a block is last used
+      by the call that releases it) and to the free stack otherwise.
+    * ``append_token(seq, token)``: as ``append_slot``; when the token fills
+      the last block and the block's key is already cached by another block,
+      the sequence switches to that block (one more reference; the filled
+      block returns to the free stack, or, when it was shared, keeps its
+      other users and no copy is made) — ``_maybe_promote_last_block``; when
+      the key is not cached, the filled block (the copy, if it was shared) is
+      registered under it.
+    * ``num_free()`` counts free and evictor blocks (blocks in the evictor are
+      available, part of the pages' account of usable blocks).
+    * The clock advances by one at every mutating call.
+
+    Sequences made by ``create`` (no tokens) never get keys; forks inherit
+    their parent's tokens.
+    """
+
+    def __init__(self, num_blocks: int, block_size: int = 16, watermark: float = 0.0,
+                 initial_free_order=None):
+        super().__init__(num_blocks, block_size, watermark, initial_free_order)
+        self.key = [None] * num_blocks          # block -> prefix key
+        self.hashed_tokens = [0] * num_blocks   # tokens the key covers
+        self.accessed = [0] * num_blocks
+        self.cached = {}                        # key -> block
+        self.evictor = []                       # blocks with a key and no reference, insertion order
+        self.tokens = {}                        # seq -> token list (only sequences made with tokens)
+        self.clock = 0
+
+    # -- queries
+    def num_free(self) -> int:
+        return len(self.free) + len(self.evictor)
+
+    def num_evictable(self) -> int:
+        return len(self.evictor)
+
+    def can_allocate(self, n_tokens: int) -> int:
+        req = self.blocks_for(n_tokens)
+        if self.N - req < self.wm:
+            return NEVER
+        if self.num_free() - req >= self.wm:
+            return OK
+        return LATER
+
+    # -- helpers
+    def _evict(self) -> int:
+        cand = self.evictor[0]
+        for b in self.evictor:
+            if self.accessed[cand] < self.accessed[b]:
+                break
+            if self.hashed_tokens[cand] < self.hashed_tokens[b]:
+                cand = b
+        self.evictor.remove(cand)
+        del self.cached[self.key[cand]]
+        self.key[cand] = None
+        self.hashed_tokens[cand] = 0
+        return cand
+
+    def _pop(self) -> int:
+        b = self.free.pop() if self.free else self._evict()
+        self.ref[b] = 1
+        return b
+
+    def _share(self, b: int) -> None:
+        if self.ref[b] == 0:
+            self.evictor.remove(b)
+        self.ref[b] += 1
+
+    def _register(self, b: int, key, ntok: int) -> None:
+        self.key[b] = key
+        self.hashed_tokens[b] = ntok
+        self.cached[key] = b
+
+    def _release(self, b: int) -> None:
+        if self.ref[b] <= 0:
+            raise RuntimeError("reference count underflow")
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            if self.key[b] is not None:
+                self.accessed[b] = self.clock
+                self.evictor.append(b)
+            else:
+                self.free.append(b)
+
+    # -- mutations
+    def create(self, seq, n_tokens: int) -> None:
+        if seq in self.tables:
+            raise ValueError("sequence exists")
+        if n_tokens < 0:
+            raise ValueError("negative length")
+        req = self.blocks_for(n_tokens)
+        if req > self.num_free():
+            raise NoBlocks("not enough free blocks")
+        self.clock += 1
+        self.tables[seq] = [self._pop() for _ in range(req)]
+        self.ntok[seq] = n_tokens
+
+    def create_tokens(self, seq, tokens) -> int:
+        tokens = [int(t) for t in tokens]
+        if seq in self.tables:
+            raise ValueError("sequence exists")
+        L, P = len(tokens), self.P
+        nblk = self.blocks_for(L)
+        keys = [tuple(tokens[:P * (j + 1)]) for j in range(L // P)]
+        hits = [j for j, k in enumerate(keys) if k in self.cached]
+        revive = sum(1 for j in hits if self.ref[self.cached[keys[j]]] == 0)
+        if nblk - len(hits) > self.num_free() - revive:
+            raise NoBlocks("not enough free blocks")
+        self.clock += 1
+        tab = [None] * nblk
+        for j in hits:
+            b = self.cached[keys[j]]
+            self._share(b)
+            tab[j] = b
+        for j in range(nblk):
+            if tab[j] is None:
+                tab[j] = self._pop()
+                if j < len(keys):
+                    self._register(tab[j], keys[j], P * (j + 1))
+        self.tables[seq] = tab
+        self.ntok[seq] = L
+        self.tokens[seq] = tokens
+        lead = 0
+        while lead < len(keys) and lead in set(hits):
+            lead += 1
+        return lead * P
+
+    def fork(self, parent, child) -> None:
+        super().fork(parent, child)
+        self.clock += 1
+        if parent in self.tokens:
+            self.tokens[child] = list(self.tokens[parent])
+
+    def append_slot(self, seq):
+        """As the base allocator's; new blocks may come from the evictor."""
+        if seq in self.tokens:
+            raise ValueError("a sequence made with tokens appends with append_token")
+        tab = self.tables[seq]
+        L = self.ntok[seq]
+        need = self.blocks_for(L + 1)
+        if (len(tab) < need or self.ref[tab[-1]] > 1) and self.num_free() == 0:
+            raise NoBlocks("no free block")
+        self.clock += 1
+        cow = None
+        if len(tab) < need:
+            tab.append(self._pop())
+        elif self.ref[tab[-1]] > 1:
+            old = tab[-1]
+            new = self._pop()
+            tab[-1] = new
+            self.ref[old] -= 1
+            cow = (old, new)
+        self.ntok[seq] = L + 1
+        return tab[L // self.P] * self.P + L % self.P, cow
+
+    def append_token(self, seq, token):
+        """Returns (slot, (old, new) or None) for the token at position ntok[seq]."""
+        if seq not in self.tables:
+            raise KeyError("unknown sequence")
+        if seq not in self.tokens:
+            raise ValueError("append_token needs a sequence made with tokens")
+        tab = self.tables[seq]
+        L, P = self.ntok[seq], self.P
+        toks = self.tokens[seq] + [int(token)]
+        need = self.blocks_for(L + 1)
+        fills = (L + 1) % P == 0
+        key = tuple(toks) if fills else None
+        hit = self.cached.get(key) if fills else None
+        if len(tab) < need:
+            if self.num_free() == 0:
+                raise NoBlocks("no free block for the new token")
+            self.clock += 1
+            tab.append(self._pop())          # a new block holds one token: never full unless P == 1
+            if fills:
+                if hit is not None:
+                    self._release(tab[-1])
+                    self._share(hit)
+                    tab[-1] = hit
+                else:
+                    self._register(tab[-1], key, L + 1)
+            cow = None
+        elif self.ref[tab[-1]] > 1:
+            if hit is None and self.num_free() == 0:
+                raise NoBlocks("no free block for copy-on-write")
+            self.clock += 1
+            old = tab[-1]
+            if hit is not None:
+                self._share(hit)
+                self.ref[old] -= 1           # still held by another sequence
+                tab[-1] = hit
+                cow = None
+            else:
+                new = self._pop()
+                self.ref[old] -= 1
+                tab[-1] = new
+                cow = (old, new)
+                if fills:
+                    self._register(new, key, L + 1)
+        else:
+            self.clock += 1
+            if fills:
+                if hit is not None:
+                    self._share(hit)
+                    self._release(tab[-1])
+                    tab[-1] = hit
+                else:
+                    self._register(tab[-1], key, L + 1)
+            cow = None
+        self.ntok[seq] = L + 1
+        self.tokens[seq] = toks
+        return tab[L // P] * P + L % P, cow
+
+    def free_seq(self, seq) -> None:
+        if seq not in self.tables:
+            raise KeyError("unknown sequence")
+        tab = self.tables[seq]
+        for b in tab:
+            if self.ref[b] <= 0:
+                raise RuntimeError("reference count underflow")
+        self.clock += 1
+        del self.tables[seq]
+        del self.ntok[seq]
+        self.tokens.pop(seq, None)
+        for b in tab:
+            self._release(b)

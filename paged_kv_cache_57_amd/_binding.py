@@ -67,6 +67,10 @@ _SIGS = {
     "pa_seq_block_table": (_i32, [_vp, _i64, _vp, _i32, _pi32]),
     "pa_seq_block_tables": (_i32, [_vp, _i32, _vp, _vp, _i32]),
     "pa_seq_free": (_i32, [_vp, _i64]),
+    "pa_alloc_enable_prefix_caching": (_i32, [_vp]),
+    "pa_alloc_num_evictable": (_i32, [_vp]),
+    "pa_seq_create_tokens": (_i32, [_vp, _i64, _vp, _i32, _vp]),
+    "pa_seq_append_tokens": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -287,3 +291,30 @@ class Allocator:
 
     def free(self, seq_id: int):
         _check(_lib.pa_seq_free(self._h, seq_id))
+
+    # prefix caching
+    def enable_prefix_caching(self):
+        _check(_lib.pa_alloc_enable_prefix_caching(self._h))
+
+    def num_evictable(self) -> int:
+        return _lib.pa_alloc_num_evictable(self._h)
+
+    def create_tokens(self, seq_id: int, token_ids) -> int:
+        """New sequence from token ids; returns the length of the cached prefix."""
+        toks = np.ascontiguousarray(token_ids, dtype=np.int32)
+        out = ctypes.c_int32()
+        _check(_lib.pa_seq_create_tokens(self._h, seq_id, _np_ptr(toks) if toks.size else None, toks.size,
+                                         ctypes.byref(out)))
+        return out.value
+
+    def append_tokens(self, seq_ids, token_ids):
+        ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+        toks = np.ascontiguousarray(token_ids, dtype=np.int32)
+        if toks.shape != ids.shape:
+            raise PAError(PA_ERR_INVALID, "one token per sequence")
+        slots = np.empty(len(ids), np.int64)
+        pairs = np.empty((max(len(ids), 1), 2), np.int32)
+        n = ctypes.c_int32()
+        _check(_lib.pa_seq_append_tokens(self._h, len(ids), _np_ptr(ids), _np_ptr(toks), _np_ptr(slots),
+                                         _np_ptr(pairs), ctypes.byref(n)))
+        return slots, pairs[:n.value].copy()

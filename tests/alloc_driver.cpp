@@ -9,6 +9,10 @@
 //   can n               -> pa_alloc_can_allocate                     prints status answer
 //   table id            -> pa_seq_block_table                        prints status n b0 b1 ...
 //   nfree               -> pa_alloc_num_free                         prints count
+//   caching             -> pa_alloc_enable_prefix_caching            prints status
+//   ctok id t0 t1 ...   -> pa_seq_create_tokens                      prints status cached
+//   atok id t           -> pa_seq_append_tokens (one sequence)       prints status slot src dst
+//   nevict              -> pa_alloc_num_evictable                    prints count
 #include <cstdio>
 #include <iostream>
 #include <sstream>
@@ -71,6 +75,27 @@ int main() {
       std::printf("\n");
     } else if (op == "nfree") {
       std::printf("%d\n", pa_alloc_num_free(a));
+    } else if (op == "caching") {
+      std::printf("%d\n", pa_alloc_enable_prefix_caching(a));
+    } else if (op == "ctok") {
+      long long id;
+      in >> id;
+      std::vector<int32_t> toks;
+      int32_t t;
+      while (in >> t) toks.push_back(t);
+      int32_t cached = -1;
+      int st = pa_seq_create_tokens(a, id, toks.data(), (int32_t)toks.size(), &cached);
+      std::printf("%d %d\n", st, cached);
+    } else if (op == "atok") {
+      long long id;
+      int32_t t;
+      in >> id >> t;
+      int64_t sid = id, slot = -1;
+      int32_t pair[2] = {-1, -1}, ncow = 0;
+      int st = pa_seq_append_tokens(a, 1, &sid, &t, &slot, pair, &ncow);
+      std::printf("%d %lld %d %d\n", st, (long long)slot, ncow ? pair[0] : -1, ncow ? pair[1] : -1);
+    } else if (op == "nevict") {
+      std::printf("%d\n", pa_alloc_num_evictable(a));
     }
   }
   if (a) pa_alloc_destroy(a);
