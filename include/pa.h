@@ -289,6 +289,33 @@ pa_status pa_seq_create_tokens(pa_allocator* a, int64_t seq_id, const int32_t* t
 pa_status pa_seq_append_tokens(pa_allocator* a, int32_t n, const int64_t* seq_ids, const int32_t* token_ids,
                                int64_t* slots_out, int32_t* cow_pairs_out, int32_t* num_cow_out);
 
+/* ------------------------------------------------------------------ SplitFuse composer
+ * Host-side composition of forward passes under a token budget
+ * ("DeepSpeed-FastGen 深度解析" §3.1-§3.2, Dynamic SplitFuse: long prompts are
+ * split over several passes, short ones fused to fill the budget exactly;
+ * "第 15 章：推理引擎与部署", chunked prefill: Σ chunk tokens + number of decodes
+ * <= budget).  A pass takes every running decode (one token each, in the
+ * order the sequences started decoding; those past the budget wait), then
+ * prompt chunks in arrival order, each min(tokens remaining, budget left),
+ * until the budget is used.  A prompt decodes from the pass after the one
+ * that took its last chunk.  Opaque handle, not thread-safe; every failing
+ * call leaves it unchanged. */
+typedef struct pa_splitfuse pa_splitfuse;
+pa_status pa_sf_create(int32_t token_budget, pa_splitfuse** out);
+void pa_sf_destroy(pa_splitfuse* c);
+/* Queue a prompt of prompt_len (> 0) tokens; seq_id must be new. */
+pa_status pa_sf_add_prompt(pa_splitfuse* c, int64_t seq_id, int32_t prompt_len);
+/* Remove a sequence, queued or decoding (PA_ERR_NOT_FOUND if unknown). */
+pa_status pa_sf_finish(pa_splitfuse* c, int64_t seq_id);
+/* Compose the next pass into host arrays of capacity cap: row i is sequence
+ * seq_ids[i] with q_lens[i] query tokens and context_lens[i] keys after the
+ * pass (its earlier tokens included) — prompt chunks first, then decodes, the
+ * order pa_forward's query_start_loc takes them.  *num_rows_out = rows (also
+ * when cap is too small: PA_ERR_INVALID, nothing changes), *num_tokens_out =
+ * Σ q_lens. */
+pa_status pa_sf_step(pa_splitfuse* c, int32_t cap, int64_t* seq_ids, int32_t* q_lens, int32_t* context_lens,
+                     int32_t* num_rows_out, int32_t* num_tokens_out);
+
 #ifdef __cplusplus
 }
 #endif

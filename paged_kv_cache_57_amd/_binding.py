@@ -71,6 +71,11 @@ _SIGS = {
     "pa_alloc_num_evictable": (_i32, [_vp]),
     "pa_seq_create_tokens": (_i32, [_vp, _i64, _vp, _i32, _vp]),
     "pa_seq_append_tokens": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "pa_sf_create": (_i32, [_i32, _vp]),
+    "pa_sf_destroy": (None, [_vp]),
+    "pa_sf_add_prompt": (_i32, [_vp, _i64, _i32]),
+    "pa_sf_finish": (_i32, [_vp, _i64]),
+    "pa_sf_step": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -318,3 +323,47 @@ class Allocator:
         _check(_lib.pa_seq_append_tokens(self._h, len(ids), _np_ptr(ids), _np_ptr(toks), _np_ptr(slots),
                                          _np_ptr(pairs), ctypes.byref(n)))
         return slots, pairs[:n.value].copy()
+
+
+class SplitFuse:
+    """Host composer of SplitFuse passes (pa_sf_*): add prompts, take passes."""
+
+    def __init__(self, token_budget: int):
+        h = ctypes.c_void_p()
+        _check(_lib.pa_sf_create(token_budget, ctypes.byref(h)))
+        self._h = h
+        self.budget = token_budget
+
+    def close(self):
+        if self._h:
+            _lib.pa_sf_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def add_prompt(self, seq_id: int, prompt_len: int):
+        _check(_lib.pa_sf_add_prompt(self._h, seq_id, prompt_len))
+
+    def finish(self, seq_id: int):
+        _check(_lib.pa_sf_finish(self._h, seq_id))
+
+    def step(self):
+        """The next pass as (seq_ids int64, q_lens int32, context_lens int32)."""
+        cap = 256
+        while True:
+            ids = np.empty(cap, np.int64)
+            ql = np.empty(cap, np.int32)
+            cl = np.empty(cap, np.int32)
+            rows, toks = ctypes.c_int32(), ctypes.c_int32()
+            st = _lib.pa_sf_step(self._h, cap, _np_ptr(ids), _np_ptr(ql), _np_ptr(cl), ctypes.byref(rows),
+                                 ctypes.byref(toks))
+            if st == PA_OK:
+                n = rows.value
+                return ids[:n].copy(), ql[:n].copy(), cl[:n].copy()
+            if rows.value <= cap:
+                _check(st)
+            cap = rows.value

@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_status.cpp", "pa_alloc.cpp", "pa_cache.hip", "pa_attention.hip"]
+SOURCES = ["pa_status.cpp", "pa_alloc.cpp", "pa_splitfuse.cpp", "pa_cache.hip", "pa_attention.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # No packed FP32 instructions; and no atomic optimizer, which wraps each atomic in a
 # branch on the first active lane (the kernels keep their work loops free of

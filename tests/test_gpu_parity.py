@@ -323,6 +323,72 @@ def test_parallel_sampling_workflow(pa):
     assert copies > 0
 
 
+def test_composer_driven_passes(pa):
+    """Passes composed by the SplitFuse composer (budget 2048, prompts of 3000, 700,
+    300 tokens, then 5000 and 64 arriving later) run end to end: allocator slots,
+    cache write of every new token, one forward per pass; every row against the
+    oracle on a host copy of the pool."""
+    from oracle import attention as oattn
+    from oracle import cache_ops
+    from tests._gpu import TOL, host_raw
+    H, d, NB, budget = 8, 128, 2048, 2048
+    ks, vs = W.cache_shapes(NB, H, d, "bf16")
+    gen = torch.Generator(device=DEV).manual_seed(3)
+    kc = W.fill_normal(torch.empty(ks, dtype=torch.bfloat16, device=DEV), gen)
+    vc = W.fill_normal(torch.empty(vs, dtype=torch.bfloat16, device=DEV), gen)
+    kh, vh = host_raw(kc).copy(), host_raw(vc).copy()
+    alloc = pa.Allocator(NB, 16)
+    comp = pa.SplitFuse(budget)
+    prompts = {0: 3000, 1: 700, 2: 300, 3: 5000, 4: 64}
+    arrive = {0: [0, 1, 2], 2: [3, 4]}
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    worst = 0.0
+    for step in range(8):
+        for sid in arrive.get(step, []):
+            comp.add_prompt(sid, prompts[sid])
+        ids, ql, cl = comp.step()
+        assert int(ql.sum()) <= budget
+        slots = []
+        for sid, q, ctx in zip(ids.tolist(), ql.tolist(), cl.tolist()):
+            if ctx == q:                          # first chunk: pages for the whole prompt
+                alloc.create(sid, prompts[sid])
+            if ctx <= prompts[sid]:
+                slots.append(alloc.slots(sid, ctx - q, q))
+            else:
+                slot, cow = alloc.append_slot(sid)
+                assert cow is None
+                slots.append(np.array([slot], np.int64))
+        slots = np.concatenate(slots)
+        T = len(slots)
+        k_new = W.fill_normal(torch.empty((T, H, d), dtype=torch.bfloat16, device=DEV), gen)
+        v_new = W.fill_normal(torch.empty((T, H, d), dtype=torch.bfloat16, device=DEV), gen)
+        q = W.fill_normal(torch.empty((T, H, d), dtype=torch.bfloat16, device=DEV), gen)
+        pa.pa_reshape_and_cache(k_new, v_new, kc, vc, torch.from_numpy(slots).to(DEV), status)
+        cache_ops.reshape_and_cache(host_raw(k_new), host_raw(v_new), kh, vh, slots, inplace=True)
+        lens = cl.astype(np.int32)
+        qsl = np.concatenate([[0], np.cumsum(ql)]).astype(np.int32)
+        cap = int((lens.max() + 15) // 16)
+        tables = alloc.block_tables(ids, max(cap, max(len(alloc.block_table(int(s))) for s in ids)))
+        nbytes = pa.pa_forward_workspace_bytes(len(ids), T, int(ql.max()), H, H, d, int(lens.max()), pa.PA_BF16)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+        out = torch.empty_like(q)
+        say(f"[case] composer pass {step}: rows {len(ids)}, tokens {T}, max q {int(ql.max())}, max ctx {int(lens.max())}")
+        pa.pa_forward(out, q, kc, vc, torch.from_numpy(tables).to(DEV), torch.from_numpy(lens).to(DEV),
+                      torch.from_numpy(qsl).to(DEV), int(ql.max()), int(lens.max()), scale, ws, status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0
+        ref = oattn.paged_attention(host_raw(q), kh, vh, tables, lens, qsl, scale, "bf16")
+        got = to_f64(out)
+        a, r = TOL["bf16"]
+        ratio = float((np.abs(got - ref) / (a + r * np.abs(ref))).max())
+        worst = max(worst, ratio)
+        assert np.isfinite(got).all() and ratio <= 1.0, (step, ratio)
+    say(f"  worst err/bound {worst:.3f}")
+    comp.close()
+    alloc.close()
+
+
 def read_probe_case():
     """Pages, a page list with one id outside the pool, and the sink the documented
     thread assignment gives: wavefront w XORs piece l, l+64, l+128, l+192 of its

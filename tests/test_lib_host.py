@@ -42,9 +42,10 @@ def test_library_exports_every_declared_function(pa):
     exported = set(re.findall(r"\bT (pa_\w+)", nm))
     assert set(names) <= exported
     assert set(pa.EXPORTS) == set(names)          # the binding declares exactly the header's functions
-    # every entry point outside the allocator (wrapped by pa.Allocator) is a package function
+    # every entry point outside the allocator and the composer (wrapped by pa.Allocator and
+    # pa.SplitFuse) is a package function
     for n in names:
-        if not n.startswith(("pa_alloc_", "pa_seq_")):
+        if not n.startswith(("pa_alloc_", "pa_seq_", "pa_sf_")):
             assert callable(getattr(pa, n, None)), n
 
 
