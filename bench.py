@@ -15,6 +15,9 @@ inputs resident in device memory before timing starts:
 * sampling: the parallel-sampling workflow (16 prompts x 4 branches sharing
   prompt pages, copy-on-write, 64 decode rows per step); value = decode
   tokens per second over the timed steps, allocator and uploads included.
+* splitfuse_rope: the same pass with the rotary embedding fused into the cache
+  write (pa_rope_reshape_and_cache rotates q and the new keys at their
+  positions; the forward reads the rotated q).
 * copy / read: calibration lines, not the path — a 4 GiB device copy, and
   every 4 KiB page of a 4 GiB pool read once in random order (pa_read_pages),
   the attainable HBM rates the kernels' fractions are set against.
@@ -120,6 +123,7 @@ def measured_traffic(workload, kernel):
 def build_workload(name):
     import workloads as W
     return {"splitfuse": lambda: W.splitfuse_mixed(0),
+            "splitfuse_rope": lambda: W.splitfuse_mixed(0),
             "llama7b": lambda: W.llama7b_decode(0),
             "gqa70b": lambda: W.gqa70b_decode(0),
             "gqa70b_long": lambda: W.gqa70b_long_decode(0),
@@ -374,7 +378,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="splitfuse",
-                    choices=["splitfuse", "llama7b", "gqa70b", "gqa70b_long", "tiny", "copy", "read", "sampling"])
+                    choices=["splitfuse", "splitfuse_rope", "llama7b", "gqa70b", "gqa70b_long", "tiny", "copy", "read",
+                             "sampling"])
     ap.add_argument("--rotate", type=int, default=0, help="pool copies cycled per step (0: enough to exceed the 256 MB MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -420,17 +425,30 @@ def main():
     out = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev).cuda_stream
     ev = HipEvents()
+    rope = args.workload == "splitfuse_rope"
+    if rope:
+        # the cache write rotates q (into qrot) and the new keys at their positions first
+        ql = np.diff(w.query_start_loc)
+        positions = torch.from_numpy(np.concatenate(
+            [np.arange(L - n, L) for n, L in zip(ql, w.context_lens)]).astype(np.int32)).to(dev)
+        cos_t, sin_t = (torch.from_numpy(t).to(dev) for t in W.rope_tables(w.max_context_len, w.head_dim))
+        qrot = torch.empty_like(q)
 
     def step(i, stage_events=None, write_events=None):
         kcur, vcur = pools[i % rotate]
+        qin = q
         if slots is not None:
             if write_events:
                 ev.record(write_events[0], stream)
-            pa.pa_reshape_and_cache(nk, nv, kcur, vcur, slots, status)
+            if rope:
+                pa.pa_rope_reshape_and_cache(qrot, q, nk, nv, kcur, vcur, slots, positions, cos_t, sin_t, status)
+                qin = qrot
+            else:
+                pa.pa_reshape_and_cache(nk, nv, kcur, vcur, slots, status)
             if write_events:
                 ev.record(write_events[1], stream)
         pa.pa_set_stage_events(stage_events)
-        pa.pa_forward(out, q, kcur, vcur, tables, lens, qsl, w.max_q_len, w.max_context_len, w.scale,
+        pa.pa_forward(out, qin, kcur, vcur, tables, lens, qsl, w.max_q_len, w.max_context_len, w.scale,
                       workspace, status)
 
     for i in range(args.warmup):
@@ -470,7 +488,7 @@ def main():
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
     }
-    if args.workload == "splitfuse":
+    if args.workload in ("splitfuse", "splitfuse_rope"):
         result.update(value=round(w.num_tokens / (ms_per_step * 1e-3), 1), unit="tokens/s")
     else:
         result.update(value=round(pass_bytes / (ms_per_step * 1e-3) / 1e9, 2), unit="GB/s")
@@ -492,7 +510,7 @@ def main():
                               "kernel_ms": round(stage_ms[dom], 4), "algorithmic_bytes": work[dom]["bytes"]}
     result["stages_ms"] = {k: round(v, 4) for k, v in stage_ms.items()}
     if slots is not None:
-        result["stages_ms"]["cache_write"] = round(write_ms, 4)
+        result["stages_ms"]["rope_cache_write" if rope else "cache_write"] = round(write_ms, 4)
     result["kv_read_GBps"] = round(pass_bytes / (sum(stage_ms[k] for k in WORKERS) * 1e-3) / 1e9, 1)
     for k in ("valu_worker", "mfma_worker"):
         if work[k]["bytes"] and not work[k]["flops"]:
@@ -509,9 +527,9 @@ def main():
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, q, kc, vc, args.cpu_seconds)
         result["cpu_baseline"] = {
-            "value": round(cb["tokens"] / cb["seconds"], 3) if args.workload == "splitfuse"
+            "value": round(cb["tokens"] / cb["seconds"], 3) if args.workload in ("splitfuse", "splitfuse_rope")
             else round(cb["kv_bytes"] / cb["seconds"] / 1e9, 4),
-            "unit": "tokens/s" if args.workload == "splitfuse" else "GB/s",
+            "unit": "tokens/s" if args.workload in ("splitfuse", "splitfuse_rope") else "GB/s",
             "cores": cb["cores"], "kind": "oracle",
             "sample": f"{cb['seqs']} decode sequences of this batch (gather + fp64 attention over host copies "
                       f"of their pages), {cb['seconds']:.1f} s on {cb['host_cpus']} host CPUs"}

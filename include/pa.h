@@ -72,6 +72,7 @@ typedef enum pa_alloc_status {
 #define PA_DEV_BAD_BLOCK 1   /* block id outside [0, num_blocks) (table entry or copy pair) */
 #define PA_DEV_BAD_SLOT 2    /* slot outside [0, num_blocks * 16)                            */
 #define PA_DEV_BAD_LENGTH 4  /* context length / query offsets inconsistent with the bounds  */
+#define PA_DEV_BAD_POSITION 8 /* position outside [0, max_position) (rotary cache write)      */
 
 /* Message for the last failing call on this thread ("" if none).  Valid until
  * the next call into the library from the same thread. */
@@ -99,6 +100,32 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
                                const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                pa_dtype dtype, int32_t* dev_status, void* stream);
+
+/* pa_rope_reshape_and_cache — the cache write with the rotary position
+ * embedding applied on the way ("第 15 章：推理引擎与部署" §15.3, RoPE fused into
+ * the kernels that read q and k, saving the round trip of the rotated tensors
+ * through memory; "DeepSpeed-FastGen 深度解析" §6, rotary embedding fused with
+ * the blocked KV layout).  For token t at position p = positions[t], with
+ * c = cos_table[p], s = sin_table[p] (head_dim/2 floats each), every head row
+ * x of q and of key is rotated pairwise (rotate-half form):
+ *   x'[i] = x[i] c[i] - x[i + d/2] s[i],  x'[i + d/2] = x[i + d/2] c[i] + x[i] s[i]
+ * in float32 (one rounded product and one fused multiply-add per element),
+ * rounded to dtype.  The rotated q goes to q_out (q_out == q allowed); the
+ * rotated key and the unchanged value are stored through slot_mapping[t] as
+ * in pa_reshape_and_cache (negative slot: q is still rotated, nothing is
+ * stored).  A position outside [0, max_position) skips the token entirely
+ * (q_out row untouched) and sets PA_DEV_BAD_POSITION.
+ *   q, q_out       device, [num_tokens][num_q_heads][head_dim] of dtype
+ *   key, value     device, [num_tokens][num_kv_heads][head_dim] of dtype
+ *   positions      device, int32 [num_tokens]
+ *   cos_table, sin_table  device, float32 [max_position][head_dim / 2]
+ */
+pa_status pa_rope_reshape_and_cache(void* q_out, const void* q, const void* key, const void* value,
+                                    void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                                    const int32_t* positions, const float* cos_table, const float* sin_table,
+                                    int32_t max_position, int32_t num_tokens, int32_t num_q_heads,
+                                    int32_t num_kv_heads, int32_t num_blocks, int32_t head_dim,
+                                    int32_t block_size, pa_dtype dtype, int32_t* dev_status, void* stream);
 
 /* ------------------------------------------------------------------ attention
  * Workspace bytes pa_forward needs for a batch within these bounds.  The

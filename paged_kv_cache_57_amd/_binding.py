@@ -19,7 +19,7 @@ PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS = 0, -1, -2, -3
 PA_ERR_REFCOUNT, PA_ERR_NOT_FOUND, PA_ERR_HIP = -4, -5, -6
 PA_F32, PA_BF16 = 0, 1
 PA_ALLOC_OK, PA_ALLOC_LATER, PA_ALLOC_NEVER = 0, 1, 2
-PA_DEV_BAD_BLOCK, PA_DEV_BAD_SLOT, PA_DEV_BAD_LENGTH = 1, 2, 4
+PA_DEV_BAD_BLOCK, PA_DEV_BAD_SLOT, PA_DEV_BAD_LENGTH, PA_DEV_BAD_POSITION = 1, 2, 4, 8
 BLOCK = 16
 
 _STATUS_NAMES = {PA_ERR_INVALID: "PA_ERR_INVALID", PA_ERR_UNSUPPORTED: "PA_ERR_UNSUPPORTED",
@@ -47,6 +47,8 @@ _SIGS = {
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_abi_version": (_i32, []),
     "pa_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "pa_rope_reshape_and_cache": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                         _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pa_forward_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                           _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
@@ -149,6 +151,28 @@ def pa_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, dev_status=
     _check(_lib.pa_reshape_and_cache(
         _dev(key, "key", k_cache.dtype), _dev(value, "value", k_cache.dtype), _dev(k_cache, "k_cache"),
         _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int64), T, nb, hkv, d, blk,
+        _dtype_code(k_cache), _dev(dev_status, "dev_status", torch.int32), _stream(k_cache, stream)))
+
+
+def pa_rope_reshape_and_cache(q_out, q, key, value, k_cache, v_cache, slot_mapping, positions, cos_table,
+                              sin_table, dev_status=None, stream=None):
+    import torch
+    nb, hkv, d, blk = _pool_dims(k_cache, v_cache)
+    T, hq, dq = q.shape
+    if dq != d or tuple(q_out.shape) != (T, hq, d):
+        raise PAError(PA_ERR_INVALID, "q/q_out must be [num_tokens, num_q_heads, head_dim]")
+    if tuple(key.shape) != (T, hkv, d) or tuple(value.shape) != (T, hkv, d):
+        raise PAError(PA_ERR_INVALID, "key/value must be [num_tokens, kv_heads, head_dim]")
+    if slot_mapping.shape != (T,) or positions.shape != (T,):
+        raise PAError(PA_ERR_INVALID, "slot_mapping and positions must be [num_tokens]")
+    if cos_table.dim() != 2 or cos_table.shape[1] != d // 2 or cos_table.shape != sin_table.shape:
+        raise PAError(PA_ERR_INVALID, "cos/sin tables must be [max_position, head_dim / 2]")
+    dt = k_cache.dtype
+    _check(_lib.pa_rope_reshape_and_cache(
+        _dev(q_out, "q_out", dt), _dev(q, "q", dt), _dev(key, "key", dt), _dev(value, "value", dt),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(slot_mapping, "slot_mapping", torch.int64),
+        _dev(positions, "positions", torch.int32), _dev(cos_table, "cos_table", torch.float32),
+        _dev(sin_table, "sin_table", torch.float32), cos_table.shape[0], T, hq, hkv, nb, d, blk,
         _dtype_code(k_cache), _dev(dev_status, "dev_status", torch.int32), _stream(k_cache, stream)))
 
 

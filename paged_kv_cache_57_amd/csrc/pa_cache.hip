@@ -44,6 +44,77 @@ __global__ __launch_bounds__(256) void reshape_and_cache_kernel(
   }
 }
 
+// Rotary embedding fused with the cache write: one workgroup per new token.
+// A unit is one 16-byte group c < head_dim/(2X) of one head together with
+// its partner group c + head_dim/(2X): the two hold the pairs (i, i + d/2)
+// that one rotation mixes.  Query units rotate q into q_out (which may be q:
+// every element is read and written by the same thread); key units rotate
+// the key and store both groups into the page and copy the same two value
+// groups.  Rotation in float32: x' = x c − y s, y' = y c + x s, each with one
+// rounded product and one fused multiply-add, then rounded to T.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void rope_cache_kernel(
+    T* q_out, const T* q, const T* __restrict__ key, const T* __restrict__ value, T* __restrict__ k_cache,
+    T* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, const int32_t* __restrict__ positions,
+    const float* __restrict__ cos_t, const float* __restrict__ sin_t, int32_t max_position, int32_t num_blocks,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t* dev_status) {
+  constexpr int X = Elem<T>::X;
+  constexpr int HC = D / X / 2;  // units per head
+  const int t = blockIdx.x;
+  const int pos = positions[t];
+  if (pos < 0 || pos >= max_position) {
+    if (threadIdx.x == 0) flag_status(dev_status, PA_DEV_BAD_POSITION);
+    return;
+  }
+  const int64_t slot = slot_mapping[t];
+  const bool bad_slot = slot >= (int64_t)num_blocks * kBlock;
+  if (bad_slot && threadIdx.x == 0) flag_status(dev_status, PA_DEV_BAD_SLOT);
+  const bool write = slot >= 0 && !bad_slot;
+  const int64_t b = write ? slot / kBlock : 0;
+  const int o = write ? (int)(slot % kBlock) : 0;
+  const int nq = num_q_heads * HC;
+  const int nu = nq + (write ? num_kv_heads * HC : 0);
+  const float* crow = cos_t + (int64_t)pos * (D / 2);
+  const float* srow = sin_t + (int64_t)pos * (D / 2);
+  for (int u = threadIdx.x; u < nu; u += blockDim.x) {
+    const bool isq = u < nq;
+    const int uu = isq ? u : u - nq;
+    const int h = uu / HC, c = uu % HC;
+    const int64_t src = ((int64_t)t * (isq ? num_q_heads : num_kv_heads) + h) * D + c * X;
+    const T* in = isq ? q : key;
+    union Grp {
+      u32x4 v;
+      T e[X];
+    } lo, hi;
+    lo.v = ld16(in + src);
+    hi.v = ld16(in + src + D / 2);
+#pragma unroll
+    for (int x = 0; x < X; ++x) {
+      const float cs = crow[c * X + x], sn = srow[c * X + x];
+      const float a = Elem<T>::to_f32(lo.e[x]), bb = Elem<T>::to_f32(hi.e[x]);
+      const float bs = bb * sn, as = a * sn;
+      lo.e[x] = Elem<T>::from_f32(__builtin_fmaf(a, cs, -bs));
+      hi.e[x] = Elem<T>::from_f32(__builtin_fmaf(bb, cs, as));
+    }
+    if (isq) {
+      st16(q_out + src, lo.v);
+      st16(q_out + src + D / 2, hi.v);
+    } else {
+      const int64_t page = (b * num_kv_heads + h) * (int64_t)(kBlock * D);
+      st16(k_cache + page + ((int64_t)c * kBlock + o) * X, lo.v);
+      st16(k_cache + page + ((int64_t)(c + HC) * kBlock + o) * X, hi.v);
+      Grp v0, v1;
+      v0.v = ld16(value + src);
+      v1.v = ld16(value + src + D / 2);
+#pragma unroll
+      for (int x = 0; x < X; ++x) {
+        v_cache[page + (int64_t)(c * X + x) * kBlock + o] = v0.e[x];
+        v_cache[page + (int64_t)(D / 2 + c * X + x) * kBlock + o] = v1.e[x];
+      }
+    }
+  }
+}
+
 // grid (num_pairs, slices): each workgroup copies one 4 KiB slice of the key
 // page and of the value page of one (src, dst) pair.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(uint8_t* __restrict__ k_cache,
@@ -120,6 +191,44 @@ __global__ __launch_bounds__(256) void read_pages_kernel(const u32x4* __restrict
 }  // namespace pa
 
 using namespace pa;
+
+extern "C" pa_status pa_rope_reshape_and_cache(void* q_out, const void* q, const void* key, const void* value,
+                                               void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                                               const int32_t* positions, const float* cos_table,
+                                               const float* sin_table, int32_t max_position, int32_t num_tokens,
+                                               int32_t num_q_heads, int32_t num_kv_heads, int32_t num_blocks,
+                                               int32_t head_dim, int32_t block_size, pa_dtype dtype,
+                                               int32_t* dev_status, void* stream) {
+  const char* fn = "pa_rope_reshape_and_cache";
+  pa_status st = check_pool_args(fn, num_blocks, num_kv_heads, head_dim, block_size, dtype);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0 || num_q_heads <= 0 || max_position <= 0)
+    return fail(PA_ERR_INVALID, "%s: num_tokens %d, num_q_heads %d, max_position %d", fn, num_tokens,
+                num_q_heads, max_position);
+  if (num_tokens == 0) return ok();
+  if (num_tokens > 2147483647 / 2 || (int64_t)num_q_heads * head_dim > (1 << 24))
+    return fail(PA_ERR_INVALID, "%s: too large", fn);
+  if (!q_out || !q || !key || !value || !k_cache || !v_cache || !slot_mapping || !positions || !cos_table ||
+      !sin_table)
+    return fail(PA_ERR_INVALID, "%s: NULL device pointer", fn);
+  hipStream_t s = (hipStream_t)stream;
+  (void)hipGetLastError();
+#define PA_ROPE_LAUNCH(T, D)                                                                                   \
+  hipLaunchKernelGGL((rope_cache_kernel<T, D>), dim3(num_tokens), dim3(256), 0, s, (T*)q_out, (const T*)q,     \
+                     (const T*)key, (const T*)value, (T*)k_cache, (T*)v_cache, slot_mapping, positions,        \
+                     cos_table, sin_table, max_position, num_blocks, num_q_heads, num_kv_heads, dev_status)
+  if (dtype == PA_BF16) {
+    if (head_dim == 64) PA_ROPE_LAUNCH(bf16_t, 64);
+    else PA_ROPE_LAUNCH(bf16_t, 128);
+  } else {
+    if (head_dim == 64) PA_ROPE_LAUNCH(float, 64);
+    else PA_ROPE_LAUNCH(float, 128);
+  }
+#undef PA_ROPE_LAUNCH
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
 
 extern "C" pa_status pa_read_pages(const void* pool, int64_t pool_bytes, const int32_t* page_ids,
                                    int32_t num_pages, uint32_t* sink, int32_t grid, int32_t* dev_status,

@@ -93,6 +93,20 @@ def copy_blocks(dtype, kp, vp, pairs):
             np.frombuffer(raw[kp.nbytes:], vp.dtype).reshape(vp.shape), st)
 
 
+def rope_reshape_and_cache(dtype, q, key, val, kp, vp, slots, positions, cos, sin):
+    """Emulated pa_rope_reshape_and_cache (q rotated in place); returns (q_out, k_pool, v_pool, status)."""
+    T, hq, d = q.shape
+    hkv, nb = key.shape[1], kp.shape[0]
+    hdr = np.array([dtype_code(dtype), T, hq, hkv, d, nb, cos.shape[0]], np.int32)
+    blob = [hdr, q, key, val, kp, vp, np.asarray(slots, np.int64), np.asarray(positions, np.int32),
+            np.ascontiguousarray(cos, np.float32), np.ascontiguousarray(sin, np.float32)]
+    raw, st = _run("rope", blob, q.nbytes + kp.nbytes + vp.nbytes)
+    qo = np.frombuffer(raw[:q.nbytes], q.dtype).reshape(q.shape)
+    k = np.frombuffer(raw[q.nbytes:q.nbytes + kp.nbytes], kp.dtype).reshape(kp.shape)
+    v = np.frombuffer(raw[q.nbytes + kp.nbytes:], vp.dtype).reshape(vp.shape)
+    return qo, k, v, st
+
+
 def read_pages(words, ids, grid):
     """Emulated pa_read_pages over int32 `words` (a whole number of 4 KiB pages)."""
     words = np.ascontiguousarray(words, np.int32)

@@ -141,6 +141,31 @@ int main(int argc, char** argv) {
     wr(kc, pool);
     wr(vc, pool);
     std::free(kc); std::free(vc); std::free(pairs);
+  } else if (!std::strcmp(argv[1], "rope")) {
+    const int dt = rd_i32(), T = rd_i32(), Hq = rd_i32(), Hkv = rd_i32(), D = rd_i32(), NB = rd_i32();
+    const int maxpos = rd_i32();
+    const size_t es = dt == PA_F32 ? 4 : 2;
+    void* q = rd_buf((size_t)T * Hq * D * es);
+    void* key = rd_buf((size_t)T * Hkv * D * es);
+    void* val = rd_buf((size_t)T * Hkv * D * es);
+    const size_t pool = (size_t)NB * Hkv * 16 * D * es;
+    void* kc = rd_buf(pool);
+    void* vc = rd_buf(pool);
+    auto* slots = (int64_t*)rd_buf((size_t)T * 8);
+    auto* pos = (int32_t*)rd_buf((size_t)T * 4);
+    auto* cs = (float*)rd_buf((size_t)maxpos * (D / 2) * 4);
+    auto* sn = (float*)rd_buf((size_t)maxpos * (D / 2) * 4);
+    pa_status st = pa_rope_reshape_and_cache(q, q, key, val, kc, vc, slots, pos, cs, sn, maxpos, T, Hq, Hkv, NB, D,
+                                             16, (pa_dtype)dt, &status, nullptr);
+    if (st != PA_OK) {
+      std::fprintf(stderr, "pa_rope_reshape_and_cache: %d %s\n", st, pa_last_error());
+      return 3;
+    }
+    wr(q, (size_t)T * Hq * D * es);
+    wr(kc, pool);
+    wr(vc, pool);
+    std::free(q); std::free(key); std::free(val); std::free(kc); std::free(vc); std::free(slots);
+    std::free(pos); std::free(cs); std::free(sn);
   } else if (!std::strcmp(argv[1], "read")) {
     const int npool = rd_i32(), n = rd_i32(), grid = rd_i32();
     void* pool = rd_buf((size_t)npool * 4096);

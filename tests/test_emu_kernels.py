@@ -174,3 +174,42 @@ def test_read_pages_probe_emulated(emu):
     got, st = emu.read_pages(words, ids, grid)
     assert st == 1  # PA_DEV_BAD_BLOCK for the id outside the pool
     assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])
+def test_rope_cache_write_emulated(emu, dtype, d):
+    from tests import _rope
+    rng = np.random.default_rng(7)
+    T, hq, hkv, nb, maxpos = 37, 6, 3, 8, 300
+    kp, vp = empty_pools(rng, dtype, nb, hkv, d)
+    def draw(shape):
+        return raw(rng.standard_normal(shape).astype(np.float32), dtype)
+    q, key, val = draw((T, hq, d)), draw((T, hkv, d)), draw((T, hkv, d))
+    slots = rng.permutation(nb * 16)[:T].astype(np.int64)
+    slots[3] = -1                                    # padding token: q rotated, nothing stored
+    pos = rng.integers(0, maxpos, size=T).astype(np.int32)
+    pos[0] = 0
+    cos, sin = W.rope_tables(maxpos, d)
+    qo, ko, vo, st = emu.rope_reshape_and_cache(dtype, q, key, val, kp, vp, slots, pos, cos, sin)
+    assert st == 0
+    same = _rope.check(dtype, qo, ko, vo, q, key, val, kp, vp, slots, pos, cos, sin)
+    # bfloat16 keeps 8 bits: the float32 evaluation almost never changes its rounding
+    assert same > 0.99 or dtype == "f32"
+
+
+def test_rope_bad_position_skips_the_token_emulated(emu):
+    rng = np.random.default_rng(8)
+    T, hq, hkv, d, nb, maxpos = 4, 2, 2, 64, 4, 10
+    kp, vp = empty_pools(rng, "bf16", nb, hkv, d)
+    def draw(shape):
+        return raw(rng.standard_normal(shape).astype(np.float32), "bf16")
+    q, key, val = draw((T, hq, d)), draw((T, hkv, d)), draw((T, hkv, d))
+    slots = np.arange(T, dtype=np.int64)
+    pos = np.array([1, 10, 2, -1], np.int32)          # tokens 1 and 3 out of range
+    cos, sin = W.rope_tables(maxpos, d)
+    qo, ko, vo, st = emu.rope_reshape_and_cache("bf16", q, key, val, kp, vp, slots, pos, cos, sin)
+    assert st == 8
+    assert np.array_equal(qo[[1, 3]], q[[1, 3]])
+    from tests import _rope
+    keep = [0, 2]
+    _rope.check("bf16", qo[keep], ko, vo, q[keep], key[keep], val[keep], kp, vp, slots[keep], pos[keep], cos, sin)

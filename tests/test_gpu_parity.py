@@ -389,6 +389,80 @@ def test_composer_driven_passes(pa):
     alloc.close()
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f32", 64)])
+def test_rope_cache_write(pa, dtype, d):
+    """Rotary cache write: rotated q and key against the exact rotation (within the float32
+    evaluation's rounding), values and untouched pool bytes bit-exact."""
+    from tests import _rope
+    from tests._pools import empty_pools, raw
+    rng = np.random.default_rng(21)
+    T, hq, hkv, nb, maxpos = 300, 32, 8, 64, 8192
+    kp, vp = empty_pools(rng, dtype, nb, hkv, d)
+    def draw(shape):
+        return raw(rng.standard_normal(shape).astype(np.float32), dtype)
+    q, key, val = draw((T, hq, d)), draw((T, hkv, d)), draw((T, hkv, d))
+    slots = rng.permutation(nb * 16)[:T].astype(np.int64)
+    slots[7] = -1
+    pos = rng.integers(0, maxpos, size=T).astype(np.int32)
+    cos, sin = W.rope_tables(maxpos, d)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    qd = torch.from_numpy(q.view(np.int16) if dtype == "bf16" else q).to(DEV).view(tdt)
+    kd = torch.from_numpy(key.view(np.int16) if dtype == "bf16" else key).to(DEV).view(tdt)
+    vd = torch.from_numpy(val.view(np.int16) if dtype == "bf16" else val).to(DEV).view(tdt)
+    kcd = torch.from_numpy(kp.view(np.int16) if dtype == "bf16" else kp).to(DEV).view(tdt)
+    vcd = torch.from_numpy(vp.view(np.int16) if dtype == "bf16" else vp).to(DEV).view(tdt)
+    qo = torch.empty_like(qd)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    say(f"[case] rope cache write {dtype} d{d}: T={T} hq={hq} hkv={hkv}")
+    pa.pa_rope_reshape_and_cache(qo, qd, kd, vd, kcd, vcd, torch.from_numpy(slots).to(DEV),
+                                 torch.from_numpy(pos).to(DEV), torch.from_numpy(cos).to(DEV),
+                                 torch.from_numpy(sin).to(DEV), status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    same = _rope.check(dtype, host_raw(qo), host_raw(kcd), host_raw(vcd), q, key, val, kp, vp, slots, pos, cos, sin)
+    assert same > 0.99 or dtype == "f32"
+    # in place on q gives the same bytes
+    pa.pa_rope_reshape_and_cache(qd, qd, kd, vd, kcd, vcd, torch.from_numpy(slots).to(DEV),
+                                 torch.from_numpy(pos).to(DEV), torch.from_numpy(cos).to(DEV),
+                                 torch.from_numpy(sin).to(DEV), status)
+    torch.cuda.synchronize()
+    assert np.array_equal(host_raw(qd), host_raw(qo))
+
+
+def test_rope_then_attention(pa):
+    """A mixed batch whose new tokens go through the rotary cache write (q rotated, keys rotated
+    into their pages) and then through pa_forward; the oracle rotates q and the new keys itself,
+    rounds them to bfloat16 as the pool stores them, and computes attention in float64."""
+    from oracle import attention as oattn
+    from tests import _rope
+    from tests._gpu import TOL
+    w = W.random_ragged(31, "bf16", 16, 4, 128, [1, 200, 1, 37], [900, 1500, 3000, 37], with_slots=True)
+    q, kc, vc, nk, nv = W.make_values(w, DEV)
+    maxpos = 4096
+    cos, sin = W.rope_tables(maxpos, 128)
+    ql = np.diff(w.query_start_loc)
+    pos = np.concatenate([np.arange(L - n, L) for n, L in zip(ql, w.context_lens)]).astype(np.int32)
+    qh, kh, vh, nkh, nvh = (host_raw(t) for t in (q, kc, vc, nk, nv))
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    qr = torch.empty_like(q)
+    say(f"[case] rope + attention: q_lens {list(ql)}, contexts {list(w.context_lens)}")
+    pa.pa_rope_reshape_and_cache(qr, q, nk, nv, kc, vc, torch.from_numpy(w.new_slots).to(DEV),
+                                 torch.from_numpy(pos).to(DEV), torch.from_numpy(cos).to(DEV),
+                                 torch.from_numpy(sin).to(DEV), status)
+    run = Run(w)
+    out = run.forward(qr, kc, vc)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0 and int(run.status.item()) == 0
+    q_ref, k_ref, v_ref, _, _ = _rope.expected("bf16", qh, nkh, nvh, kh, vh, w.new_slots, pos, cos, sin)
+    ref = oattn.paged_attention(q_ref, k_ref, v_ref, w.block_tables, w.context_lens, w.query_start_loc,
+                                w.scale, "bf16")
+    got = to_f64(out)
+    a, r = TOL["bf16"]
+    ratio = float((np.abs(got - ref) / (a + r * np.abs(ref))).max())
+    say(f"  worst err/bound {ratio:.3f}")
+    assert np.isfinite(got).all() and ratio <= 1.0
+
+
 def read_probe_case():
     """Pages, a page list with one id outside the pool, and the sink the documented
     thread assignment gives: wavefront w XORs piece l, l+64, l+128, l+192 of its

@@ -274,3 +274,12 @@ def make_values(w: Workload, device, fill_pool: bool = True):
         new_k = fill_normal(torch.empty((T, w.num_kv_heads, w.head_dim), dtype=td, device=device), gen)
         new_v = fill_normal(torch.empty((T, w.num_kv_heads, w.head_dim), dtype=td, device=device), gen)
     return q, k_cache, v_cache, new_k, new_v
+
+
+def rope_tables(max_position: int, head_dim: int, base: float = 10000.0):
+    """cos / sin tables [max_position][head_dim/2] in float32 for rotary embeddings:
+    angle(p, i) = p · base^(-2i/head_dim), evaluated in float64 and rounded once."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    inv = base ** (-2.0 * i / head_dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
