@@ -236,33 +236,40 @@ def copy_calibration(torch, dev, args, nbytes=4 << 30):
 
 
 def read_calibration(torch, pa, dev, args, nbytes=4 << 30, grid=2048):
-    """Every 4 KiB page of a 4 GiB pool read once per step in a seeded random order,
-    16-byte loads, two pages per wavefront in flight: the rate the decode workers'
-    page reads could reach if they did no arithmetic."""
+    """4 KiB pages of a 4 GiB pool read in a seeded random order, 16-byte loads, two
+    pages per wavefront in flight: the rate the decode workers' page reads could
+    reach if they did no arithmetic.  By default a step reads every page once;
+    with --read-mib M a step reads the next M MiB of the order (successive steps
+    take disjoint slices, so none finds its pages in the 256 MB Infinity Cache),
+    the rate a pass of that size can reach."""
     pool = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(7)
     npages = nbytes // 4096
     order = torch.from_numpy(np.random.default_rng(5).permutation(npages).astype(np.int32)).to(dev)
+    per = npages if not args.read_mib else min(npages, args.read_mib * 256)
+    nslices = npages // per
+    slices = [order[i * per:(i + 1) * per] for i in range(nslices)]
+    g = grid if per == npages else min(grid, max(1, (per + 7) // 8))
     sink = torch.empty(grid * 256, dtype=torch.int32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
-    for _ in range(args.warmup):
-        pa.pa_read_pages(pool, order, sink, grid, status)
+    for i in range(args.warmup):
+        pa.pa_read_pages(pool, slices[i % nslices], sink, g, status)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
-    for _ in range(args.steps):
-        pa.pa_read_pages(pool, order, sink, grid, status)
+    for i in range(args.steps):
+        pa.pa_read_pages(pool, slices[(args.warmup + i) % nslices], sink, g, status)
     t1.record()
     torch.cuda.synchronize()
     if int(status.item()) != 0:
         raise RuntimeError(f"pa_read_pages flagged status {int(status.item())}")
     ms = t0.elapsed_time(t1) / args.steps
-    gbps = nbytes / (ms * 1e-3) / 1e9
+    gbps = per * 4096 / (ms * 1e-3) / 1e9
+    name = "read_pages_4GiB" if per == npages else f"read_pages_{per * 4096 >> 20}MiB_of_4GiB"
     print(json.dumps({"metric": "random 4 KiB page reads GB/s", "value": round(gbps, 1), "unit": "GB/s",
                       "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
                       "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
-                      "data": "synthetic", "config": {"workload": "read_pages_4GiB", "pages": npages,
-                                                      "grid": grid},
+                      "data": "synthetic", "config": {"workload": name, "pages": per, "grid": g},
                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}), flush=True)
 
 
@@ -383,6 +390,7 @@ def main():
     ap.add_argument("--rotate", type=int, default=0, help="pool copies cycled per step (0: enough to exceed the 256 MB MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--read-mib", type=int, default=0, help="read workload: MiB per step (0: the whole 4 GiB pool)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus})",
