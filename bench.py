@@ -15,6 +15,8 @@ inputs resident in device memory before timing starts:
 * sampling: the parallel-sampling workflow (16 prompts x 4 branches sharing
   prompt pages, copy-on-write, 64 decode rows per step); value = decode
   tokens per second over the timed steps, allocator and uploads included.
+  --shared-prefix attends with pa_forward_shared (a prompt's pages are read
+  once for its four branches).
 * splitfuse_rope: the same pass with the rotary embedding fused into the cache
   write (pa_rope_reshape_and_cache rotates q and the new keys at their
   positions; the forward reads the rotated q).
@@ -309,7 +311,14 @@ def sampling_workflow(torch, pa, W, dev, args):
     max_ctx = int(lens.max()) + total
     cap_max = (max_ctx + 15) // 16
     qsl = torch.arange(n + 1, dtype=torch.int32, device=dev)
-    nbytes = pa.pa_forward_workspace_bytes(n, n, 1, H, H, d, max_ctx, pa.PA_BF16)
+    cascade = args.shared_prefix
+    if cascade:
+        # each prompt's branches (consecutive sequences) share its full pages
+        groups = torch.tensor([[p * B, B, 16 * (int(L) // 16)] for p, L in enumerate(spec.prompt_lens)],
+                              dtype=torch.int32, device=dev)
+        nbytes = pa.pa_forward_shared_workspace_bytes(n, P, n, 1, H, H, d, max_ctx, pa.PA_BF16)
+    else:
+        nbytes = pa.pa_forward_workspace_bytes(n, n, 1, H, H, d, max_ctx, pa.PA_BF16)
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((n, H, d), dtype=torch.bfloat16, device=dev)
     # pinned upload buffers, one set per step, so no copy waits for the device
@@ -339,8 +348,12 @@ def sampling_workflow(torch, pa, W, dev, args):
         tables = up_tab[i, :n * cap].to(dev, non_blocking=True).view(n, cap)
         if record:
             ev.record(fwd_ev[2 * i], stream)
-        pa.pa_forward(out, qs[i], kc, vc, tables, up_lens[i].to(dev, non_blocking=True), qsl, 1, int(lens.max()),
-                      1.0 / np.sqrt(d), ws, status)
+        if cascade:
+            pa.pa_forward_shared(out, qs[i], kc, vc, tables, up_lens[i].to(dev, non_blocking=True), qsl, groups, 1,
+                                 int(lens.max()), 1.0 / np.sqrt(d), ws, status)
+        else:
+            pa.pa_forward(out, qs[i], kc, vc, tables, up_lens[i].to(dev, non_blocking=True), qsl, 1,
+                          int(lens.max()), 1.0 / np.sqrt(d), ws, status)
         if record:
             ev.record(fwd_ev[2 * i + 1], stream)
             logical.append(int(lens.sum()))
@@ -370,7 +383,8 @@ def sampling_workflow(torch, pa, W, dev, args):
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "parallel_sampling_16x4", "prompts": P, "branches": B, "q_heads": H, "kv_heads": H,
-                   "head_dim": d, "block_size": 16, "pool_blocks": NB, "decode_steps": total},
+                   "head_dim": d, "block_size": 16, "pool_blocks": NB, "decode_steps": total,
+                   "forward": "pa_forward_shared (prompt pages read once per prompt)" if cascade else "pa_forward"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "pa_forward",
                      "kernel_ms": round(1e3 * fwd_s / args.steps, 4), "algorithmic_bytes": "unique KV pages per step"},
@@ -391,6 +405,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--read-mib", type=int, default=0, help="read workload: MiB per step (0: the whole 4 GiB pool)")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="sampling workload: attend with pa_forward_shared, the branches of a prompt as one group")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus})",

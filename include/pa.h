@@ -73,6 +73,7 @@ typedef enum pa_alloc_status {
 #define PA_DEV_BAD_SLOT 2    /* slot outside [0, num_blocks * 16)                            */
 #define PA_DEV_BAD_LENGTH 4  /* context length / query offsets inconsistent with the bounds  */
 #define PA_DEV_BAD_POSITION 8 /* position outside [0, max_position) (rotary cache write)      */
+#define PA_DEV_BAD_GROUP 16   /* a shared-prefix group failed its checks and was ignored        */
 
 /* Message for the last failing call on this thread ("" if none).  Valid until
  * the next call into the library from the same thread. */
@@ -173,6 +174,42 @@ pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* 
                      int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
                      pa_dtype dtype, void* workspace, size_t workspace_bytes,
                      int32_t* dev_status, void* stream);
+
+/* pa_forward_shared — pa_forward for batches in which groups of decode
+ * sequences share the pages of a common prefix (the samples of one prompt:
+ * "大模型部署.md" §2.1 item 4 and "【自用】AI infra相关" part 二.2(1), sharing
+ * between the samples of one prompt; "第 15 章" §15.6).  The result is the
+ * same attention as pa_forward; what changes is the work: a shared page is
+ * read once for all members of its group.  Each member's attention is split
+ * at the shared length S into the shared keys, computed for all members
+ * together as one MFMA tile (members x query heads of a KV head as rows),
+ * and its own keys S .. L-1; the two partial softmax states are combined by
+ * the log-sum-exp merge of split contexts ("第 15 章" §15.1 rescaling),
+ * which is exact.
+ *   groups  device, int32 [num_groups][3]: first sequence, number of members,
+ *           shared keys S.  Members are the consecutive sequences first ..
+ *           first + members - 1; groups are listed in increasing order and do
+ *           not overlap.  A group is used only if: 2 <= members,
+ *           members x (num_q_heads / num_kv_heads) <= 16, S > 0 is a multiple
+ *           of 16 and at most max_context_len, every member is a single-row
+ *           decode with context length >= S, and the first S/16 block-table
+ *           entries of every member equal those of the first member.  Any
+ *           other group is ignored (its members are attended as plain
+ *           sequences, still correctly) and PA_DEV_BAD_GROUP is set.
+ * Other arguments as pa_forward; workspace >= pa_forward_shared_workspace_bytes.
+ * bfloat16 only, at most 8 query heads per KV head (PA_ERR_UNSUPPORTED). */
+pa_status pa_forward_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, const int32_t* query_start_loc,
+                            const int32_t* groups, int32_t num_groups, int32_t num_seqs,
+                            int32_t total_q_tokens, int32_t max_q_len, int32_t max_context_len,
+                            int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int32_t num_blocks, float scale, pa_dtype dtype,
+                            void* workspace, size_t workspace_bytes, int32_t* dev_status, void* stream);
+/* Workspace bytes of pa_forward_shared for these bounds and num_groups groups. */
+size_t pa_forward_shared_workspace_bytes(int32_t num_seqs, int32_t num_groups, int32_t total_q_tokens,
+                                         int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                         int32_t head_dim, int32_t max_context_len, pa_dtype dtype);
 
 /* Measurement hook, for timing only (changes nothing that is computed).
  * pa_forward runs five stages on its stream: 0 planner, 1 VALU worker (decode

@@ -19,7 +19,7 @@ PA_OK, PA_ERR_INVALID, PA_ERR_UNSUPPORTED, PA_ERR_NO_BLOCKS = 0, -1, -2, -3
 PA_ERR_REFCOUNT, PA_ERR_NOT_FOUND, PA_ERR_HIP = -4, -5, -6
 PA_F32, PA_BF16 = 0, 1
 PA_ALLOC_OK, PA_ALLOC_LATER, PA_ALLOC_NEVER = 0, 1, 2
-PA_DEV_BAD_BLOCK, PA_DEV_BAD_SLOT, PA_DEV_BAD_LENGTH, PA_DEV_BAD_POSITION = 1, 2, 4, 8
+PA_DEV_BAD_BLOCK, PA_DEV_BAD_SLOT, PA_DEV_BAD_LENGTH, PA_DEV_BAD_POSITION, PA_DEV_BAD_GROUP = 1, 2, 4, 8, 16
 BLOCK = 16
 
 _STATUS_NAMES = {PA_ERR_INVALID: "PA_ERR_INVALID", PA_ERR_UNSUPPORTED: "PA_ERR_UNSUPPORTED",
@@ -52,6 +52,9 @@ _SIGS = {
     "pa_forward_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_forward": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                           _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
+    "pa_forward_shared": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                 _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
+    "pa_forward_shared_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pa_set_stage_events": (_i32, [_vp, _i32]),
     "pa_read_pages": (_i32, [_vp, _i64, _vp, _i32, _vp, _i32, _vp, _vp]),
@@ -199,6 +202,36 @@ def pa_forward(out, q, k_cache, v_cache, block_tables, context_lens, query_start
         S, T, int(max_q_len), int(max_context_len), hq, hkv, d, blk, nb, float(scale), _dtype_code(q),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _dev(dev_status, "dev_status", torch.int32), _stream(q, stream)))
+
+
+def pa_forward_shared(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, groups, max_q_len,
+                      max_context_len, scale, workspace, dev_status=None, stream=None):
+    """pa_forward with shared-prefix groups: groups is a device int32 [G, 3] tensor of
+    (first sequence, members, shared keys)."""
+    import torch
+    nb, hkv, d, blk = _pool_dims(k_cache, v_cache)
+    T, hq, dq = q.shape
+    if dq != d or tuple(out.shape) != (T, hq, d):
+        raise PAError(PA_ERR_INVALID, "q/out must be [total_q_tokens, num_q_heads, head_dim]")
+    S = context_lens.shape[0]
+    if tuple(query_start_loc.shape) != (S + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise PAError(PA_ERR_INVALID, "context_lens [S], query_start_loc [S+1], block_tables [S, M]")
+    if groups.dim() != 2 or groups.shape[1] != 3:
+        raise PAError(PA_ERR_INVALID, "groups must be [num_groups, 3]")
+    _check(_lib.pa_forward_shared(
+        _dev(out, "out", q.dtype), _dev(q, "q", k_cache.dtype), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), _dev(query_start_loc, "query_start_loc", torch.int32),
+        _dev(groups, "groups", torch.int32) if groups.shape[0] else None, groups.shape[0], S, T, int(max_q_len),
+        int(max_context_len), hq, hkv, d, blk, nb, float(scale), _dtype_code(q),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _dev(dev_status, "dev_status", torch.int32), _stream(q, stream)))
+
+
+def pa_forward_shared_workspace_bytes(num_seqs, num_groups, total_q_tokens, max_q_len, num_q_heads, num_kv_heads,
+                                      head_dim, max_context_len, dtype: int) -> int:
+    return int(_lib.pa_forward_shared_workspace_bytes(num_seqs, num_groups, total_q_tokens, max_q_len, num_q_heads,
+                                                      num_kv_heads, head_dim, max_context_len, dtype))
 
 
 def pa_copy_blocks(k_cache, v_cache, block_pairs, dev_status=None, stream=None):

@@ -111,14 +111,26 @@ struct AttnParams {
   int32_t* pre_m;  // ... of MFMA items
   int32_t* pre_t;  // ... of TILE items
   int32_t* pre_g;  // ... of (query token, query head) rows whose context was split
-  i32x4* seqinfo;  // per sequence: first query row, q_len, context length, 1 if valid
+  i32x4* seqinfo;  // per entry: first query row, q_len, context length, flags (kEnt*)
   float* partials;  // [T][Hq][maxparts][D + 4]: O (unnormalised), m, l, 2 pad
   int32_t maxparts;
   int32_t* dev_status;
+  // Shared prefixes: entries [num_seqs, num_ent) stand for the groups of
+  // `groups` ([num_groups][3]: first sequence, members, shared keys).
+  int32_t num_ent;
+  const int32_t* groups;
+  int32_t num_groups;
+  i32x4* seqx;  // per entry: key offset, shared partitions before the own ones, member flag, table row
 };
 
+// Entry flags.  A group entry's rows are its members' single decode rows,
+// all at the last position of the shared keys (every row sees all of them);
+// its partitions fill the members' partial slots 0 .. nps-1.  A member
+// skips the shared keys and numbers its own partitions from nps on.
+constexpr int kEntValid = 1, kEntGroup = 2, kEntMember = 4;
+
 struct SeqInfo {
-  int a, q_len, L;
+  int a, q_len, L, flags;
   bool ok;
 };
 
@@ -131,7 +143,23 @@ __device__ inline SeqInfo read_seq(const AttnParams& p, int s) {
   si.L = p.context_lens[s];
   si.ok = si.a >= 0 && b >= si.a && b <= p.T && si.q_len <= p.max_q_len && si.L >= 0 &&
           si.L <= p.max_ctx && si.q_len <= si.L && (si.L + kBlock - 1) / kBlock <= p.mbps;
+  si.flags = si.ok ? kEntValid : 0;
   return si;
+}
+
+// Key offset, shared partitions and table row of an entry (all 0 / s without groups).
+struct EntX {
+  int koff, nps, trow;
+};
+__device__ inline EntX ent_x(const AttnParams& p, int s, int flags) {
+  EntX x{0, 0, s};
+  if (flags & (kEntGroup | kEntMember)) {
+    const i32x4 v = p.seqx[s];
+    x.koff = __builtin_amdgcn_readfirstlane(v[0]);
+    x.nps = __builtin_amdgcn_readfirstlane(v[1]);
+    if (flags & kEntGroup) x.trow = __builtin_amdgcn_readfirstlane(v[3]);
+  }
+  return x;
 }
 
 // The planner's record of sequence s, as wave-uniform values (one 16-byte load).
@@ -141,7 +169,8 @@ __device__ inline SeqInfo seq_record(const AttnParams& p, int s) {
   si.a = __builtin_amdgcn_readfirstlane(v[0]);
   si.q_len = __builtin_amdgcn_readfirstlane(v[1]);
   si.L = __builtin_amdgcn_readfirstlane(v[2]);
-  si.ok = __builtin_amdgcn_readfirstlane(v[3]) != 0;
+  si.flags = __builtin_amdgcn_readfirstlane(v[3]);
+  si.ok = (si.flags & kEntValid) != 0;
   return si;
 }
 
@@ -218,6 +247,54 @@ __device__ inline i32x4 wave_incl_scan(i32x4 v, int lane) {
   return v;
 }
 
+// With shared-prefix groups it first checks every group (one at a time, all
+// threads comparing the members' table entries with the first member's) and
+// records the group entries and the members' offsets; a group that fails a
+// check is dropped (its members are attended as plain sequences) and
+// PA_DEV_BAD_GROUP is set.
+__device__ inline void plan_groups(const AttnParams& p, int tid) {
+  __shared__ int g_bad, g_prev_end;
+  for (int s = tid; s < p.num_seqs; s += 1024) p.seqx[s] = i32x4{0, 0, 0, 0};
+  if (tid == 0) g_prev_end = 0;
+  __syncthreads();
+  for (int g = 0; g < p.num_groups; ++g) {
+    const int first = p.groups[3 * g], n = p.groups[3 * g + 1], S = p.groups[3 * g + 2];
+    // groups in increasing order, no overlap, 2..16/G members inside the batch, whole shared pages
+    const bool shape = first >= g_prev_end && n >= 2 && n <= kTileRows && n * p.G <= kTileRows &&
+                       first <= p.num_seqs - n && S > 0 && S % kBlock == 0 && S <= p.max_ctx;
+    __syncthreads();  // every thread has read g_prev_end
+    if (tid == 0) g_bad = shape ? 0 : 1;
+    __syncthreads();
+    if (shape) {
+      if (tid < n) {
+        const SeqInfo si = read_seq(p, first + tid);
+        if (!si.ok || si.q_len != 1 || si.L < S) atomicOr(&g_bad, 1);
+      }
+      const int nb = S / kBlock;  // <= mbps, as S <= max_ctx
+      const int64_t cmp = (int64_t)(n - 1) * nb;
+      for (int64_t i = tid; i < cmp; i += 1024) {
+        const int m = 1 + (int)(i / nb), j = (int)(i % nb);
+        if (p.block_tables[(int64_t)(first + m) * p.mbps + j] != p.block_tables[(int64_t)first * p.mbps + j])
+          atomicOr(&g_bad, 1);
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      const bool good = shape && g_bad == 0;
+      const int nps = good ? seq_work(false, p.G, p.Hq, p.Hkv, n, S).nparts : 0;
+      if (good) {
+        for (int m = 0; m < n; ++m) p.seqx[first + m] = i32x4{S, nps, 1, 0};
+        g_prev_end = first + n;
+      } else {
+        flag_status(p.dev_status, PA_DEV_BAD_GROUP);
+      }
+      p.seqinfo[p.num_seqs + g] = i32x4{good ? p.qsl[first] : 0, n, S, good ? (kEntValid | kEntGroup) : 0};
+      p.seqx[p.num_seqs + g] = i32x4{0, 0, 0, good ? first : 0};
+    }
+    __syncthreads();
+  }
+}
+
 __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
   __shared__ i32x4 wsum[16];
   __shared__ i32x4 carry;
@@ -226,22 +303,38 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
     carry = i32x4{0, 0, 0, 0};
     if (p.qsl[0] != 0 || p.qsl[p.num_seqs] != p.T) flag_status(p.dev_status, PA_DEV_BAD_LENGTH);
   }
+  if (p.num_groups > 0) plan_groups(p, tid);
   __syncthreads();
-  for (int base = 0; base < p.num_seqs; base += 1024) {
+  for (int base = 0; base < p.num_ent; base += 1024) {
     const int s = base + tid;
     i32x4 cnt = {0, 0, 0, 0};  // VALU, MFMA, TILE items, rows to merge
     if (s < p.num_seqs) {
-      const SeqInfo si = read_seq(p, s);
-      p.seqinfo[s] = i32x4{si.a, si.q_len, si.L, si.ok ? 1 : 0};
+      SeqInfo si = read_seq(p, s);
+      int koff = 0, nps = 0;
+      if (p.num_groups > 0) {
+        const i32x4 x = p.seqx[s];
+        if (x[2]) {
+          koff = x[0];
+          nps = x[1];
+          si.flags |= kEntMember;
+        }
+      }
+      p.seqinfo[s] = i32x4{si.a, si.q_len, si.L, si.flags};
       if (!si.ok) {
         flag_status(p.dev_status, PA_DEV_BAD_LENGTH);
       } else {
-        const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L);
+        const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L - koff);
         const int items = w.groups * w.nparts;
         if (w.cls == CLS_VALU) cnt[0] = items;
         else if (w.cls == CLS_MFMA) cnt[1] = items;
         else if (w.cls == CLS_TILE) cnt[2] = items;
-        if (w.nparts > 1) cnt[3] = si.q_len * p.Hq;
+        if (nps > 0 || w.nparts > 1) cnt[3] = si.q_len * p.Hq;
+      }
+    } else if (s < p.num_ent) {
+      const i32x4 r = p.seqinfo[s];  // a group entry, recorded by plan_groups
+      if (r[3] & kEntGroup) {
+        const SeqWork w = seq_work(false, p.G, p.Hq, p.Hkv, r[1], r[2]);
+        cnt[1] = w.groups * w.nparts;
       }
     }
     const i32x4 inc = wave_incl_scan(cnt, lane);
@@ -249,7 +342,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
     __syncthreads();
     i32x4 before = carry;
     for (int k = 0; k < wv; ++k) before += wsum[k];
-    if (s < p.num_seqs) {
+    if (s < p.num_ent) {
       const i32x4 ex = before + inc - cnt;
       p.pre_v[s] = ex[0];
       p.pre_m[s] = ex[1];
@@ -265,10 +358,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
     __syncthreads();
   }
   if (tid == 0) {
-    p.pre_v[p.num_seqs] = carry[0];
-    p.pre_m[p.num_seqs] = carry[1];
-    p.pre_t[p.num_seqs] = carry[2];
-    p.pre_g[p.num_seqs] = carry[3];
+    p.pre_v[p.num_ent] = carry[0];
+    p.pre_m[p.num_ent] = carry[1];
+    p.pre_t[p.num_ent] = carry[2];
+    p.pre_g[p.num_ent] = carry[3];
     p.ctrl[2] = carry[0];
     p.ctrl[3] = carry[1];
     p.ctrl[4] = carry[2];
@@ -331,17 +424,18 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
   const int wave_id = wave_uniform((int)(blockIdx.x * 4 + wv));
   const int nwaves = (int)gridDim.x * 4;
   const int total = wave_uniform(p.ctrl[2]);
-  const SkipTable tab = stage_skip(skip, p.pre_v, p.num_seqs);
+  const SkipTable tab = stage_skip(skip, p.pre_v, p.num_ent);
   const T* __restrict__ kc = (const T*)p.k_cache;
   const T* __restrict__ vc = (const T*)p.v_cache;
   const int64_t page_elems = (int64_t)kBlock * D;
 
   for (int item = wave_id; item < total; item += nwaves) {
-    const SeqHit hit = find_seq(skip, tab, p.pre_v, p.num_seqs, item);
+    const SeqHit hit = find_seq(skip, tab, p.pre_v, p.num_ent, item);
     const int s = hit.s;
     const int local = item - hit.first;
     const SeqInfo si = seq_record(p, s);
-    const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L);
+    const EntX ex = ent_x(p, s, si.flags);  // a member skips the shared keys
+    const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L - ex.koff);
     const int pidx = local % w.nparts;
     const int rh = local / w.nparts;
     const int h = rh % p.Hq;
@@ -349,7 +443,7 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
     const int t = si.a + i;
     const int pos = si.L - si.q_len + i;
     const int g = h / p.G;
-    const int kv_lo = pidx * w.part;
+    const int kv_lo = ex.koff + pidx * w.part;
     const int kv_hi = min(kv_lo + w.part, pos + 1);
 
     float m = kNegInf, lsum = 0.f;
@@ -464,12 +558,12 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
       if constexpr (LPR == 4) acc[k] += shfl_xor_f(acc[k], 2);
     }
     // every lane of a column group holds the column's value: all of them store it
-    if (w.nparts == 1) {
+    if (ex.nps == 0 && w.nparts == 1) {
       T* orow = (T*)p.out + ((int64_t)t * p.Hq + h) * D;
 #pragma unroll
       for (int k = 0; k < NIV; ++k) orow[RPI * k + lane / LPR] = Elem<T>::from_f32(acc[k] / l);
     } else {
-      float* slot = p.partials + (((int64_t)t * p.Hq + h) * p.maxparts + pidx) * slot_floats(D);
+      float* slot = p.partials + (((int64_t)t * p.Hq + h) * p.maxparts + ex.nps + pidx) * slot_floats(D);
 #pragma unroll
       for (int k = 0; k < NIV; ++k) slot[RPI * k + lane / LPR] = acc[k];
       slot[D] = m;
@@ -512,14 +606,16 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
   const float csc = fmaxf(fabsf(p.scale_log2), 1e-30f);  // scale 0 gives equal weights, as it should
   const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
   __shared__ int skip[kSkip];
-  const SkipTable tab = stage_skip(skip, p.pre_m, p.num_seqs);
+  const SkipTable tab = stage_skip(skip, p.pre_m, p.num_ent);
 
   for (int item = wave_id; item < total; item += nwaves) {
-    const SeqHit hit = find_seq(skip, tab, p.pre_m, p.num_seqs, item);
+    const SeqHit hit = find_seq(skip, tab, p.pre_m, p.num_ent, item);
     const int s = hit.s;
     const int local = item - hit.first;
     const SeqInfo si = seq_record(p, s);
-    const SeqWork w = seq_work(false, p.G, p.Hq, p.Hkv, si.q_len, si.L);
+    const EntX ex = ent_x(p, s, si.flags);
+    const bool grp = si.flags & kEntGroup;  // rows of several members over their shared keys
+    const SeqWork w = seq_work(false, p.G, p.Hq, p.Hkv, si.q_len, si.L - ex.koff);
     const int pidx = local % w.nparts;
     const int rest = local / w.nparts;
     const int kvh = rest % p.Hkv;
@@ -532,10 +628,10 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
     const int qi = R / p.G;
     const int hh = kvh * p.G + R % p.G;
     const int t = si.a + qi;
-    const int pos_r = si.L - si.q_len + qi;
+    const int pos_r = grp ? si.L - 1 : si.L - si.q_len + qi;
     const int last_row = min(tile * kTileRows + kTileRows - 1, rows_total - 1);
-    const int tile_pos_max = si.L - si.q_len + last_row / p.G;
-    const int kv_lo = pidx * w.part;
+    const int tile_pos_max = grp ? si.L - 1 : si.L - si.q_len + last_row / p.G;
+    const int kv_lo = ex.koff + pidx * w.part;
     const int kv_hi = min(kv_lo + w.part, tile_pos_max + 1);
 
     float m_r = kNegInf, lsum = 0.f;
@@ -545,7 +641,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
 
     if (kv_lo < kv_hi) {
       const int nblk = (kv_hi - kv_lo + kBlock - 1) / kBlock;
-      const int bidv = load_block_ids(p, s, kv_lo / kBlock, nblk, lane);
+      const int bidv = load_block_ids(p, ex.trow, kv_lo / kBlock, nblk, lane);  // a group reads its first member's table
 
       bf16x8 qop[KS];
       {
@@ -561,7 +657,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
       // again: their scores are masked and their values zeroed, and every
       // address stays inside the pool.
       constexpr int NH = 2;  // 32-key halves per step
-      const int pos_lo = si.L - si.q_len + (tile * kTileRows) / p.G;  // lowest row position of the tile
+      const int pos_lo = grp ? si.L - 1 : si.L - si.q_len + (tile * kTileRows) / p.G;  // lowest row position
       for (int base = kv_lo; base < kv_hi; base += 32 * NH) {
         bf16x8 k0[NH][KS], k1[NH][KS];
         uint32_t vw[NH][NJ][4];  // value operand words: keys 4*g4 + 0..3 of the half's page 0, then of its page 1
@@ -677,7 +773,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
       }
     }
     const float l = sum_over_rows(lsum);
-    if (w.nparts == 1) {
+    if (!grp && ex.nps == 0 && w.nparts == 1) {
       bf16_t* orow = (bf16_t*)p.out + ((int64_t)t * p.Hq + hh) * D;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
@@ -685,7 +781,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
         *reinterpret_cast<u32x2*>(orow + 16 * j + 4 * g4) = pk;
       }
     } else {
-      float* slot = p.partials + (((int64_t)t * p.Hq + hh) * p.maxparts + pidx) * slot_floats(D);
+      float* slot = p.partials + (((int64_t)t * p.Hq + hh) * p.maxparts + ex.nps + pidx) * slot_floats(D);
 #pragma unroll
       for (int j = 0; j < NJ; ++j) *reinterpret_cast<f32x4*>(slot + 16 * j + 4 * g4) = oacc[j];
       slot[D] = m_r;  // the four lanes of a row hold the same m and l
@@ -749,7 +845,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
   const float csc = fmaxf(fabsf(p.scale_log2), 1e-30f);  // scale 0 gives equal weights, as it should
   const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
   const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
-  const SkipTable tab = stage_skip(skip, p.pre_t, p.num_seqs);
+  const SkipTable tab = stage_skip(skip, p.pre_t, p.num_ent);
   // this lane's key operand: page r/8, key 8((r/4)%2) + 4mm + r%4; value piece: page g/2, keys 8(g%2) ..
   const int krow = 8 * ((r >> 2) & 1) + (r & 3);
   const int kpage = r >> 3;
@@ -763,7 +859,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
     return wave_uniform(ticket) + (int)gridDim.x;
   };
   for (int item = (int)blockIdx.x; item < total; item = next_item()) {
-    const SeqHit hit = find_seq(skip, tab, p.pre_t, p.num_seqs, item);
+    const SeqHit hit = find_seq(skip, tab, p.pre_t, p.num_ent, item);
     const int s = hit.s;
     const int local = item - hit.first;
     const SeqInfo si = seq_record(p, s);
@@ -995,17 +1091,19 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
   const int wv = wave_uniform((int)(threadIdx.x >> 6));
   const int sub = wv % WPR;
   const int total = wave_uniform(p.ctrl[5]);
-  const SkipTable tab = stage_skip(skip, p.pre_g, p.num_seqs);
+  const SkipTable tab = stage_skip(skip, p.pre_g, p.num_ent);
   // row g of the merge list; the WPR wavefronts sharing a row see the same g
   for (int g = (int)blockIdx.x * RPB + wv / WPR; g < total; g += (int)gridDim.x * RPB) {
-    const SeqHit hit = find_seq(skip, tab, p.pre_g, p.num_seqs, g);
+    const SeqHit hit = find_seq(skip, tab, p.pre_g, p.num_ent, g);
     const SeqInfo si = seq_record(p, hit.s);
-    const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L);
+    const EntX ex = ent_x(p, hit.s, si.flags);
+    const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L - ex.koff);
     const int local = g - hit.first;
     const int i = local / p.Hq, h = local % p.Hq;
     const int t = si.a + i;
     const int pos = si.L - si.q_len + i;
-    const int np = min(w.nparts, pos / w.part + 1);  // later partitions hold no visible key
+    // shared partitions, then the row's own ones; later partitions hold no visible key
+    const int np = ex.nps + (w.nparts > 0 ? min(w.nparts, (pos - ex.koff) / w.part + 1) : 0);
     const float* base = p.partials + ((int64_t)t * p.Hq + h) * p.maxparts * SF;
     // M and l over all partitions; lanes past np read partition 0 and drop it
     float M = kNegInf;
@@ -1068,24 +1166,28 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
 
 // ---------------------------------------------------------------- host side
 struct WsLayout {
-  size_t ctrl, pre_v, pre_m, pre_t, pre_g, seqinfo, partials, total;
+  size_t ctrl, pre_v, pre_m, pre_t, pre_g, seqinfo, seqx, partials, total;
   int maxparts;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-WsLayout ws_layout(int S, int T, int Hq, int Hkv, int D, int max_ctx, bool is_f32) {
+// Workspace of a batch of S sequences and NG shared-prefix groups (entries S + NG).
+WsLayout ws_layout(int S, int NG, int T, int Hq, int Hkv, int D, int max_ctx, bool is_f32) {
   WsLayout l;
   const int G = Hq / Hkv;
   const int part = min_part(is_f32, G);
-  l.maxparts = max(1, (max_ctx + part - 1) / part);
+  const int E = S + NG;
+  // a member of a group adds at most one partition: its shared and own keys are split separately
+  l.maxparts = max(1, (max_ctx + part - 1) / part) + (NG > 0 ? 1 : 0);
   l.ctrl = 0;
   l.pre_v = 256;
-  l.pre_m = l.pre_v + align256((size_t)(S + 1) * 4);
-  l.pre_t = l.pre_m + align256((size_t)(S + 1) * 4);
-  l.pre_g = l.pre_t + align256((size_t)(S + 1) * 4);
-  l.seqinfo = l.pre_g + align256((size_t)(S + 1) * 4);
-  l.partials = l.seqinfo + align256((size_t)S * 16);
+  l.pre_m = l.pre_v + align256((size_t)(E + 1) * 4);
+  l.pre_t = l.pre_m + align256((size_t)(E + 1) * 4);
+  l.pre_g = l.pre_t + align256((size_t)(E + 1) * 4);
+  l.seqinfo = l.pre_g + align256((size_t)(E + 1) * 4);
+  l.seqx = l.seqinfo + align256((size_t)E * 16);
+  l.partials = l.seqx + (NG > 0 ? align256((size_t)E * 16) : 0);
   const size_t part_bytes = l.maxparts > 1 ? (size_t)T * Hq * l.maxparts * slot_floats(D) * 4 : 0;
   l.total = l.partials + align256(part_bytes);
   return l;
@@ -1147,20 +1249,32 @@ extern "C" size_t pa_forward_workspace_bytes(int32_t num_seqs, int32_t total_q_t
   if (num_seqs < 0 || total_q_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       head_dim <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads)
     return 0;
-  return ws_layout(num_seqs, total_q_tokens, num_q_heads, num_kv_heads, head_dim, max_context_len,
+  return ws_layout(num_seqs, 0, total_q_tokens, num_q_heads, num_kv_heads, head_dim, max_context_len,
                    dtype == PA_F32)
       .total;
 }
 
-extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* v_cache,
-                                const int32_t* block_tables, int32_t max_blocks_per_seq,
-                                const int32_t* context_lens, const int32_t* query_start_loc,
-                                int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
-                                int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
-                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                                float scale, pa_dtype dtype, void* workspace,
-                                size_t workspace_bytes, int32_t* dev_status, void* stream) {
-  const char* fn = "pa_forward";
+extern "C" size_t pa_forward_shared_workspace_bytes(int32_t num_seqs, int32_t num_groups, int32_t total_q_tokens,
+                                                    int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                                    int32_t head_dim, int32_t max_context_len, pa_dtype dtype) {
+  (void)max_q_len;
+  if (num_seqs < 0 || num_groups < 0 || total_q_tokens < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0 || max_context_len < 0 || num_q_heads % num_kv_heads)
+    return 0;
+  return ws_layout(num_seqs, num_groups, total_q_tokens, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                   dtype == PA_F32)
+      .total;
+}
+
+namespace {
+
+pa_status forward_impl(const char* fn, void* out, const void* q, const void* k_cache, const void* v_cache,
+                       const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       const int32_t* query_start_loc, const int32_t* groups, int32_t num_groups,
+                       int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len, int32_t max_context_len,
+                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, float scale, pa_dtype dtype, void* workspace, size_t workspace_bytes,
+                       int32_t* dev_status, void* stream) {
   if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
   if (block_size != kBlock)
     return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only 16 is supported)", fn, block_size);
@@ -1191,7 +1305,12 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
     return fail(PA_ERR_INVALID, "%s: NULL device pointer", fn);
   if ((uintptr_t)workspace % 256) return fail(PA_ERR_INVALID, "%s: workspace not 256-byte aligned", fn);
   const bool is_f32 = dtype == PA_F32;
-  const WsLayout wl = ws_layout(num_seqs, total_q_tokens, num_q_heads, num_kv_heads, head_dim,
+  if (num_groups < 0 || (num_groups > 0 && !groups)) return fail(PA_ERR_INVALID, "%s: bad group list", fn);
+  if (num_groups > 0 && (is_f32 || 2 * (num_q_heads / num_kv_heads) > kTileRows))
+    return fail(PA_ERR_UNSUPPORTED, "%s: shared prefixes need bfloat16 and at most %d query heads per KV head", fn,
+                kTileRows / 2);
+  if (num_groups > num_seqs) return fail(PA_ERR_INVALID, "%s: %d groups for %d sequences", fn, num_groups, num_seqs);
+  const WsLayout wl = ws_layout(num_seqs, num_groups, total_q_tokens, num_q_heads, num_kv_heads, head_dim,
                                 max_context_len, is_f32);
   if (workspace_bytes < wl.total)
     return fail(PA_ERR_INVALID, "%s: workspace of %zu bytes, %zu needed", fn, workspace_bytes, wl.total);
@@ -1225,13 +1344,17 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
   p.partials = (float*)(ws + wl.partials);
   p.maxparts = wl.maxparts;
   p.dev_status = dev_status;
+  p.num_ent = num_seqs + num_groups;
+  p.groups = groups;
+  p.num_groups = num_groups;
+  p.seqx = num_groups > 0 ? (i32x4*)(ws + wl.seqx) : nullptr;
 
   // Which worker classes can receive items (decided from host-known bounds only).
   const bool may_valu = is_f32 || p.G == 1;
-  const bool may_mfma = !is_f32 && p.G <= kTileRows && (p.G > 1 || max_q_len > 1);
+  const bool may_mfma = !is_f32 && p.G <= kTileRows && (p.G > 1 || max_q_len > 1 || num_groups > 0);
   const bool may_tile = !is_f32 && (int64_t)max_q_len * p.G > kTileRows;
   const int64_t bound_v = (int64_t)total_q_tokens * num_q_heads * wl.maxparts;
-  const int64_t bound_m = (int64_t)num_seqs * num_kv_heads * wl.maxparts;
+  const int64_t bound_m = (int64_t)(num_seqs + num_groups) * num_kv_heads * wl.maxparts;
   const int64_t bound_t =
       ((int64_t)total_q_tokens * p.G / kBigRows + num_seqs) * num_kv_heads * wl.maxparts;
   const int grid_v = (int)std::min<int64_t>(kMaxWorkerGroups, (bound_v + 3) / 4);
@@ -1249,6 +1372,37 @@ extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, c
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" pa_status pa_forward(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, const int32_t* query_start_loc,
+                                int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                                int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                float scale, pa_dtype dtype, void* workspace,
+                                size_t workspace_bytes, int32_t* dev_status, void* stream) {
+  return forward_impl("pa_forward", out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens,
+                      query_start_loc, nullptr, 0, num_seqs, total_q_tokens, max_q_len, max_context_len,
+                      num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype, workspace,
+                      workspace_bytes, dev_status, stream);
+}
+
+extern "C" pa_status pa_forward_shared(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                       const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                       const int32_t* context_lens, const int32_t* query_start_loc,
+                                       const int32_t* groups, int32_t num_groups, int32_t num_seqs,
+                                       int32_t total_q_tokens, int32_t max_q_len, int32_t max_context_len,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t num_blocks, float scale, pa_dtype dtype,
+                                       void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                                       void* stream) {
+  return forward_impl("pa_forward_shared", out, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                      context_lens, query_start_loc, groups, num_groups, num_seqs, total_q_tokens, max_q_len,
+                      max_context_len, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, dtype,
+                      workspace, workspace_bytes, dev_status, stream);
 }
 
 extern "C" pa_status pa_set_stage_events(void* const* events, int32_t num_events) {

@@ -74,6 +74,21 @@ def forward(w, q, kp, vp):
     return np.frombuffer(raw, dt).reshape(w.num_tokens, w.num_q_heads, w.head_dim), st
 
 
+def forward_shared(w, q, kp, vp, groups):
+    """Emulated pa_forward_shared; groups: int [G, 3] (first sequence, members, shared keys)."""
+    es = 4 if w.dtype == "f32" else 2
+    groups = np.ascontiguousarray(np.asarray(groups, np.int32).reshape(-1, 3))
+    hdr = np.array([dtype_code(w.dtype), w.num_seqs, w.num_tokens, w.max_q_len, w.max_context_len,
+                    w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_blocks, w.max_blocks_per_seq], np.int32)
+    blob = [hdr, np.array([w.scale], np.float32), q, kp, vp, w.block_tables.astype(np.int32),
+            w.context_lens.astype(np.int32), w.query_start_loc.astype(np.int32),
+            np.array([groups.shape[0]], np.int32), groups]
+    n = w.num_tokens * w.num_q_heads * w.head_dim
+    raw, st = _run("forward_shared", blob, n * es)
+    dt = np.float32 if w.dtype == "f32" else np.uint16
+    return np.frombuffer(raw, dt).reshape(w.num_tokens, w.num_q_heads, w.head_dim), st
+
+
 def reshape_and_cache(dtype, key, val, kp, vp, slots):
     T, hkv, d = key.shape
     nb = kp.shape[0]

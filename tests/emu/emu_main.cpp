@@ -109,6 +109,35 @@ int main(int argc, char** argv) {
     std::free(ws);
     std::free(out);
     std::free(q); std::free(kc); std::free(vc); std::free(tab); std::free(lens); std::free(qsl);
+  } else if (!std::strcmp(argv[1], "forward_shared")) {
+    // forward, then i32 num_groups and the groups [num_groups][3]
+    const int dt = rd_i32(), S = rd_i32(), T = rd_i32(), mq = rd_i32(), mc = rd_i32();
+    const int Hq = rd_i32(), Hkv = rd_i32(), D = rd_i32(), NB = rd_i32(), mbps = rd_i32();
+    const float scale = rd_f32();
+    const size_t es = dt == PA_F32 ? 4 : 2;
+    void* q = rd_buf((size_t)T * Hq * D * es);
+    void* kc = rd_buf((size_t)NB * Hkv * 16 * D * es);
+    void* vc = rd_buf((size_t)NB * Hkv * 16 * D * es);
+    auto* tab = (int32_t*)rd_buf((size_t)S * mbps * 4);
+    auto* lens = (int32_t*)rd_buf((size_t)S * 4);
+    auto* qsl = (int32_t*)rd_buf((size_t)(S + 1) * 4);
+    const int NG = rd_i32();
+    auto* groups = (int32_t*)rd_buf((size_t)NG * 12);
+    void* out = std::malloc((size_t)T * Hq * D * es);
+    std::memset(out, 0xff, (size_t)T * Hq * D * es);
+    const size_t wsb = pa_forward_shared_workspace_bytes(S, NG, T, mq, Hq, Hkv, D, mc, (pa_dtype)dt);
+    void* ws = std::aligned_alloc(256, wsb);
+    std::memset(ws, 0xa5, wsb);
+    pa_status st = pa_forward_shared(out, q, kc, vc, tab, mbps, lens, qsl, NG ? groups : nullptr, NG, S, T, mq, mc,
+                                     Hq, Hkv, D, 16, NB, scale, (pa_dtype)dt, ws, wsb, &status, nullptr);
+    if (st != PA_OK) {
+      std::fprintf(stderr, "pa_forward_shared: %d %s\n", st, pa_last_error());
+      return 3;
+    }
+    wr(out, (size_t)T * Hq * D * es);
+    std::free(ws);
+    std::free(out);
+    std::free(q); std::free(kc); std::free(vc); std::free(tab); std::free(lens); std::free(qsl); std::free(groups);
   } else if (!std::strcmp(argv[1], "reshape")) {
     const int dt = rd_i32(), T = rd_i32(), NB = rd_i32(), Hkv = rd_i32(), D = rd_i32();
     const size_t es = dt == PA_F32 ? 4 : 2;

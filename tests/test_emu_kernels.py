@@ -14,7 +14,8 @@ from oracle import attention as oattn
 from oracle import cache_ops, layout
 from tests import _emu
 from tests._pools import empty_pools, raw
-from tests.test_gpu_parity import RAGGED, REJECTED, many_sequences_batch, read_probe_case
+from tests.test_gpu_parity import (RAGGED, REJECTED, SHARED_CASES, many_sequences_batch, read_probe_case,
+                                   shared_prefix_batch)
 
 pytestmark = pytest.mark.skipif(not _emu.available(), reason="needs the ROCm clang++ for the host build")
 TOL = {"bf16": (2e-3, 1e-2), "f32": (1e-5, 1e-5)}
@@ -213,3 +214,15 @@ def test_rope_bad_position_skips_the_token_emulated(emu):
     from tests import _rope
     keep = [0, 2]
     _rope.check("bf16", qo[keep], ko, vo, q[keep], key[keep], val[keep], kp, vp, slots[keep], pos[keep], cos, sin)
+
+
+@pytest.mark.parametrize("case", range(len(SHARED_CASES)))
+def test_shared_prefix_forward_emulated(emu, case):
+    seed, hq, hkv, d, spec, bad = SHARED_CASES[case]
+    w, groups = shared_prefix_batch(seed, hq, hkv, d, spec, bad_group=bad)
+    rng = np.random.default_rng(50 + case)
+    kp, vp = empty_pools(rng, "bf16", w.num_blocks, hkv, d)
+    q = raw(rng.standard_normal((w.num_tokens, hq, d)).astype(np.float32), "bf16")
+    out, st = emu.forward_shared(w, q, kp, vp, groups)
+    assert st == (16 if bad else 0)
+    check(w, q, kp, vp, out, f"shared case {case}")

@@ -187,6 +187,63 @@ def many_sequences_batch(n=5000):
     return W.random_ragged(32, "bf16", 2, 2, 64, ql, cl)
 
 
+def shared_prefix_batch(seed, hq, hkv, d, groups_spec, loose_decodes=2, chunk=(5, 300), bad_group=False):
+    """A batch whose decode sequences come in groups sharing the pages of a prompt.
+    groups_spec: [(members, prompt length)]; every member's context is the prompt plus a
+    few tokens of its own (its own partial and later pages), and the group shares the
+    prompt's full pages (shared keys = 16 * floor(prompt / 16)).  Plus loose decodes and
+    one prefill chunk (q_len, context) that belong to no group.  With bad_group the last
+    group's second member gets a different page at position 0 (the group must be refused).
+    Returns the workload and the [G, 3] group list."""
+    rng = np.random.default_rng(seed)
+    lens, qls, tabs, groups = [], [], [], []
+    nxt = [0]
+    def fresh(n):
+        ids = list(range(nxt[0], nxt[0] + n))
+        nxt[0] += n
+        return ids
+    for members, plen in groups_spec:
+        shared = fresh(plen // 16)
+        groups.append([len(lens), members, 16 * (plen // 16)])
+        for m in range(members):
+            L = plen + int(rng.integers(1, 40))
+            own = fresh((L + 15) // 16 - len(shared))
+            lens.append(L)
+            qls.append(1)
+            tabs.append(shared + own)
+    for _ in range(loose_decodes):
+        L = int(rng.integers(20, 700))
+        lens.append(L)
+        qls.append(1)
+        tabs.append(fresh((L + 15) // 16))
+    if chunk:
+        q, L = chunk
+        lens.append(L)
+        qls.append(q)
+        tabs.append(fresh((L + 15) // 16))
+    if bad_group:
+        g = groups[-1]
+        tabs[g[0] + 1] = [fresh(1)[0]] + tabs[g[0] + 1][1:]
+    nb = nxt[0] + 4
+    perm = rng.permutation(nb).astype(np.int32)          # physical blocks in random order
+    mb = max(len(t) for t in tabs)
+    tables = np.full((len(lens), mb), -1, np.int32)
+    for i, t in enumerate(tabs):
+        tables[i, :len(t)] = perm[np.asarray(t)]
+    qsl = np.concatenate([[0], np.cumsum(qls)]).astype(np.int32)
+    w = W.Workload(f"shared_s{seed}", "bf16", hq, hkv, d, nb, np.asarray(lens, np.int32), qsl, tables,
+                   float(np.float32(1.0 / np.sqrt(d))), None, seed)
+    return w, np.asarray(groups, np.int32)
+
+
+SHARED_CASES = [  # (seed, hq, hkv, d, groups, bad)
+    (1, 8, 8, 128, [(3, 100), (4, 530), (2, 40)], False),
+    (2, 8, 2, 128, [(4, 300), (2, 1100)], False),
+    (3, 4, 4, 64, [(16, 70), (3, 2100)], False),
+    (4, 8, 8, 128, [(3, 100), (2, 200)], True),
+]
+
+
 def test_many_sequences(pa):
     w = many_sequences_batch()
     run_and_check(pa, w, label="5000 sequences")
@@ -461,6 +518,38 @@ def test_rope_then_attention(pa):
     ratio = float((np.abs(got - ref) / (a + r * np.abs(ref))).max())
     say(f"  worst err/bound {ratio:.3f}")
     assert np.isfinite(got).all() and ratio <= 1.0
+
+
+@pytest.mark.parametrize("case", range(len(SHARED_CASES)))
+def test_shared_prefix_forward(pa, case):
+    """Decode groups sharing prompt pages through pa_forward_shared: every row against the
+    fp64 oracle (plain attention over each sequence's own table) and against pa_forward."""
+    seed, hq, hkv, d, spec, bad = SHARED_CASES[case]
+    w, groups = shared_prefix_batch(seed, hq, hkv, d, spec, bad_group=bad)
+    say(f"[case] shared prefixes {spec} hq={hq} hkv={hkv} d={d} bad={bad}")
+    check_tables_in_pool(w)
+    q, kc, vc, _, _ = W.make_values(w, DEV)
+    r = Run(w)
+    ref_out = r.forward(q, kc, vc)
+    torch.cuda.synchronize()
+    r.check_status()
+    nbytes = pa.pa_forward_shared_workspace_bytes(w.num_seqs, len(groups), w.num_tokens, w.max_q_len, hq, hkv, d,
+                                                  w.max_context_len, pa.PA_BF16)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = torch.empty_like(q)
+    pa.pa_forward_shared(out, q, kc, vc, r.tables, r.lens, r.qsl, torch.from_numpy(groups).to(DEV), w.max_q_len,
+                         w.max_context_len, w.scale, ws, status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == (pa.PA_DEV_BAD_GROUP if bad else 0)
+    rows, ref = oracle_rows(w, q, kc, vc, range(w.num_seqs))
+    got = to_f64(out)
+    assert np.isfinite(got).all()
+    assert_close(got[rows], ref, "bf16", f"shared case {case}")
+    # the same attention as pa_forward, up to the rounding of the split
+    a, rr = 2e-3, 1e-2
+    plain = to_f64(ref_out)
+    assert (np.abs(got - plain) <= a + rr * np.abs(plain)).all()
 
 
 def read_probe_case():
