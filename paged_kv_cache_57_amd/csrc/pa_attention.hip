@@ -86,6 +86,15 @@ __host__ __device__ inline SeqWork seq_work(bool is_f32, int G, int Hq, int Hkv,
   return w;
 }
 
+// A shared-prefix group entry: its members' rows over the S shared keys, in
+// partitions of the one-row decode size (the group's rows are decode rows,
+// and short partitions spread its keys over many wavefronts).
+__host__ __device__ inline SeqWork group_work(int Hkv, int S) {
+  SeqWork w{CLS_MFMA, kPartMfmaDecode, 0, Hkv};
+  w.nparts = (S + kPartMfmaDecode - 1) / kPartMfmaDecode;
+  return w;
+}
+
 // Smallest partition any sequence of this batch can use (bounds the partial states).
 inline int min_part(bool is_f32, int G) {
   if (is_f32) return kPartValu;
@@ -281,7 +290,7 @@ __device__ inline void plan_groups(const AttnParams& p, int tid) {
     __syncthreads();
     if (tid == 0) {
       const bool good = shape && g_bad == 0;
-      const int nps = good ? seq_work(false, p.G, p.Hq, p.Hkv, n, S).nparts : 0;
+      const int nps = good ? group_work(p.Hkv, S).nparts : 0;
       if (good) {
         for (int m = 0; m < n; ++m) p.seqx[first + m] = i32x4{S, nps, 1, 0};
         g_prev_end = first + n;
@@ -333,7 +342,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
     } else if (s < p.num_ent) {
       const i32x4 r = p.seqinfo[s];  // a group entry, recorded by plan_groups
       if (r[3] & kEntGroup) {
-        const SeqWork w = seq_work(false, p.G, p.Hq, p.Hkv, r[1], r[2]);
+        const SeqWork w = group_work(p.Hkv, r[2]);
         cnt[1] = w.groups * w.nparts;
       }
     }
@@ -615,7 +624,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
     const SeqInfo si = seq_record(p, s);
     const EntX ex = ent_x(p, s, si.flags);
     const bool grp = si.flags & kEntGroup;  // rows of several members over their shared keys
-    const SeqWork w = seq_work(false, p.G, p.Hq, p.Hkv, si.q_len, si.L - ex.koff);
+    const SeqWork w = grp ? group_work(p.Hkv, si.L) : seq_work(false, p.G, p.Hq, p.Hkv, si.q_len, si.L - ex.koff);
     const int pidx = local % w.nparts;
     const int rest = local / w.nparts;
     const int kvh = rest % p.Hkv;
@@ -1176,7 +1185,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 WsLayout ws_layout(int S, int NG, int T, int Hq, int Hkv, int D, int max_ctx, bool is_f32) {
   WsLayout l;
   const int G = Hq / Hkv;
-  const int part = min_part(is_f32, G);
+  // group entries split their shared keys in decode-size partitions
+  const int part = NG > 0 ? std::min(min_part(is_f32, G), kPartMfmaDecode) : min_part(is_f32, G);
   const int E = S + NG;
   // a member of a group adds at most one partition: its shared and own keys are split separately
   l.maxparts = max(1, (max_ctx + part - 1) / part) + (NG > 0 ? 1 : 0);
