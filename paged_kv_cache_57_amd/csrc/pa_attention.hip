@@ -256,51 +256,42 @@ __device__ inline i32x4 wave_incl_scan(i32x4 v, int lane) {
   return v;
 }
 
-// With shared-prefix groups it first checks every group (one at a time, all
-// threads comparing the members' table entries with the first member's) and
-// records the group entries and the members' offsets; a group that fails a
-// check is dropped (its members are attended as plain sequences) and
-// PA_DEV_BAD_GROUP is set.
+// With shared-prefix groups it first checks every group — one wavefront per
+// group, the lanes comparing the members' table entries with the first
+// member's — and records the group entries and the members' offsets; a group
+// that fails a check is dropped (its members are attended as plain
+// sequences) and PA_DEV_BAD_GROUP is set.
 __device__ inline void plan_groups(const AttnParams& p, int tid) {
-  __shared__ int g_bad, g_prev_end;
   for (int s = tid; s < p.num_seqs; s += 1024) p.seqx[s] = i32x4{0, 0, 0, 0};
-  if (tid == 0) g_prev_end = 0;
-  __syncthreads();
-  for (int g = 0; g < p.num_groups; ++g) {
+  __syncthreads();  // members are marked below, after every entry has been cleared
+  const int lane = tid & 63;
+  for (int g = tid >> 6; g < p.num_groups; g += 16) {
     const int first = p.groups[3 * g], n = p.groups[3 * g + 1], S = p.groups[3 * g + 2];
-    // groups in increasing order, no overlap, 2..16/G members inside the batch, whole shared pages
-    const bool shape = first >= g_prev_end && n >= 2 && n <= kTileRows && n * p.G <= kTileRows &&
+    // in increasing order without overlap, 2..16/G members inside the batch, whole shared pages
+    const bool after_prev = g == 0 || (int64_t)first >= (int64_t)p.groups[3 * g - 3] + p.groups[3 * g - 2];
+    const bool shape = after_prev && n >= 2 && n <= kTileRows && n * p.G <= kTileRows && first >= 0 &&
                        first <= p.num_seqs - n && S > 0 && S % kBlock == 0 && S <= p.max_ctx;
-    __syncthreads();  // every thread has read g_prev_end
-    if (tid == 0) g_bad = shape ? 0 : 1;
-    __syncthreads();
+    bool bad = !shape;
     if (shape) {
-      if (tid < n) {
-        const SeqInfo si = read_seq(p, first + tid);
-        if (!si.ok || si.q_len != 1 || si.L < S) atomicOr(&g_bad, 1);
-      }
+      const SeqInfo si = read_seq(p, first + min(lane, n - 1));
+      bad = !si.ok || si.q_len != 1 || si.L < S;
       const int nb = S / kBlock;  // <= mbps, as S <= max_ctx
       const int64_t cmp = (int64_t)(n - 1) * nb;
-      for (int64_t i = tid; i < cmp; i += 1024) {
+      const int32_t* lead = p.block_tables + (int64_t)first * p.mbps;
+#pragma unroll 4
+      for (int64_t i = lane; i < cmp; i += 64) {
         const int m = 1 + (int)(i / nb), j = (int)(i % nb);
-        if (p.block_tables[(int64_t)(first + m) * p.mbps + j] != p.block_tables[(int64_t)first * p.mbps + j])
-          atomicOr(&g_bad, 1);
+        bad = bad || p.block_tables[(int64_t)(first + m) * p.mbps + j] != lead[j];
       }
     }
-    __syncthreads();
-    if (tid == 0) {
-      const bool good = shape && g_bad == 0;
-      const int nps = good ? group_work(p.Hkv, S).nparts : 0;
-      if (good) {
-        for (int m = 0; m < n; ++m) p.seqx[first + m] = i32x4{S, nps, 1, 0};
-        g_prev_end = first + n;
-      } else {
-        flag_status(p.dev_status, PA_DEV_BAD_GROUP);
-      }
+    const bool good = __builtin_amdgcn_ballot_w64(bad) == 0;
+    const int nps = good ? group_work(p.Hkv, S).nparts : 0;
+    if (good && lane < n) p.seqx[first + lane] = i32x4{S, nps, 1, 0};
+    if (lane == 0) {
+      if (!good) flag_status(p.dev_status, PA_DEV_BAD_GROUP);
       p.seqinfo[p.num_seqs + g] = i32x4{good ? p.qsl[first] : 0, n, S, good ? (kEntValid | kEntGroup) : 0};
       p.seqx[p.num_seqs + g] = i32x4{0, 0, 0, good ? first : 0};
     }
-    __syncthreads();
   }
 }
 
