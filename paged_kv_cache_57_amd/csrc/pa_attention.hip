@@ -278,11 +278,13 @@ __device__ inline void plan_groups(const AttnParams& p, int tid) {
       const int nb = S / kBlock;  // <= mbps, as S <= max_ctx
       const int64_t cmp = (int64_t)(n - 1) * nb;
       const int32_t* lead = p.block_tables + (int64_t)first * p.mbps;
+      bool diff = false;  // no short circuit: the loads of all iterations are independent
 #pragma unroll 4
       for (int64_t i = lane; i < cmp; i += 64) {
         const int m = 1 + (int)(i / nb), j = (int)(i % nb);
-        bad = bad || p.block_tables[(int64_t)(first + m) * p.mbps + j] != lead[j];
+        diff |= p.block_tables[(int64_t)(first + m) * p.mbps + j] != lead[j];
       }
+      bad = bad || diff;
     }
     const bool good = __builtin_amdgcn_ballot_w64(bad) == 0;
     const int nps = good ? group_work(p.Hkv, S).nparts : 0;
