@@ -1028,24 +1028,33 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
     // registers, and every half requests one step (past the last step it
     // requests the last one again): the number of loads in flight is then
     // the same on every path, and the compiler waits for exactly the set
-    // being stored.
+    // being stored.  The loop has a single exit, at its top: exits in the
+    // middle of the body reach the loop head in the compiler's control flow
+    // with the other set's loads still pending, and it then waited for all
+    // loads at the head of every pass, which made the prefetch one step deep.
     u32x4 rset0[IPW], rset1[IPW];
     __syncthreads();  // every wavefront is done with the stages of the previous item
     fetch(0, rset0);
     fetch(min(1, nsteps - 1), rset1);
     put(rset0, 0);
     __syncthreads();
-    for (int st = 0;; st += 2) {
-      fetch(min(st + 2, nsteps - 1), rset0);
+    int st = 0;
+    for (; st + 2 < nsteps; st += 2) {
+      fetch(st + 2, rset0);
       compute_step(st);
-      if (st + 1 >= nsteps) break;
       put(rset1, (st + 1) % kTileStages);
       __syncthreads();
       fetch(min(st + 3, nsteps - 1), rset1);
       compute_step(st + 1);
-      if (st + 2 >= nsteps) break;
       put(rset0, (st + 2) % kTileStages);
       __syncthreads();
+    }
+    // the last one or two steps: stage st holds step st, rset1 step st + 1
+    compute_step(st);
+    if (st + 1 < nsteps) {
+      put(rset1, (st + 1) % kTileStages);
+      __syncthreads();
+      compute_step(st + 1);
     }
 
     if (active) {
