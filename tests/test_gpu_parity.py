@@ -151,10 +151,10 @@ RAGGED = [
     ("bf16", 8, 8, 128, [37, 1, 16, 1], [37, 900, 1100, 2]),      # prefill tiles (prior 0 and 1084)
     ("bf16", 16, 4, 128, [9, 3, 1], [2100, 3, 64]),               # GQA prefill: rows = positions x heads
     ("bf16", 4, 4, 64, [70, 1], [1500, 5]),                       # prefill crossing partitions of 1024
-    ("bf16", 8, 8, 128, [300, 1], [2500, 40]),                    # 128-row tiles: 3 tiles, last one 44 rows
+    ("bf16", 2, 2, 128, [300, 1], [2500, 40]),                    # 128-row tiles: 3 tiles, last one 44 rows
     ("bf16", 16, 2, 64, [40, 17], [40, 1100]),                    # GQA tiles: 320 and 136 rows
     ("bf16", 4, 4, 128, [129, 128, 2], [129, 1152, 2]),           # tile edges: 129 and 128 rows, 2-row MFMA
-    ("bf16", 4, 1, 64, [1, 3], [9000, 8500]),                     # >= 32 partitions: four waves merge a row
+    ("bf16", 2, 2, 64, [1, 3], [16500, 700]),                     # >= 32 partitions: four waves merge a row
     ("f32", 2, 2, 64, [1, 2], [17000, 40]),                       # the same for float32 (512-key partitions)
 ]
 
@@ -174,7 +174,7 @@ def test_ragged_batches(pa, i):
     run_and_check(pa, w, label=f"ragged[{i}] {dt} Hq={hq} Hkv={hkv} d={d} q={ql} L={cl}")
 
 
-def many_sequences_batch(n=5000):
+def many_sequences_batch(n=5000, n_split=12, split_hi=1500, heads=2):
     """n sequences (more than the 2,047 the workers' LDS lookup table holds one by one):
     MHA decodes, some split into partitions, plus short prefill rows and empty-query sequences."""
     rng = np.random.default_rng(31)
@@ -182,9 +182,9 @@ def many_sequences_batch(n=5000):
     ql[rng.choice(n, 40, replace=False)] = 0                  # sequences with no query rows this pass
     ql[rng.choice(n, 20, replace=False)] = 3                  # short prefill rows (MFMA class)
     cl = rng.integers(1, 90, size=n)
-    cl[rng.choice(n, 12, replace=False)] = rng.integers(600, 1500, size=12)   # split contexts
+    cl[rng.choice(n, n_split, replace=False)] = rng.integers(600, split_hi, size=n_split)   # split contexts
     cl = np.maximum(cl, ql)
-    return W.random_ragged(32, "bf16", 2, 2, 64, ql, cl)
+    return W.random_ragged(32, "bf16", heads, heads, 64, ql, cl)
 
 
 def shared_prefix_batch(seed, hq, hkv, d, groups_spec, loose_decodes=2, chunk=(5, 300), bad_group=False):

@@ -237,3 +237,31 @@ def test_allocator_under_address_and_ub_sanitizers():
             res = res[:1]
         got.append(res + (nfree,))
     assert got == run_mirror(ops, n_blocks, bs, 0.05, order)
+
+
+def test_shared_prefix_and_rope_argument_checks(pa):
+    """pa_forward_shared and pa_rope_reshape_and_cache reject bad arguments on the host
+    (the fake device addresses below are never touched: every call fails a check first)."""
+    lib = pa._binding._lib
+    fake = ctypes.c_void_p(1 << 20)
+
+    def shared(groups, ng, hq, hkv, d, dtype, ws_bytes=1 << 30, S=4, T=4):
+        return lib.pa_forward_shared(fake, fake, fake, fake, fake, 8, fake, fake, groups, ng, S, T, 1, 100, hq, hkv,
+                                     d, 16, 64, 1.0, dtype, fake, ws_bytes, None, None)
+    assert shared(fake, 1, 4, 4, 64, pa.PA_F32) == pa.PA_ERR_UNSUPPORTED and "bfloat16" in pa.pa_last_error()
+    assert shared(fake, 1, 32, 2, 128, pa.PA_BF16) == pa.PA_ERR_UNSUPPORTED      # 16 query heads per KV head
+    assert shared(fake, -1, 4, 4, 128, pa.PA_BF16) == pa.PA_ERR_INVALID and "group" in pa.pa_last_error()
+    assert shared(None, 2, 4, 4, 128, pa.PA_BF16) == pa.PA_ERR_INVALID
+    assert shared(fake, 5, 4, 4, 128, pa.PA_BF16) == pa.PA_ERR_INVALID          # more groups than sequences
+    assert shared(fake, 1, 4, 4, 128, pa.PA_BF16, ws_bytes=256) == pa.PA_ERR_INVALID and "workspace" in pa.pa_last_error()
+    plain = pa.pa_forward_workspace_bytes(4, 4, 1, 4, 4, 128, 100, pa.PA_BF16)
+    with_groups = pa.pa_forward_shared_workspace_bytes(4, 2, 4, 1, 4, 4, 128, 100, pa.PA_BF16)
+    assert with_groups > plain and pa.pa_forward_shared_workspace_bytes(-1, 0, 4, 1, 4, 4, 128, 100, 1) == 0
+
+    def rope(maxpos, d, cos=fake, T=3):
+        return lib.pa_rope_reshape_and_cache(fake, fake, fake, fake, fake, fake, fake, fake, cos, fake, maxpos, T, 4, 2,
+                                             8, d, 16, pa.PA_BF16, None, None)
+    assert rope(0, 128) == pa.PA_ERR_INVALID
+    assert rope(10, 96) == pa.PA_ERR_UNSUPPORTED
+    assert rope(10, 128, cos=None) == pa.PA_ERR_INVALID and "NULL" in pa.pa_last_error()
+    assert rope(10, 128, T=0) == pa.PA_OK                                       # nothing to do, nothing launched
