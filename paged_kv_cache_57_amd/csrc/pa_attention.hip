@@ -832,6 +832,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
   constexpr int NI = 2 * KS + NJ;         // 1 KiB operand blocks per step: keys (2 chains x KS), then values
   constexpr int IPW = NI / kTileWaves;    // blocks each wavefront loads per step
   static_assert(NI % kTileWaves == 0, "the blocks of a step split evenly over the wavefronts");
+  static_assert(IPW == 2 || IPW == 4, "loads pair the page halves of two blocks of one kind");
   static_assert(kPartTile % 32 == 0 && kPartTile <= 64 * kBlock, "a partition is whole steps of at most 64 pages");
   __shared__ u32x4 stage[kTileStages][NI * 64];
   __shared__ int skip[kSkip];
@@ -848,10 +849,6 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
   const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
   const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
   const SkipTable tab = stage_skip(skip, p.pre_t, p.num_ent);
-  // this lane's key operand: page r/8, key 8((r/4)%2) + 4mm + r%4; value piece: page g/2, keys 8(g%2) ..
-  const int krow = 8 * ((r >> 2) & 1) + (r & 3);
-  const int kpage = r >> 3;
-  const int vpage = g4 >> 1, vhalf = g4 & 1;
 
   __shared__ int ticket;
   auto next_item = [&]() {
@@ -903,32 +900,52 @@ __global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParam
     const int bidv = load_block_ids(p, s, kv_lo / kBlock, nblk, lane);
     const int nsteps = (kv_hi - kv_lo + 31) / 32;
 
-    // This lane's pieces of step st (blocks wv, wv + 4, ...): key block
-    // (mm, k) holds key 8((r/4)%2) + 4mm + r%4 of page r/8, dims 32k + 8g ..;
-    // value block j holds column 16j + r, keys 8(g%2) .. of page g/2.  Pages
-    // past the last one (odd counts) read the last page again: their scores
-    // are masked, their values zeroed, and every address stays inside the
-    // pool.  Only the two page offsets change from step to step.
-    const bf16_t* klane = kc + (int64_t)kvh * page_elems + (g4 * kBlock + krow) * 8;
-    const bf16_t* vlane = vc + (int64_t)kvh * page_elems + r * kBlock + 8 * vhalf;
-    auto fetch = [&](int st, u32x4 (&reg)[IPW]) {
-      const int64_t pg0 = (int64_t)readlane(bidv, min(2 * st, nblk - 1)) * blk_elems;
-      const int64_t pg1 = (int64_t)readlane(bidv, min(2 * st + 1, nblk - 1)) * blk_elems;
-      const bf16_t* kb = klane + (kpage ? pg1 : pg0);
-      const bf16_t* vb = vlane + (vpage ? pg1 : pg0);
+    // The pieces of a step: key block (mm, k) holds, for compute lane
+    // l = r + 16g, key 8((r/4)%2) + 4mm + r%4 of page r/8, dims 32k + 8g ..;
+    // value block j holds column 16j + r, keys 8(g%2) .. of page g/2.  This
+    // wavefront stores blocks ii(u) (u < IPW; blocks of one pair u = 2j, 2j+1
+    // are both keys or both values), and each of its loads reads ONE page:
+    // load q takes page q%2 of the pair q/2, loading lane λ fetching the piece
+    // of block u = 2(q/2) + λ/32 for the (λ%32)-th compute lane on that page
+    // and storing it at that lane's place in the LDS image.  A load's address
+    // is then a wave-uniform page base plus a constant 32-bit lane offset.
+    // Pages past the last one (odd counts) read the last page again: their
+    // scores are masked, their values zeroed, and every address stays inside
+    // the pool.
+    auto block_of = [&](int u) { return IPW == 4 ? wv + kTileWaves * u : IPW * wv + u; };  // wave-uniform
+    uint32_t loff[IPW];
+    int ldst[IPW];
 #pragma unroll
-      for (int u = 0; u < IPW; ++u) {
-        const int ii = wv + kTileWaves * u;  // wave-uniform
-        if (ii < 2 * KS) reg[u] = ld16(kb + ((ii % KS) * 4 * kBlock + 4 * (ii / KS)) * 8);
-        else reg[u] = ld16(vb + (ii - 2 * KS) * 16 * kBlock);
+    for (int q = 0; q < IPW; ++q) {
+      const int pq = q & 1, ii = block_of(2 * (q >> 1) + (lane >> 5)), m = lane & 31;
+      if (ii < 2 * KS) {  // key block
+        const int rr = 8 * pq + (m & 7), gg = m >> 3;
+        const int kr = 8 * ((rr >> 2) & 1) + (rr & 3);
+        loff[q] = (uint32_t)((gg * kBlock + kr) * 8 + ((ii % KS) * 4 * kBlock + 4 * (ii / KS)) * 8);
+        ldst[q] = ii * 64 + rr + 16 * gg;
+      } else {  // value block
+        const int l = 32 * pq + m;
+        loff[q] = (uint32_t)((l & 15) * kBlock + 8 * ((l >> 4) & 1) + (ii - 2 * KS) * 16 * kBlock);
+        ldst[q] = ii * 64 + l;
+      }
+    }
+    const int64_t head_off = (int64_t)kvh * page_elems;
+    auto fetch = [&](int st, u32x4 (&reg)[IPW]) {
+      const int64_t pg0 = (int64_t)readlane(bidv, min(2 * st, nblk - 1)) * blk_elems + head_off;
+      const int64_t pg1 = (int64_t)readlane(bidv, min(2 * st + 1, nblk - 1)) * blk_elems + head_off;
+#pragma unroll
+      for (int q = 0; q < IPW; ++q) {
+        const bool key = block_of(2 * (q >> 1)) < 2 * KS;  // wave-uniform
+        const bf16_t* base = (key ? kc : vc) + ((q & 1) ? pg1 : pg0);
+        reg[q] = ld16(base + loff[q]);
       }
     };
     // values enter LDS already as half x 2^-8 (each converted once per workgroup)
     auto put = [&](const u32x4 (&reg)[IPW], int stg) {
 #pragma unroll
-      for (int u = 0; u < IPW; ++u) {
-        const int ii = wv + kTileWaves * u;
-        stage[stg][ii * 64 + lane] = ii < 2 * KS ? reg[u] : bf16x8_to_f16x8_scaled(reg[u]);
+      for (int q = 0; q < IPW; ++q) {
+        const bool key = block_of(2 * (q >> 1)) < 2 * KS;
+        stage[stg][ldst[q]] = key ? reg[q] : bf16x8_to_f16x8_scaled(reg[q]);
       }
     };
 
