@@ -315,6 +315,23 @@ pa_status pa_seq_block_tables(const pa_allocator* a, int32_t n, const int64_t* s
  * caching, a block carrying a hash goes to the evictor instead). */
 pa_status pa_seq_free(pa_allocator* a, int64_t seq_id);
 
+/* Streaming sequence (StreamingLLM, "第 15 章：推理引擎与部署" §15.4 Attention
+ * Sink): the cache keeps the first num_sinks tokens and the most recent
+ * `window` tokens, at most num_sinks + window, at cache positions
+ * 0 .. num_sinks + window - 1.  Created with num_tokens <= num_sinks + window
+ * tokens (positions 0 .. num_tokens - 1; the caller keeps a longer prompt's
+ * sinks and last tokens).  pa_seq_append_slot / pa_seq_append_slots: while the
+ * cache grows, as for any sequence; once it is full, the new token takes the
+ * position of the oldest window token, num_sinks + (seen - num_sinks) mod
+ * window, seen = tokens appended before it (a ring: attention does not depend
+ * on the order of its keys), and the block holding that position is copied on
+ * write first when it is shared.  pa_seq_num_tokens gives the cached tokens,
+ * min(seen, num_sinks + window) — the context length to attend.  All or
+ * nothing; PA_ERR_INVALID for a negative count, window <= 0 or too many
+ * tokens. */
+pa_status pa_seq_create_streaming(pa_allocator* a, int64_t seq_id, int32_t num_sinks, int32_t window,
+                                  int32_t num_tokens);
+
 /* ------------------------------------------------------------------ prefix caching
  * Reuse of the pages of equal prompt prefixes ("大模型部署.md" §2.1 item 3,
  * CachedBlockAllocator and LRUEvictor; "【自用】AI infra相关" part 二.4(2)).

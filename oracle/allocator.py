@@ -400,3 +400,83 @@ class PrefixCachingAllocator(Allocator):
         self.tokens.pop(seq, None)
         for b in tab:
             self._release(b)
+
+
+def streaming_append_position(seen: int, sinks: int, window: int) -> int:
+    """Cache position of the token that raises a streaming sequence from `seen` to seen + 1
+    tokens ("第 15 章：推理引擎与部署" §15.4, StreamingLLM: the first `sinks` tokens are
+    kept, then only the most recent `window`).  The cache holds at most sinks + window
+    tokens at positions 0 .. sinks + window - 1: the first sinks + window tokens take
+    them in order; after that, token `seen` replaces the oldest window token, which sits
+    at position sinks + (seen - sinks) mod window (a ring over the window positions).
+    Attention is the same for any order of its keys, so the ring needs no reordering."""
+    if seen < sinks + window:
+        return seen
+    return sinks + (seen - sinks) % window
+
+
+class StreamingMixin:
+    """Streaming sequences (sink tokens + sliding window) on the ref-counted allocator.
+
+    * ``create_streaming(seq, sinks, window, n)``: n <= sinks + window tokens at
+      positions 0 .. n-1, ⌈n/P⌉ blocks (the caller keeps a longer prompt's sinks
+      and its last tokens).
+    * ``append_streaming(seq)``: the new token's position is
+      ``streaming_append_position``; while the cache grows, as ``append_slot``
+      (a new block when the table is one short, copy-on-write of a shared last
+      block); once full, the token overwrites a window position, and the block
+      holding it is copied first when it is shared (copy-on-write of any block,
+      not only the last).
+    * ``num_tokens`` of a streaming sequence is the number of cached tokens,
+      min(seen, sinks + window): the attention context length.
+    """
+
+    def _streaming_init(self):
+        self.stream = {}   # seq -> [sinks, window, seen]
+
+    def create_streaming(self, seq, sinks: int, window: int, n_tokens: int) -> None:
+        if sinks < 0 or window <= 0 or n_tokens < 0 or n_tokens > sinks + window:
+            raise ValueError("bad streaming parameters")
+        self.create(seq, n_tokens)
+        self.stream[seq] = [sinks, window, n_tokens]
+
+    def append_streaming(self, seq):
+        if seq not in self.tables:
+            raise KeyError("unknown sequence")
+        if seq not in self.stream:
+            raise ValueError("not a streaming sequence")
+        sinks, window, seen = self.stream[seq]
+        cap = sinks + window
+        if seen < cap:
+            slot, cow = self.append_slot(seq)
+        else:
+            pos = streaming_append_position(seen, sinks, window)
+            tab = self.tables[seq]
+            j = pos // self.P
+            cow = None
+            if self.ref[tab[j]] > 1:
+                if self.num_free() == 0:
+                    raise NoBlocks("no free block for copy-on-write")
+                old = tab[j]
+                new = self._pop()
+                self.ref[old] -= 1
+                tab[j] = new
+                cow = (old, new)
+            slot = tab[j] * self.P + pos % self.P
+        self.stream[seq][2] = seen + 1
+        return slot, cow
+
+    def fork(self, parent, child) -> None:
+        super().fork(parent, child)
+        if parent in self.stream:
+            self.stream[child] = list(self.stream[parent])
+
+    def free_seq(self, seq) -> None:
+        super().free_seq(seq)
+        self.stream.pop(seq, None)
+
+
+class StreamingAllocator(StreamingMixin, Allocator):
+    def __init__(self, *a, **k):
+        super().__init__(*a, **k)
+        self._streaming_init()

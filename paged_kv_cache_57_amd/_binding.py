@@ -72,6 +72,7 @@ _SIGS = {
     "pa_seq_block_table": (_i32, [_vp, _i64, _vp, _i32, _pi32]),
     "pa_seq_block_tables": (_i32, [_vp, _i32, _vp, _vp, _i32]),
     "pa_seq_free": (_i32, [_vp, _i64]),
+    "pa_seq_create_streaming": (_i32, [_vp, _i64, _i32, _i32, _i32]),
     "pa_alloc_enable_prefix_caching": (_i32, [_vp]),
     "pa_alloc_num_evictable": (_i32, [_vp]),
     "pa_seq_create_tokens": (_i32, [_vp, _i64, _vp, _i32, _vp]),
@@ -353,6 +354,10 @@ class Allocator:
 
     def free(self, seq_id: int):
         _check(_lib.pa_seq_free(self._h, seq_id))
+
+    def create_streaming(self, seq_id: int, num_sinks: int, window: int, num_tokens: int):
+        """A sequence keeping its first num_sinks tokens and its last `window` tokens."""
+        _check(_lib.pa_seq_create_streaming(self._h, seq_id, num_sinks, window, num_tokens))
 
     # prefix caching
     def enable_prefix_caching(self):

@@ -40,6 +40,9 @@ struct pa_allocator {
     bool hashed = false;            // made from token ids on a caching allocator
     std::vector<int32_t> tokens;    // all tokens (hashed sequences)
     std::vector<uint64_t> chain;    // hash of every full block, in order (hashed sequences)
+    int32_t sinks = -1;             // streaming sequences (sinks >= 0): sink tokens kept,
+    int32_t window = 0;             // then the most recent `window` tokens;
+    int64_t seen = 0;               // tokens appended so far (ntok stops at sinks + window)
   };
   int32_t num_blocks = 0;
   int32_t block_size = 16;
@@ -281,6 +284,29 @@ pa_status pa_seq_append_slot(pa_allocator* a, int64_t seq_id, int64_t* slot_out,
   if (s.hashed)
     return fail(PA_ERR_INVALID, "pa_seq_append_slot: sequence %lld was made from token ids: use pa_seq_append_tokens",
                 (long long)seq_id);
+  if (s.sinks >= 0 && s.seen >= (int64_t)s.sinks + s.window) {
+    // a full streaming cache: the new token replaces the oldest window token (a ring over the
+    // window positions; attention does not depend on the order of its keys)
+    const int64_t pos = s.sinks + (s.seen - s.sinks) % s.window;
+    const int64_t j = pos / a->block_size;
+    int32_t src = -1, dst = -1;
+    if (a->ref[s.table[j]] > 1) {
+      if (a->available() == 0)
+        return fail(PA_ERR_NO_BLOCKS, "pa_seq_append_slot: no free block for copy-on-write");
+      a->clock += 1;
+      src = s.table[j];
+      dst = a->take();
+      a->ref[src] -= 1;  // > 1 before, so still held by another sequence
+      s.table[j] = dst;
+    } else {
+      a->clock += 1;
+    }
+    s.seen += 1;
+    *slot_out = (int64_t)s.table[j] * a->block_size + pos % a->block_size;
+    *cow_src = src;
+    *cow_dst = dst;
+    return ok();
+  }
   const int64_t L = s.ntok;
   if (L >= INT32_MAX) return fail(PA_ERR_INVALID, "pa_seq_append_slot: sequence too long");
   const int64_t need = a->blocks_for(L + 1);
@@ -305,9 +331,26 @@ pa_status pa_seq_append_slot(pa_allocator* a, int64_t seq_id, int64_t* slot_out,
     a->clock += 1;
   }
   s.ntok = (int32_t)(L + 1);
+  if (s.sinks >= 0) s.seen += 1;
   *slot_out = (int64_t)s.table[L / a->block_size] * a->block_size + L % a->block_size;
   *cow_src = src;
   *cow_dst = dst;
+  return ok();
+}
+
+pa_status pa_seq_create_streaming(pa_allocator* a, int64_t seq_id, int32_t num_sinks, int32_t window,
+                                  int32_t num_tokens) {
+  if (!a) return fail(PA_ERR_INVALID, "pa_seq_create_streaming: NULL allocator");
+  if (num_sinks < 0 || window <= 0 || (int64_t)num_sinks + window > INT32_MAX || num_tokens < 0 ||
+      (int64_t)num_tokens > (int64_t)num_sinks + window)
+    return fail(PA_ERR_INVALID, "pa_seq_create_streaming: sinks %d, window %d, %d tokens", num_sinks, window,
+                num_tokens);
+  pa_status st = pa_seq_create(a, seq_id, num_tokens);
+  if (st != PA_OK) return st;
+  auto& s = a->seqs.find(seq_id)->second;
+  s.sinks = num_sinks;
+  s.window = window;
+  s.seen = num_tokens;
   return ok();
 }
 

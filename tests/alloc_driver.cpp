@@ -13,6 +13,7 @@
 //   ctok id t0 t1 ...   -> pa_seq_create_tokens                      prints status cached
 //   atok id t           -> pa_seq_append_tokens (one sequence)       prints status slot src dst
 //   nevict              -> pa_alloc_num_evictable                    prints count
+//   stream id k w n     -> pa_seq_create_streaming                   prints status
 #include <cstdio>
 #include <iostream>
 #include <sstream>
@@ -94,6 +95,11 @@ int main() {
       int32_t pair[2] = {-1, -1}, ncow = 0;
       int st = pa_seq_append_tokens(a, 1, &sid, &t, &slot, pair, &ncow);
       std::printf("%d %lld %d %d\n", st, (long long)slot, ncow ? pair[0] : -1, ncow ? pair[1] : -1);
+    } else if (op == "stream") {
+      long long id;
+      int k, w, n;
+      in >> id >> k >> w >> n;
+      std::printf("%d\n", pa_seq_create_streaming(a, id, k, w, n));
     } else if (op == "nevict") {
       std::printf("%d\n", pa_alloc_num_evictable(a));
     }

@@ -552,6 +552,71 @@ def test_shared_prefix_forward(pa, case):
     assert (np.abs(got - plain) <= a + rr * np.abs(plain)).all()
 
 
+def test_streaming_sequences_attention(pa):
+    """Attention sinks + sliding window (k = 4, w = 100): tokens stream through the
+    allocator's slots into the pool; a second sequence forks at token 120 and goes on
+    by itself (its first overwrite of the shared pages copies them).  At checkpoints one
+    decode row per sequence attends its cache, compared with the oracle over exactly the
+    sink tokens and the last w tokens of that sequence (kept on the host, independent
+    of where the pages put them)."""
+    from oracle import attention as oattn
+    from tests._gpu import TOL
+    H, d, k, w, NB = 8, 128, 4, 100, 64
+    ks, vs = W.cache_shapes(NB, H, d, "bf16")
+    gen = torch.Generator(device=DEV).manual_seed(9)
+    kc = W.fill_normal(torch.empty(ks, dtype=torch.bfloat16, device=DEV), gen)
+    vc = W.fill_normal(torch.empty(vs, dtype=torch.bfloat16, device=DEV), gen)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    alloc = pa.Allocator(NB, 16)
+    alloc.create_streaming(0, k, w, 0)
+    hist = {0: []}                                   # per sequence: host bf16 bits of every token's (K, V)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    a, r = TOL["bf16"]
+    worst = 0.0
+    for t in range(320):
+        if t == 120:
+            alloc.fork(0, 1)
+            hist[1] = list(hist[0])
+        for sq in sorted(hist):
+            slot, cow = alloc.append_slot(sq)
+            if cow:
+                pa.pa_copy_blocks(kc, vc, torch.tensor([cow], dtype=torch.int32, device=DEV), status)
+            kn = W.fill_normal(torch.empty((1, H, d), dtype=torch.bfloat16, device=DEV), gen)
+            vn = W.fill_normal(torch.empty((1, H, d), dtype=torch.bfloat16, device=DEV), gen)
+            pa.pa_reshape_and_cache(kn, vn, kc, vc, torch.tensor([slot], dtype=torch.int64, device=DEV), status)
+            hist[sq].append((host_raw(kn)[0], host_raw(vn)[0]))
+        if t in (50, 103, 104, 121, 200, 319):
+            for sq in sorted(hist):
+                n = len(hist[sq])
+                L = alloc.num_tokens(sq)
+                assert L == min(n, k + w)
+                tab = alloc.block_tables([sq], (k + w + 15) // 16)
+                q = W.fill_normal(torch.empty((1, H, d), dtype=torch.bfloat16, device=DEV), gen)
+                nbytes = pa.pa_forward_workspace_bytes(1, 1, 1, H, H, d, L, pa.PA_BF16)
+                ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=DEV)
+                out = torch.empty_like(q)
+                pa.pa_forward(out, q, kc, vc, torch.from_numpy(tab).to(DEV),
+                              torch.tensor([L], dtype=torch.int32, device=DEV),
+                              torch.tensor([0, 1], dtype=torch.int32, device=DEV), 1, L, scale, ws, status)
+                torch.cuda.synchronize()
+                assert int(status.item()) == 0
+                kept = list(range(min(k, n))) + list(range(max(min(k, n), n - w), n))
+                K = np.stack([hist[sq][i][0] for i in kept])
+                V = np.stack([hist[sq][i][1] for i in kept])
+                ref = oattn.attend_sequence(to_f64_bits(host_raw(q)), to_f64_bits(K), to_f64_bits(V), scale)
+                got = to_f64(out)
+                ratio = float((np.abs(got - ref) / (a + r * np.abs(ref))).max())
+                worst = max(worst, ratio)
+                assert np.isfinite(got).all() and ratio <= 1.0, (t, sq, ratio)
+    say(f"[case] streaming sinks+window: worst err/bound {worst:.3f}")
+    alloc.close()
+
+
+def to_f64_bits(bits):
+    from oracle import layout
+    return layout.to_f64(bits, "bf16")
+
+
 def read_probe_case():
     """Pages, a page list with one id outside the pool, and the sink the documented
     thread assignment gives: wavefront w XORs piece l, l+64, l+128, l+192 of its
