@@ -321,39 +321,50 @@ def sampling_workflow(torch, pa, W, dev, args):
         nbytes = pa.pa_forward_workspace_bytes(n, n, 1, H, H, d, max_ctx, pa.PA_BF16)
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((n, H, d), dtype=torch.bfloat16, device=dev)
-    # pinned upload buffers, one set per step, so no copy waits for the device
-    up_slots = torch.empty((total, n), dtype=torch.int64).pin_memory()
-    up_tab = torch.empty((total, n * cap_max), dtype=torch.int32).pin_memory()
-    up_lens = torch.empty((total, n), dtype=torch.int32).pin_memory()
-    up_pairs = torch.empty((total, 2 * n), dtype=torch.int32).pin_memory()
-    stream = torch.cuda.current_stream(dev).cuda_stream
+    # One upload per step: slots (int64), context lengths, block tables and copy pairs (int32)
+    # staged in a pinned region of their own for every step (no copy waits for the device) and
+    # copied into one device buffer (stream order keeps a step's copy behind the last step's kernels).
+    o_lens = 8 * n
+    o_pairs = o_lens + 4 * n
+    o_tab = o_pairs + 8 * n
+    stride = o_tab + 4 * n * cap_max
+    up = torch.empty((total, stride), dtype=torch.uint8).pin_memory()
+    dbuf = torch.empty(stride, dtype=torch.uint8, device=dev)
+    d_slots = dbuf[:o_lens].view(torch.int64)
+    d_lens = dbuf[o_lens:o_pairs].view(torch.int32)
+    d_pairs = dbuf[o_pairs:o_tab].view(torch.int32).view(n, 2)
+    d_tab = dbuf[o_tab:].view(torch.int32)
+    cur = torch.cuda.current_stream(dev)
+    stream = cur.cuda_stream
     ev = HipEvents()
     fwd_ev = ev.new(2 * total)
     logical = []
+    scale = 1.0 / np.sqrt(d)
     torch.cuda.synchronize()
 
     def decode_step(i, record):
         sl, pairs = alloc.append_slots(ids)
         lens[:] += 1
-        cap = (int(lens.max()) + 15) // 16
+        L = int(lens.max())
+        cap = (L + 15) // 16
         tab = alloc.block_tables(ids, cap)
-        up_slots[i].numpy()[:] = sl
-        up_lens[i].numpy()[:] = lens
-        up_tab[i].numpy()[:n * cap] = tab.reshape(-1)
+        h = up[i].numpy()
+        h[:o_lens].view(np.int64)[:] = sl
+        h[o_lens:o_pairs].view(np.int32)[:] = lens
+        h[o_tab:o_tab + 4 * n * cap].view(np.int32)[:] = tab.reshape(-1)
         if len(pairs):
-            pr = up_pairs[i, :2 * len(pairs)]
-            pr.numpy()[:] = np.asarray(pairs, np.int32).reshape(-1)
-            pa.pa_copy_blocks(kc, vc, pr.to(dev, non_blocking=True).view(-1, 2), status)
-        pa.pa_reshape_and_cache(kst[i], vst[i], kc, vc, up_slots[i].to(dev, non_blocking=True), status)
-        tables = up_tab[i, :n * cap].to(dev, non_blocking=True).view(n, cap)
+            h[o_pairs:o_pairs + 8 * len(pairs)].view(np.int32)[:] = np.asarray(pairs, np.int32).reshape(-1)
+        dbuf.copy_(up[i], non_blocking=True)
+        if len(pairs):
+            pa.pa_copy_blocks(kc, vc, d_pairs[:len(pairs)], status, cur)
+        pa.pa_reshape_and_cache(kst[i], vst[i], kc, vc, d_slots, status, cur)
+        tables = d_tab[:n * cap].view(n, cap)
         if record:
             ev.record(fwd_ev[2 * i], stream)
         if cascade:
-            pa.pa_forward_shared(out, qs[i], kc, vc, tables, up_lens[i].to(dev, non_blocking=True), qsl, groups, 1,
-                                 int(lens.max()), 1.0 / np.sqrt(d), ws, status)
+            pa.pa_forward_shared(out, qs[i], kc, vc, tables, d_lens, qsl, groups, 1, L, scale, ws, status, cur)
         else:
-            pa.pa_forward(out, qs[i], kc, vc, tables, up_lens[i].to(dev, non_blocking=True), qsl, 1,
-                          int(lens.max()), 1.0 / np.sqrt(d), ws, status)
+            pa.pa_forward(out, qs[i], kc, vc, tables, d_lens, qsl, 1, L, scale, ws, status, cur)
         if record:
             ev.record(fwd_ev[2 * i + 1], stream)
             logical.append(int(lens.sum()))
