@@ -36,6 +36,8 @@ def build(verbose: bool = False) -> str:
         cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".hip"):
             cmd[1:1] = ["-x", "hip", *DEVICE_FLAGS]
+        else:
+            cmd[1:1] = ["-x", "c++"]  # host code only: no device pass
         _run(cmd, verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"
