@@ -16,9 +16,12 @@ Page titles used in citations:
 * "第7章：大模型部署实战", §2.1 (KV-cache size), §2.2.1 (block allocation),
   §2.2.2 (attention over blocks), §2.3 (BlockManager).
 * "第 15 章：推理引擎与部署", §15.1 "算法详解" (online softmax) and its Python
-  simulation, §15.6 "PagedAttention：分页 KV Cache", "KV Cache 大小计算",
+  simulation, §15.3 (RoPE fused with attention), §15.4 (Attention Sink,
+  StreamingLLM), §15.6 "PagedAttention：分页 KV Cache", "KV Cache 大小计算",
   "两阶段与 Chunked Prefill".
+* "大模型部署.md" §2.1 item 3 also for CachedBlockAllocator and LRUEvictor, and
+  "【自用】AI infra相关" part 二.4(2) (prefix caching by block hashes).
 
 Parity status of each function is stated in its module header.
 """
-from . import layout, attention, online_softmax, cache_ops, allocator, sizes  # noqa: F401
+from . import layout, attention, online_softmax, cache_ops, allocator, sizes, rope, splitfuse  # noqa: F401
