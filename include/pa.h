@@ -397,6 +397,64 @@ pa_status pa_sf_finish(pa_splitfuse* c, int64_t seq_id);
 pa_status pa_sf_step(pa_splitfuse* c, int32_t cap, int64_t* seq_ids, int32_t* q_lens, int32_t* context_lens,
                      int32_t* num_rows_out, int32_t* num_tokens_out);
 
+/* ------------------------------------------------------------------ decode step
+ * One decode step of num_seqs sequences with one new token each, driven from
+ * the host allocator (parallel sampling: "大模型部署.md" §2.1 items 3-4,
+ * append_slots returning the copy-on-write pairs, pages shared between the
+ * samples of a prompt): pa_seq_append_slots for every sequence, then one
+ * upload of the step's slots, context lengths, query starts, copy pairs and
+ * block tables, pa_copy_blocks of the reported pairs, pa_reshape_and_cache of
+ * the new keys and values, and pa_forward (pa_forward_shared when groups are
+ * given) for one query row per sequence — all enqueued on `stream`, the
+ * operations the caller would otherwise issue one by one.
+ *
+ * Staging layout (offsets in bytes, n = num_seqs, c = table columns):
+ *   slots int64 [n] at 0; context lengths int32 [n] at 8n; query starts int32
+ *   [n + 1] at 12n; copy pairs int32 [n][2] at P = 16n + 4 rounded up to a
+ *   multiple of 8; block tables int32 [n][c] at P + 8n, padded with -1.
+ * Bytes needed for tables of up to max_blocks_per_seq columns (0 for a
+ * non-positive argument): */
+size_t pa_decode_step_staging_bytes(int32_t num_seqs, int32_t max_blocks_per_seq);
+/* Host half: appends one slot to each sequence (in order) and writes the
+ * staging layout above into host_staging (host, 8-byte aligned, at least
+ * pa_decode_step_staging_bytes(num_seqs, max_blocks_per_seq) bytes), with
+ * c = ceil(longest context / 16) columns.  Out: *num_cow_out copy pairs,
+ * *max_context_len_out, *table_cols_out = c, *used_bytes_out = bytes of the
+ * layout for c columns.  Unknown sequences and a sequence whose table would
+ * exceed max_blocks_per_seq fail before the allocator changes; an exhausted
+ * pool fails as pa_seq_append_slots (the sequences before the failing one
+ * keep their new slot). */
+pa_status pa_decode_step_stage(pa_allocator* a, int32_t num_seqs, const int64_t* seq_ids,
+                               int32_t max_blocks_per_seq, void* host_staging, size_t staging_bytes,
+                               int32_t* num_cow_out, int32_t* max_context_len_out, int32_t* table_cols_out,
+                               size_t* used_bytes_out);
+/* The whole step.  pa_decode_step_stage into host_staging, then hipMemcpyAsync
+ * of the used bytes into dev_staging and the three launches on `stream`.
+ *   seq_ids        host, int64 [num_seqs]; row i of q / new_key / new_value / out
+ *                  is sequence seq_ids[i]
+ *   q, out         device, [num_seqs][num_q_heads][head_dim] of dtype
+ *   new_key, new_value  device, [num_seqs][num_kv_heads][head_dim] of dtype
+ *   k_cache, v_cache    device, pool layout above, num_blocks blocks
+ *   groups         device, int32 [num_groups][3] as in pa_forward_shared, or
+ *                  NULL with num_groups 0 (plain pa_forward)
+ *   host_staging   host, pinned (hipHostMalloc) for an asynchronous copy; it
+ *                  must not be rewritten before the copy has run: give each
+ *                  step in flight a region of its own, or synchronise
+ *   dev_staging    device, 8-byte aligned, staging_bytes bytes (both buffers
+ *                  are at least pa_decode_step_staging_bytes(num_seqs,
+ *                  max_blocks_per_seq))
+ *   workspace      device, 256-byte aligned, at least the workspace bytes of
+ *                  pa_forward (pa_forward_shared with groups) for num_seqs
+ *                  single-row sequences of up to 16 x max_blocks_per_seq keys
+ * Argument errors are reported before the allocator changes; a HIP error of
+ * the upload returns PA_ERR_HIP after the allocator has advanced. */
+pa_status pa_decode_step(pa_allocator* a, int32_t num_seqs, const int64_t* seq_ids, void* out, const void* q,
+                         const void* new_key, const void* new_value, void* k_cache, void* v_cache,
+                         int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                         pa_dtype dtype, float scale, const int32_t* groups, int32_t num_groups,
+                         int32_t max_blocks_per_seq, void* host_staging, void* dev_staging, size_t staging_bytes,
+                         void* workspace, size_t workspace_bytes, int32_t* dev_status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -82,6 +82,10 @@ _SIGS = {
     "pa_sf_add_prompt": (_i32, [_vp, _i64, _i32]),
     "pa_sf_finish": (_i32, [_vp, _i64]),
     "pa_sf_step": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "pa_decode_step_staging_bytes": (_sz, [_i32, _i32]),
+    "pa_decode_step_stage": (_i32, [_vp, _i32, _vp, _i32, _vp, _sz, _pi32, _pi32, _pi32, ctypes.POINTER(_sz)]),
+    "pa_decode_step": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
+                              _vp, _i32, _i32, _vp, _vp, _sz, _vp, _sz, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -429,3 +433,51 @@ class SplitFuse:
             if rows.value <= cap:
                 _check(st)
             cap = rows.value
+
+
+# ---------------------------------------------------------------- decode step
+
+def pa_decode_step_staging_bytes(num_seqs: int, max_blocks_per_seq: int) -> int:
+    return int(_lib.pa_decode_step_staging_bytes(num_seqs, max_blocks_per_seq))
+
+
+def pa_decode_step_stage(alloc, seq_ids, max_blocks_per_seq: int, host_staging):
+    """Host half of a decode step into host_staging (a uint8 numpy array or CPU tensor).
+    Returns (num_cow, max_context_len, table_cols, used_bytes)."""
+    ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+    buf = host_staging.numpy() if hasattr(host_staging, "numpy") else host_staging
+    ncow, mx, cols, used = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_size_t()
+    _check(_lib.pa_decode_step_stage(alloc._h, len(ids), _np_ptr(ids), max_blocks_per_seq, _np_ptr(buf), buf.nbytes,
+                                     ctypes.byref(ncow), ctypes.byref(mx), ctypes.byref(cols), ctypes.byref(used)))
+    return ncow.value, mx.value, cols.value, used.value
+
+
+def pa_decode_step(alloc, seq_ids, out, q, new_key, new_value, k_cache, v_cache, scale, max_blocks_per_seq,
+                   host_staging, dev_staging, workspace, groups=None, dev_status=None, stream=None):
+    """One decode step driven from the allocator (see pa.h): host_staging is a uint8
+    CPU tensor (pinned: the upload is then asynchronous; each step in flight needs
+    its own), dev_staging a uint8 device tensor at least as large."""
+    import torch
+    nb, hkv, d, blk = _pool_dims(k_cache, v_cache)
+    ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+    n, hq, dq = q.shape
+    if n != len(ids) or dq != d or tuple(out.shape) != (n, hq, d):
+        raise PAError(PA_ERR_INVALID, "q/out must be [num_seqs, num_q_heads, head_dim]")
+    if tuple(new_key.shape) != (n, hkv, d) or tuple(new_value.shape) != (n, hkv, d):
+        raise PAError(PA_ERR_INVALID, "new_key/new_value must be [num_seqs, num_kv_heads, head_dim]")
+    if not isinstance(host_staging, torch.Tensor) or host_staging.device.type != "cpu":
+        raise PAError(PA_ERR_INVALID, "host_staging must be a CPU tensor (pinned, for an asynchronous upload)")
+    nbytes = host_staging.numel() * host_staging.element_size()
+    if dev_staging.numel() * dev_staging.element_size() < nbytes:
+        raise PAError(PA_ERR_INVALID, "dev_staging is smaller than host_staging")
+    ng = 0 if groups is None else groups.shape[0]
+    if groups is not None and (groups.dim() != 2 or groups.shape[1] != 3):
+        raise PAError(PA_ERR_INVALID, "groups must be [num_groups, 3]")
+    _check(_lib.pa_decode_step(
+        alloc._h, n, _np_ptr(ids), _dev(out, "out", q.dtype), _dev(q, "q", k_cache.dtype),
+        _dev(new_key, "new_key", k_cache.dtype), _dev(new_value, "new_value", k_cache.dtype),
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), nb, hq, hkv, d, _dtype_code(q), float(scale),
+        _dev(groups, "groups", torch.int32) if ng else None, ng, int(max_blocks_per_seq),
+        ctypes.c_void_p(host_staging.data_ptr()), _dev(dev_staging, "dev_staging"), nbytes,
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _dev(dev_status, "dev_status", torch.int32), _stream(q, stream)))

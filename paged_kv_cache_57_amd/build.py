@@ -14,8 +14,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_status.cpp", "pa_alloc.cpp", "pa_splitfuse.cpp", "pa_cache.hip", "pa_attention.hip"]
-HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+SOURCES = ["pa_status.cpp", "pa_alloc.cpp", "pa_splitfuse.cpp", "pa_step.cpp", "pa_cache.hip", "pa_attention.hip"]
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+HIPCC = os.environ.get("HIPCC", os.path.join(ROCM, "bin", "hipcc"))
 # No packed FP32 instructions; and no atomic optimizer, which wraps each atomic in a
 # branch on the first active lane (the kernels keep their work loops free of
 # lane-dependent branches).
@@ -37,7 +38,8 @@ def build(verbose: bool = False) -> str:
         if src.endswith(".hip"):
             cmd[1:1] = ["-x", "hip", *DEVICE_FLAGS]
         else:
-            cmd[1:1] = ["-x", "c++"]  # host code only: no device pass
+            # host code only: no device pass (the HIP runtime API header for the upload of a step)
+            cmd[1:1] = ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I" + os.path.join(ROCM, "include")]
         _run(cmd, verbose)
         objs.append(obj)
     tmp = LIB + ".tmp"

@@ -647,3 +647,91 @@ def test_read_pages_probe(pa):
     torch.cuda.synchronize()
     assert int(status.item()) == pa.PA_DEV_BAD_BLOCK
     assert np.array_equal(sink.cpu().numpy().view(np.uint32), want)
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_decode_step_native(pa, shared):
+    """pa_decode_step (allocator + one upload + copy + cache write + attention in one
+    call) against the same step composed from the single entry points on a twin pool
+    and allocator: outputs and pool bytes bit-identical every step (the same kernels
+    on the same inputs); the last step's rows also against the oracle on a host copy
+    of the pool.  4 prompts x 4 branches (copy-on-write of the shared partial page),
+    40 steps, 8 heads of 128, with (shared=True) the prompts' full pages as
+    shared-prefix groups."""
+    from oracle import attention as oattn
+    spec = W.parallel_sampling_spec(3, prompts=4, lo=100, hi=600, branches=4, steps=40, num_blocks=512,
+                                    heads=8, head_dim=128)
+    P, B, NB, H, d = len(spec.prompt_lens), spec.branches, spec.num_blocks, spec.heads, spec.head_dim
+    say(f"[case] native decode step shared={shared}: prompts {list(spec.prompt_lens)} x {B}, NB={NB}")
+    ks, vs = W.cache_shapes(NB, H, d, "bf16")
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    kc_a = W.fill_normal(torch.empty(ks, dtype=torch.bfloat16, device=DEV), gen)
+    vc_a = W.fill_normal(torch.empty(vs, dtype=torch.bfloat16, device=DEV), gen)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    allocs = [pa.Allocator(NB, 16, 0.0, spec.initial_free_order) for _ in range(2)]
+    ids = [p * B + b for p in range(P) for b in range(B)]
+    n = len(ids)
+    for al in allocs:
+        for p, L in enumerate(spec.prompt_lens):
+            al.create(p * B, int(L))
+    slots = np.concatenate([allocs[0].slots(p * B, 0, int(L)) for p, L in enumerate(spec.prompt_lens)])
+    knew = W.fill_normal(torch.empty((len(slots), H, d), dtype=torch.bfloat16, device=DEV), gen)
+    vnew = W.fill_normal(torch.empty((len(slots), H, d), dtype=torch.bfloat16, device=DEV), gen)
+    pa.pa_reshape_and_cache(knew, vnew, kc_a, vc_a, torch.from_numpy(slots.astype(np.int64)).to(DEV), status)
+    kc_b, vc_b = kc_a.clone(), vc_a.clone()
+    for al in allocs:
+        for p in range(P):
+            for b in range(1, B):
+                al.fork(p * B, p * B + b)
+    mbps = (int(spec.prompt_lens.max()) + spec.steps + 15) // 16
+    groups = None
+    if shared:
+        groups = torch.tensor([[p * B, B, 16 * (int(L) // 16)] for p, L in enumerate(spec.prompt_lens)],
+                              dtype=torch.int32, device=DEV)
+        nbytes = pa.pa_forward_shared_workspace_bytes(n, P, n, 1, H, H, d, 16 * mbps, pa.PA_BF16)
+    else:
+        nbytes = pa.pa_forward_workspace_bytes(n, n, 1, H, H, d, 16 * mbps, pa.PA_BF16)
+    ws_a = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    ws_b = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    sb = pa.pa_decode_step_staging_bytes(n, mbps)
+    host = torch.empty(sb, dtype=torch.uint8).pin_memory()
+    dev = torch.empty(sb, dtype=torch.uint8, device=DEV)
+    qsl = torch.arange(n + 1, dtype=torch.int32, device=DEV)
+    scale = 1.0 / np.sqrt(d)
+    out_a = torch.empty((n, H, d), dtype=torch.bfloat16, device=DEV)
+    out_b = torch.empty_like(out_a)
+    copies = 0
+    for step in range(spec.steps):
+        q = W.fill_normal(torch.empty((n, H, d), dtype=torch.bfloat16, device=DEV), gen)
+        kn = W.fill_normal(torch.empty((n, H, d), dtype=torch.bfloat16, device=DEV), gen)
+        vn = W.fill_normal(torch.empty((n, H, d), dtype=torch.bfloat16, device=DEV), gen)
+        # composed: the single entry points one by one
+        sl, pairs = allocs[0].append_slots(ids)
+        if len(pairs):
+            pa.pa_copy_blocks(kc_a, vc_a, torch.from_numpy(pairs).to(DEV), status)
+            copies += len(pairs)
+        pa.pa_reshape_and_cache(kn, vn, kc_a, vc_a, torch.from_numpy(sl).to(DEV), status)
+        lens = np.array([allocs[0].num_tokens(s) for s in ids], np.int32)
+        L = int(lens.max())
+        tab = torch.from_numpy(allocs[0].block_tables(ids, (L + 15) // 16)).to(DEV)
+        dl = torch.from_numpy(lens).to(DEV)
+        if shared:
+            pa.pa_forward_shared(out_a, q, kc_a, vc_a, tab, dl, qsl, groups, 1, L, scale, ws_a, status)
+        else:
+            pa.pa_forward(out_a, q, kc_a, vc_a, tab, dl, qsl, 1, L, scale, ws_a, status)
+        # native: one call
+        pa.pa_decode_step(allocs[1], ids, out_b, q, kn, vn, kc_b, vc_b, scale, mbps, host, dev, ws_b,
+                          groups=groups, dev_status=status)
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, step
+        assert torch.equal(out_a.view(torch.int16), out_b.view(torch.int16)), f"outputs differ at step {step}"
+    assert copies > 0
+    assert torch.equal(kc_a.view(torch.int16), kc_b.view(torch.int16))
+    assert torch.equal(vc_a.view(torch.int16), vc_b.view(torch.int16))
+    kh, vh = host_raw(kc_b), host_raw(vc_b)
+    lens = np.array([allocs[1].num_tokens(s) for s in ids], np.int32)
+    tables = allocs[1].block_tables(ids, (int(lens.max()) + 15) // 16)
+    ref = oattn.paged_attention(host_raw(q), kh, vh, tables, lens, np.arange(n + 1, dtype=np.int32),
+                                float(np.float32(scale)), "bf16")
+    assert_close(to_f64(out_b), ref, "bf16", "native decode step, last step")
+    say(f"  {spec.steps} steps bit-identical to the composed calls; copy-on-write pairs {copies}")
