@@ -16,7 +16,9 @@ inputs resident in device memory before timing starts:
   prompt pages, copy-on-write, 64 decode rows per step); value = decode
   tokens per second over the timed steps, allocator and uploads included.
   --shared-prefix attends with pa_forward_shared (a prompt's pages are read
-  once for its four branches).
+  once for its four branches).  A step is one pa_decode_step call (allocator,
+  one upload, copies, cache write and attention); --composed-step issues the
+  same operations one by one from Python.
 * splitfuse_rope: the same pass with the rotary embedding fused into the cache
   write (pa_rope_reshape_and_cache rotates q and the new keys at their
   positions; the forward reads the rotated q).
@@ -281,11 +283,14 @@ def sampling_workflow(torch, pa, W, dev, args):
     appends one token per branch in the host allocator, copies the pages it
     reports (copy-on-write of a shared partial page), writes the 64 new K/V
     through their slots and runs attention for the 64 rows.  warmup + steps
-    decode steps in all (256 by default), the last `steps` timed, host allocator
-    work and the per-step uploads of slots and tables included."""
+    decode steps are timed by the wall clock (host allocator work and uploads
+    included), then EVENT_STEPS more steps run with HIP events around the
+    forward's stages for its device time.  A step is one pa_decode_step call;
+    with --composed-step, the same operations issued one by one from Python."""
+    EVENT_STEPS = 16
     spec = W.parallel_sampling_spec(0)
     P, B, NB, H, d = len(spec.prompt_lens), spec.branches, spec.num_blocks, spec.heads, spec.head_dim
-    total = args.warmup + args.steps
+    total = args.warmup + args.steps + EVENT_STEPS
     n = P * B
     ks, vs = W.cache_shapes(NB, H, d, "bf16")
     gen = torch.Generator(device=dev).manual_seed(0)
@@ -312,81 +317,83 @@ def sampling_workflow(torch, pa, W, dev, args):
     cap_max = (max_ctx + 15) // 16
     qsl = torch.arange(n + 1, dtype=torch.int32, device=dev)
     cascade = args.shared_prefix
+    groups = None
     if cascade:
         # each prompt's branches (consecutive sequences) share its full pages
         groups = torch.tensor([[p * B, B, 16 * (int(L) // 16)] for p, L in enumerate(spec.prompt_lens)],
                               dtype=torch.int32, device=dev)
-        nbytes = pa.pa_forward_shared_workspace_bytes(n, P, n, 1, H, H, d, max_ctx, pa.PA_BF16)
+        nbytes = pa.pa_forward_shared_workspace_bytes(n, P, n, 1, H, H, d, 16 * cap_max, pa.PA_BF16)
     else:
-        nbytes = pa.pa_forward_workspace_bytes(n, n, 1, H, H, d, max_ctx, pa.PA_BF16)
+        nbytes = pa.pa_forward_workspace_bytes(n, n, 1, H, H, d, 16 * cap_max, pa.PA_BF16)
     ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((n, H, d), dtype=torch.bfloat16, device=dev)
-    # One upload per step: slots (int64), context lengths, block tables and copy pairs (int32)
-    # staged in a pinned region of their own for every step (no copy waits for the device) and
-    # copied into one device buffer (stream order keeps a step's copy behind the last step's kernels).
-    o_lens = 8 * n
-    o_pairs = o_lens + 4 * n
-    o_tab = o_pairs + 8 * n
-    stride = o_tab + 4 * n * cap_max
+    # Every step stages its slots, context lengths, tables and copy pairs in a
+    # pinned region of its own (no copy waits for the device) and uploads them
+    # into one device buffer (stream order keeps a step's copy behind the last
+    # step's kernels): the staging layout of pa_decode_step.
+    stride = pa.pa_decode_step_staging_bytes(n, cap_max)
     up = torch.empty((total, stride), dtype=torch.uint8).pin_memory()
     dbuf = torch.empty(stride, dtype=torch.uint8, device=dev)
+    o_lens, o_qsl = 8 * n, 12 * n
+    o_pairs = (16 * n + 4 + 7) // 8 * 8
+    o_tab = o_pairs + 8 * n
     d_slots = dbuf[:o_lens].view(torch.int64)
-    d_lens = dbuf[o_lens:o_pairs].view(torch.int32)
+    d_lens = dbuf[o_lens:o_qsl].view(torch.int32)
     d_pairs = dbuf[o_pairs:o_tab].view(torch.int32).view(n, 2)
     d_tab = dbuf[o_tab:].view(torch.int32)
     cur = torch.cuda.current_stream(dev)
-    stream = cur.cuda_stream
     ev = HipEvents()
-    fwd_ev = ev.new(2 * total)
+    stage_ev = [ev.new(2 * len(STAGES)) for _ in range(EVENT_STEPS)]
     logical = []
     scale = 1.0 / np.sqrt(d)
     torch.cuda.synchronize()
 
-    def decode_step(i, record):
-        sl, pairs = alloc.append_slots(ids)
-        lens[:] += 1
-        L = int(lens.max())
-        cap = (L + 15) // 16
-        tab = alloc.block_tables(ids, cap)
+    def composed_step(i):
         h = up[i].numpy()
-        h[:o_lens].view(np.int64)[:] = sl
-        h[o_lens:o_pairs].view(np.int32)[:] = lens
-        h[o_tab:o_tab + 4 * n * cap].view(np.int32)[:] = tab.reshape(-1)
-        if len(pairs):
-            h[o_pairs:o_pairs + 8 * len(pairs)].view(np.int32)[:] = np.asarray(pairs, np.int32).reshape(-1)
-        dbuf.copy_(up[i], non_blocking=True)
-        if len(pairs):
-            pa.pa_copy_blocks(kc, vc, d_pairs[:len(pairs)], status, cur)
+        ncow, L, cols, used = pa.pa_decode_step_stage(alloc, ids, cap_max, h)
+        dbuf[:used].copy_(up[i, :used], non_blocking=True)
+        if ncow:
+            pa.pa_copy_blocks(kc, vc, d_pairs[:ncow], status, cur)
         pa.pa_reshape_and_cache(kst[i], vst[i], kc, vc, d_slots, status, cur)
-        tables = d_tab[:n * cap].view(n, cap)
-        if record:
-            ev.record(fwd_ev[2 * i], stream)
+        tables = d_tab[:n * cols].view(n, cols)
         if cascade:
             pa.pa_forward_shared(out, qs[i], kc, vc, tables, d_lens, qsl, groups, 1, L, scale, ws, status, cur)
         else:
             pa.pa_forward(out, qs[i], kc, vc, tables, d_lens, qsl, 1, L, scale, ws, status, cur)
-        if record:
-            ev.record(fwd_ev[2 * i + 1], stream)
-            logical.append(int(lens.sum()))
 
+    def native_step(i):
+        pa.pa_decode_step(alloc, ids, out, qs[i], kst[i], vst[i], kc, vc, scale, cap_max, up[i], dbuf, ws,
+                          groups=groups, dev_status=status, stream=cur)
+
+    step = composed_step if args.composed_step else native_step
     for i in range(args.warmup):
-        decode_step(i, False)
+        step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.warmup, total):
-        decode_step(i, True)
+    for i in range(args.warmup, args.warmup + args.steps):
+        step(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # the forward's device time, from events around its stages on extra steps
+    first_ev = args.warmup + args.steps
+    for j in range(EVENT_STEPS):
+        pa.pa_set_stage_events(stage_ev[j])
+        step(first_ev + j)
+        logical.append(int(sum(alloc.num_tokens(s) for s in ids)))
+    torch.cuda.synchronize()
+    pa.pa_set_stage_events(None)
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item()):#x}")
-    fwd_ms = [ev.ms(fwd_ev[2 * i], fwd_ev[2 * i + 1]) for i in range(args.warmup, total)]
+    # the forward's kernels: the sum of its stage durations (the gaps the events add between them excluded)
+    fwd_ms = [sum(ev.ms(e[2 * k], e[2 * k + 1]) for k in range(len(STAGES))) for e in stage_ev]
     ev.close()
     tok_bytes = 2 * H * d * 2
     logical_bytes = sum(logical) * tok_bytes
     # unique pages: every prompt token once, plus each branch's own decode tokens
-    unique_bytes = sum((int(spec.prompt_lens.sum()) + n * (i + 1)) * tok_bytes for i in range(args.warmup, total))
+    unique_bytes = sum((int(spec.prompt_lens.sum()) + n * (i + 1)) * tok_bytes for i in range(first_ev, total))
     fwd_s = sum(fwd_ms) * 1e-3
     ms_per_step = 1e3 * elapsed / args.steps
+    fwd_ms_mean = 1e3 * fwd_s / EVENT_STEPS
     achieved = unique_bytes / fwd_s / 1e9
     print(json.dumps({
         "metric": "parallel sampling decode tokens/s (shared prompt pages, copy-on-write)",
@@ -395,14 +402,14 @@ def sampling_workflow(torch, pa, W, dev, args):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "parallel_sampling_16x4", "prompts": P, "branches": B, "q_heads": H, "kv_heads": H,
                    "head_dim": d, "block_size": 16, "pool_blocks": NB, "decode_steps": total,
+                   "step": "composed from the single entry points" if args.composed_step else "pa_decode_step",
                    "forward": "pa_forward_shared (prompt pages read once per prompt)" if cascade else "pa_forward"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "pa_forward",
-                     "kernel_ms": round(1e3 * fwd_s / args.steps, 4), "algorithmic_bytes": "unique KV pages per step"},
+                     "kernel_ms": round(fwd_ms_mean, 4), "algorithmic_bytes": "unique KV pages per step"},
         "forward_logical_kv_GBps": round(logical_bytes / fwd_s / 1e9, 1),
         "forward_unique_kv_GBps": round(achieved, 1),
-        # the host loop (allocator, uploads and launches from Python) paces the steps
-        "forward_share_of_step": round(1e3 * fwd_s / args.steps / ms_per_step, 4)}), flush=True)
+        "forward_share_of_step": round(fwd_ms_mean / ms_per_step, 4)}), flush=True)
 
 
 def main():
@@ -419,6 +426,8 @@ def main():
     ap.add_argument("--read-mib", type=int, default=0, help="read workload: MiB per step (0: the whole 4 GiB pool)")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="sampling workload: attend with pa_forward_shared, the branches of a prompt as one group")
+    ap.add_argument("--composed-step", action="store_true",
+                    help="sampling workload: issue a step's operations one by one instead of one pa_decode_step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus})",
