@@ -430,7 +430,7 @@ def main():
                     help="sampling workload: issue a step's operations one by one instead of one pa_decode_step")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for {args.gpus})",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for {args.gpus})",
               file=sys.stderr)
         sys.exit(2)
 
