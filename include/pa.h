@@ -37,8 +37,7 @@
  *
  * Supported: head_dim 64 or 128, block_size 16, num_q_heads a multiple of
  * num_kv_heads, dtype float32 or bfloat16 (q, caches and output share it;
- * accumulation is float32).  pa_forward in float32 takes head_dim 64 only
- * (PA_ERR_UNSUPPORTED otherwise); cache write and block copy take both.
+ * accumulation is float32).
  */
 #ifndef PA_H
 #define PA_H

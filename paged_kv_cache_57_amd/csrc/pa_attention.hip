@@ -1309,11 +1309,6 @@ pa_status forward_impl(const char* fn, void* out, const void* q, const void* k_c
     return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d (only 16 is supported)", fn, block_size);
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128 supported)", fn, head_dim);
-  // float32 attention is built for head_dim 64 only: its head_dim-128 variant
-  // needed more registers than a wavefront can hold without spilling, and it
-  // is switched off until that variant is reworked.
-  if (dtype == PA_F32 && head_dim != 64)
-    return fail(PA_ERR_UNSUPPORTED, "%s: float32 attention supports head_dim 64 only", fn);
   if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads)
     return fail(PA_ERR_INVALID, "%s: %d query heads are not a multiple of %d KV heads", fn,
                 num_q_heads, num_kv_heads);
@@ -1393,7 +1388,8 @@ pa_status forward_impl(const char* fn, void* out, const void* q, const void* k_c
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   if (is_f32) {
-    launch_attention<float, 64>(p, may_valu, false, false, grid_v, grid_m, grid_t, s);
+    if (head_dim == 64) launch_attention<float, 64>(p, may_valu, false, false, grid_v, grid_m, grid_t, s);
+    else launch_attention<float, 128>(p, may_valu, false, false, grid_v, grid_m, grid_t, s);
   } else {
     if (head_dim == 64) launch_attention<bf16_t, 64>(p, may_valu, may_mfma, may_tile, grid_v, grid_m, grid_t, s);
     else launch_attention<bf16_t, 128>(p, may_valu, may_mfma, may_tile, grid_v, grid_m, grid_t, s);

@@ -109,8 +109,6 @@ extern "C" pa_status pa_decode_step(pa_allocator* a, int32_t num_seqs, const int
   if (dtype != PA_F32 && dtype != PA_BF16) return pa::fail(PA_ERR_UNSUPPORTED, "%s: dtype %d", fn, (int)dtype);
   if (head_dim != 64 && head_dim != 128)
     return pa::fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d (64 or 128 supported)", fn, head_dim);
-  if (dtype == PA_F32 && head_dim != 64)
-    return pa::fail(PA_ERR_UNSUPPORTED, "%s: float32 attention supports head_dim 64 only", fn);
   if (num_groups > 0 && (dtype != PA_BF16 || 2 * (num_q_heads / num_kv_heads) > 16))
     return pa::fail(PA_ERR_UNSUPPORTED, "%s: shared prefixes need bfloat16 and at most 8 query heads per KV head",
                    fn);

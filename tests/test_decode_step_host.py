@@ -130,7 +130,7 @@ def test_decode_step_argument_checks(pa):
     assert call(ws_bytes=ws_need - 1) == pa.PA_ERR_INVALID
     assert call(dtype=7) == pa.PA_ERR_UNSUPPORTED
     assert call(head_dim=96) == pa.PA_ERR_UNSUPPORTED
-    assert call(dtype=pa.PA_F32, head_dim=128) == pa.PA_ERR_UNSUPPORTED
+    assert call(dtype=pa.PA_F32, groups=fake, ng=1) == pa.PA_ERR_UNSUPPORTED                  # groups need bf16
     assert call(ng=1) == pa.PA_ERR_INVALID                                         # groups NULL
     assert call(hq=6, hkv=4) == pa.PA_ERR_INVALID
     assert call(scale=float("nan")) == pa.PA_ERR_INVALID

@@ -88,11 +88,16 @@ def test_large_value_magnitudes(emu):
     assert np.isfinite(got).all() and ratio <= 1.0, f"large values: worst err/bound {ratio:.3f}"
 
 
-def test_float32_head_dim_128_is_rejected(emu):
-    w = W.random_ragged(1, "f32", 4, 4, 128, [1], [20])
-    kp, vp = empty_pools(np.random.default_rng(0), "f32", w.num_blocks, 4, 128)
-    with pytest.raises(RuntimeError, match="head_dim 64 only"):
-        emu.forward(w, np.zeros((1, 4, 128), np.float32), kp, vp)
+def test_float32_head_dim_128_decode_and_prefill(emu):
+    # float32 at head_dim 128 (VALU worker only, values kept in 32 bits): MHA decode rows
+    # with split contexts (512-key partitions) and a 7-row prefill chunk
+    w = W.random_ragged(23, "f32", 4, 4, 128, [1, 7, 1], [900, 40, 17])
+    rng = np.random.default_rng(23)
+    kp, vp = empty_pools(rng, "f32", w.num_blocks, 4, 128)
+    q = raw(rng.standard_normal((w.num_tokens, 4, 128)).astype(np.float32), "f32")
+    out, st = emu.forward(w, q, kp, vp)
+    assert st == 0
+    check(w, q, kp, vp, out, "float32 head_dim 128")
 
 
 def test_nan_outside_context_is_never_read(emu):

@@ -137,12 +137,12 @@ def test_tiny_decode_fp32(pa):
 # have no per-lane branches (checked on the compiled code by
 # test_kernel_resources).  float32 with head_dim 128 stays unsupported: its
 # kernel needed more registers than it could hold without spilling.
-REJECTED = {1: "float32 attention supports head_dim 64 only"}
+REJECTED = {}  # cases the host refuses (index -> message); none at present
 
 RAGGED = [
     # dtype, Hq, Hkv, d, q_lens, ctx_lens
     ("f32", 4, 4, 64, [1, 1, 1], [1, 16, 17]),
-    ("f32", 8, 2, 128, [1, 5, 1], [1300, 40, 513]),              # rejected, see REJECTED
+    ("f32", 8, 2, 128, [1, 5, 1], [1300, 40, 513]),              # float32 at head_dim 128: VALU rows, GQA, prefill
     ("f32", 8, 2, 64, [1, 5, 1], [1300, 40, 513]),               # VALU split contexts, GQA, fp32 prefill rows
     ("bf16", 32, 32, 128, [1, 1, 1, 1], [1, 15, 513, 2049]),      # MHA decode, partitions + ragged tails
     ("bf16", 8, 8, 64, [1, 1], [700, 33]),
@@ -156,6 +156,7 @@ RAGGED = [
     ("bf16", 4, 4, 128, [129, 128, 2], [129, 1152, 2]),           # tile edges: 129 and 128 rows, 2-row MFMA
     ("bf16", 2, 2, 64, [1, 3], [16500, 700]),                     # >= 32 partitions: four waves merge a row
     ("f32", 2, 2, 64, [1, 2], [17000, 40]),                       # the same for float32 (512-key partitions)
+    ("f32", 4, 4, 128, [1, 3], [9000, 130]),                      # float32 at head_dim 128: 18 partitions merged
 ]
 
 

@@ -64,7 +64,7 @@ def test_host_argument_checks_fail_before_any_launch(pa):
     assert st == pa.PA_ERR_UNSUPPORTED and "block_size" in pa.pa_last_error()
     st = lib.pa_forward(None, None, None, None, None, 8, None, None, 1, 1, 1, 1, 4, 4, 128, 16, 8, 1.0, 0,
                         None, 0, None, None)
-    assert st == pa.PA_ERR_UNSUPPORTED and "head_dim 64 only" in pa.pa_last_error()
+    assert st == pa.PA_ERR_INVALID and "NULL" in pa.pa_last_error()   # float32 at head_dim 128 is supported
     st = lib.pa_forward(None, None, None, None, None, 1, None, None, 1, 1, 1, 1, 6, 4, 128, 16, 8, 1.0, 1,
                         None, 0, None, None)
     assert st == pa.PA_ERR_INVALID
