@@ -245,10 +245,20 @@ def read_calibration(torch, pa, dev, args, nbytes=4 << 30, grid=2048):
     reach if they did no arithmetic.  By default a step reads every page once;
     with --read-mib M a step reads the next M MiB of the order (successive steps
     take disjoint slices, so none finds its pages in the 256 MB Infinity Cache),
-    the rate a pass of that size can reach."""
+    the rate a pass of that size can reach.  With --read-chunk-pages N the order is
+    a random permutation of runs of N consecutive pages (0: every page in address
+    order), read by neighbouring wavefronts at the same time."""
     pool = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(7)
     npages = nbytes // 4096
-    order = torch.from_numpy(np.random.default_rng(5).permutation(npages).astype(np.int32)).to(dev)
+    run = args.read_chunk_pages
+    if run < 0 or (run and npages % run):
+        raise SystemExit(f"--read-chunk-pages must be 0 or divide {npages}")
+    if run == 0:
+        ids = np.arange(npages, dtype=np.int64)
+    else:
+        runs = np.random.default_rng(5).permutation(npages // run).astype(np.int64)
+        ids = (runs[:, None] * run + np.arange(run)[None, :]).reshape(-1)
+    order = torch.from_numpy(ids.astype(np.int32)).to(dev)
     per = npages if not args.read_mib else min(npages, args.read_mib * 256)
     nslices = npages // per
     slices = [order[i * per:(i + 1) * per] for i in range(nslices)]
@@ -270,6 +280,8 @@ def read_calibration(torch, pa, dev, args, nbytes=4 << 30, grid=2048):
     ms = t0.elapsed_time(t1) / args.steps
     gbps = per * 4096 / (ms * 1e-3) / 1e9
     name = "read_pages_4GiB" if per == npages else f"read_pages_{per * 4096 >> 20}MiB_of_4GiB"
+    if run != 1:
+        name += "_in_address_order" if run == 0 else f"_runs_of_{run}"
     print(json.dumps({"metric": "random 4 KiB page reads GB/s", "value": round(gbps, 1), "unit": "GB/s",
                       "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
                       "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
@@ -424,6 +436,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--read-mib", type=int, default=0, help="read workload: MiB per step (0: the whole 4 GiB pool)")
+    ap.add_argument("--read-chunk-pages", type=int, default=1,
+                    help="read workload: pages per run of consecutive pages in the random order (0: address order)")
     ap.add_argument("--shared-prefix", action="store_true",
                     help="sampling workload: attend with pa_forward_shared, the branches of a prompt as one group")
     ap.add_argument("--composed-step", action="store_true",
