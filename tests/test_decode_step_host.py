@@ -137,3 +137,37 @@ def test_decode_step_argument_checks(pa):
     assert call(mbps=0) == pa.PA_ERR_INVALID
     assert "workspace" in pa.pa_last_error() or "table" in pa.pa_last_error()
     assert alloc.num_tokens(0) == 20 and alloc.num_free() == 62
+
+
+def test_stage_with_streaming_sequences(pa):
+    """Two streaming sequences (4 sinks + a window of 40, one of them forked) beside a
+    plain one: once a stream's cache is full, the staged slot is the ring position of
+    the mirror, the staged length stays at 44 and a shared block is copied on write."""
+    NB = 64
+    alloc = pa.Allocator(NB, 16)
+    mirror = mirror_alloc.StreamingAllocator(NB, 16)
+    alloc.create_streaming(0, 4, 40, 30)
+    mirror.create_streaming(0, 4, 40, 30)
+    alloc.fork(0, 1)
+    mirror.fork(0, 1)
+    alloc.create(2, 5)
+    mirror.create(2, 5)
+    ids = [0, 1, 2]
+    M = 8
+    buf = np.zeros(pa.pa_decode_step_staging_bytes(len(ids), M), np.uint8)
+    cows = 0
+    for step in range(60):
+        ncow, mx, cols, used = pa.pa_decode_step_stage(alloc, ids, M, buf)
+        want_slots, want_pairs = [], []
+        for s in ids:
+            sl, cow = mirror.append_streaming(s) if s in mirror.stream else mirror.append_slot(s)
+            want_slots.append(sl)
+            if cow:
+                want_pairs.append(cow)
+        o_lens, o_qsl, o_pairs, o_tab, end = layout(len(ids), cols)
+        assert list(buf[:o_lens].view(np.int64)) == want_slots, step
+        assert [tuple(x) for x in buf[o_pairs:o_pairs + 8 * ncow].view(np.int32).reshape(-1, 2)] == want_pairs, step
+        lens = [mirror.ntok[s] for s in ids]
+        assert list(buf[o_lens:o_qsl].view(np.int32)) == lens, step
+        cows += ncow
+    assert lens[:2] == [44, 44] and lens[2] == 65 and cows > 0
