@@ -414,7 +414,9 @@ pa_status pa_sf_step(pa_splitfuse* c, int32_t cap, int64_t* seq_ids, int32_t* q_
  * Bytes needed for tables of up to max_blocks_per_seq columns (0 for a
  * non-positive argument): */
 size_t pa_decode_step_staging_bytes(int32_t num_seqs, int32_t max_blocks_per_seq);
-/* Host half: appends one slot to each sequence (in order) and writes the
+/* Host half: appends one slot to each sequence (in order; with token_ids, a
+ * host int32 [num_seqs] array of the new tokens, through pa_seq_append_tokens
+ * for sequences made from token ids, else pa_seq_append_slots) and writes the
  * staging layout above into host_staging (host, 8-byte aligned, at least
  * pa_decode_step_staging_bytes(num_seqs, max_blocks_per_seq) bytes), with
  * c = ceil(longest context / 16) columns.  Out: *num_cow_out copy pairs,
@@ -424,13 +426,15 @@ size_t pa_decode_step_staging_bytes(int32_t num_seqs, int32_t max_blocks_per_seq
  * pool fails as pa_seq_append_slots (the sequences before the failing one
  * keep their new slot). */
 pa_status pa_decode_step_stage(pa_allocator* a, int32_t num_seqs, const int64_t* seq_ids,
-                               int32_t max_blocks_per_seq, void* host_staging, size_t staging_bytes,
+                               const int32_t* token_ids, int32_t max_blocks_per_seq, void* host_staging, size_t staging_bytes,
                                int32_t* num_cow_out, int32_t* max_context_len_out, int32_t* table_cols_out,
                                size_t* used_bytes_out);
 /* The whole step.  pa_decode_step_stage into host_staging, then hipMemcpyAsync
  * of the used bytes into dev_staging and the three launches on `stream`.
  *   seq_ids        host, int64 [num_seqs]; row i of q / new_key / new_value / out
  *                  is sequence seq_ids[i]
+ *   token_ids      host, int32 [num_seqs] new tokens of sequences made from
+ *                  token ids (prefix caching), or NULL
  *   q, out         device, [num_seqs][num_q_heads][head_dim] of dtype
  *   new_key, new_value  device, [num_seqs][num_kv_heads][head_dim] of dtype
  *   k_cache, v_cache    device, pool layout above, num_blocks blocks
@@ -447,7 +451,8 @@ pa_status pa_decode_step_stage(pa_allocator* a, int32_t num_seqs, const int64_t*
  *                  single-row sequences of up to 16 x max_blocks_per_seq keys
  * Argument errors are reported before the allocator changes; a HIP error of
  * the upload returns PA_ERR_HIP after the allocator has advanced. */
-pa_status pa_decode_step(pa_allocator* a, int32_t num_seqs, const int64_t* seq_ids, void* out, const void* q,
+pa_status pa_decode_step(pa_allocator* a, int32_t num_seqs, const int64_t* seq_ids, const int32_t* token_ids,
+                         void* out, const void* q,
                          const void* new_key, const void* new_value, void* k_cache, void* v_cache,
                          int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                          pa_dtype dtype, float scale, const int32_t* groups, int32_t num_groups,

@@ -83,8 +83,8 @@ _SIGS = {
     "pa_sf_finish": (_i32, [_vp, _i64]),
     "pa_sf_step": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp]),
     "pa_decode_step_staging_bytes": (_sz, [_i32, _i32]),
-    "pa_decode_step_stage": (_i32, [_vp, _i32, _vp, _i32, _vp, _sz, _pi32, _pi32, _pi32, ctypes.POINTER(_sz)]),
-    "pa_decode_step": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
+    "pa_decode_step_stage": (_i32, [_vp, _i32, _vp, _vp, _i32, _vp, _sz, _pi32, _pi32, _pi32, ctypes.POINTER(_sz)]),
+    "pa_decode_step": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32,
                               _vp, _i32, _i32, _vp, _vp, _sz, _vp, _sz, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -441,25 +441,38 @@ def pa_decode_step_staging_bytes(num_seqs: int, max_blocks_per_seq: int) -> int:
     return int(_lib.pa_decode_step_staging_bytes(num_seqs, max_blocks_per_seq))
 
 
-def pa_decode_step_stage(alloc, seq_ids, max_blocks_per_seq: int, host_staging):
-    """Host half of a decode step into host_staging (a uint8 numpy array or CPU tensor).
+def _token_arg(token_ids, n):
+    if token_ids is None:
+        return None, None
+    toks = np.ascontiguousarray(token_ids, dtype=np.int32)
+    if toks.shape != (n,):
+        raise PAError(PA_ERR_INVALID, "one token per sequence")
+    return toks, _np_ptr(toks)
+
+
+def pa_decode_step_stage(alloc, seq_ids, max_blocks_per_seq: int, host_staging, token_ids=None):
+    """Host half of a decode step into host_staging (a uint8 numpy array or CPU tensor);
+    token_ids: the new tokens of sequences made from token ids.
     Returns (num_cow, max_context_len, table_cols, used_bytes)."""
     ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+    toks, tok_ptr = _token_arg(token_ids, len(ids))
     buf = host_staging.numpy() if hasattr(host_staging, "numpy") else host_staging
     ncow, mx, cols, used = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32(), ctypes.c_size_t()
-    _check(_lib.pa_decode_step_stage(alloc._h, len(ids), _np_ptr(ids), max_blocks_per_seq, _np_ptr(buf), buf.nbytes,
+    _check(_lib.pa_decode_step_stage(alloc._h, len(ids), _np_ptr(ids), tok_ptr, max_blocks_per_seq, _np_ptr(buf),
+                                     buf.nbytes,
                                      ctypes.byref(ncow), ctypes.byref(mx), ctypes.byref(cols), ctypes.byref(used)))
     return ncow.value, mx.value, cols.value, used.value
 
 
 def pa_decode_step(alloc, seq_ids, out, q, new_key, new_value, k_cache, v_cache, scale, max_blocks_per_seq,
-                   host_staging, dev_staging, workspace, groups=None, dev_status=None, stream=None):
+                   host_staging, dev_staging, workspace, groups=None, dev_status=None, stream=None, token_ids=None):
     """One decode step driven from the allocator (see pa.h): host_staging is a uint8
     CPU tensor (pinned: the upload is then asynchronous; each step in flight needs
     its own), dev_staging a uint8 device tensor at least as large."""
     import torch
     nb, hkv, d, blk = _pool_dims(k_cache, v_cache)
     ids = np.ascontiguousarray(seq_ids, dtype=np.int64)
+    toks, tok_ptr = _token_arg(token_ids, len(ids))
     n, hq, dq = q.shape
     if n != len(ids) or dq != d or tuple(out.shape) != (n, hq, d):
         raise PAError(PA_ERR_INVALID, "q/out must be [num_seqs, num_q_heads, head_dim]")
@@ -474,7 +487,7 @@ def pa_decode_step(alloc, seq_ids, out, q, new_key, new_value, k_cache, v_cache,
     if groups is not None and (groups.dim() != 2 or groups.shape[1] != 3):
         raise PAError(PA_ERR_INVALID, "groups must be [num_groups, 3]")
     _check(_lib.pa_decode_step(
-        alloc._h, n, _np_ptr(ids), _dev(out, "out", q.dtype), _dev(q, "q", k_cache.dtype),
+        alloc._h, n, _np_ptr(ids), tok_ptr, _dev(out, "out", q.dtype), _dev(q, "q", k_cache.dtype),
         _dev(new_key, "new_key", k_cache.dtype), _dev(new_value, "new_value", k_cache.dtype),
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), nb, hq, hkv, d, _dtype_code(q), float(scale),
         _dev(groups, "groups", torch.int32) if ng else None, ng, int(max_blocks_per_seq),

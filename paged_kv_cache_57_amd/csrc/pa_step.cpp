@@ -44,7 +44,7 @@ extern "C" size_t pa_decode_step_staging_bytes(int32_t num_seqs, int32_t max_blo
 }
 
 extern "C" pa_status pa_decode_step_stage(pa_allocator* a, int32_t num_seqs, const int64_t* seq_ids,
-                                          int32_t max_blocks_per_seq, void* host_staging, size_t staging_bytes,
+                                          const int32_t* token_ids, int32_t max_blocks_per_seq, void* host_staging, size_t staging_bytes,
                                           int32_t* num_cow_out, int32_t* max_context_len_out,
                                           int32_t* table_cols_out, size_t* used_bytes_out) {
   const char* fn = "pa_decode_step_stage";
@@ -70,7 +70,9 @@ extern "C" pa_status pa_decode_step_stage(pa_allocator* a, int32_t num_seqs, con
                      (long long)seq_ids[i], max_blocks_per_seq);
   }
   int32_t ncow = 0;
-  pa_status st = pa_seq_append_slots(a, num_seqs, seq_ids, (int64_t*)h, (int32_t*)(h + bound.pairs), &ncow);
+  pa_status st = token_ids ? pa_seq_append_tokens(a, num_seqs, seq_ids, token_ids, (int64_t*)h,
+                                                  (int32_t*)(h + bound.pairs), &ncow)
+                            : pa_seq_append_slots(a, num_seqs, seq_ids, (int64_t*)h, (int32_t*)(h + bound.pairs), &ncow);
   if (st != PA_OK) return st;
   int32_t max_len = 0;
   for (int32_t i = 0; i < num_seqs; ++i) {
@@ -91,7 +93,8 @@ extern "C" pa_status pa_decode_step_stage(pa_allocator* a, int32_t num_seqs, con
   return pa::ok();
 }
 
-extern "C" pa_status pa_decode_step(pa_allocator* a, int32_t num_seqs, const int64_t* seq_ids, void* out,
+extern "C" pa_status pa_decode_step(pa_allocator* a, int32_t num_seqs, const int64_t* seq_ids,
+                                    const int32_t* token_ids, void* out,
                                     const void* q, const void* new_key, const void* new_value, void* k_cache,
                                     void* v_cache, int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t head_dim, pa_dtype dtype, float scale, const int32_t* groups,
@@ -129,8 +132,8 @@ extern "C" pa_status pa_decode_step(pa_allocator* a, int32_t num_seqs, const int
 
   int32_t ncow = 0, max_len = 0, cap = 0;
   size_t used = 0;
-  pa_status st = pa_decode_step_stage(a, num_seqs, seq_ids, max_blocks_per_seq, host_staging, staging_bytes, &ncow,
-                                      &max_len, &cap, &used);
+  pa_status st = pa_decode_step_stage(a, num_seqs, seq_ids, token_ids, max_blocks_per_seq, host_staging,
+                                      staging_bytes, &ncow, &max_len, &cap, &used);
   if (st != PA_OK) return st;
   const StepLayout l = step_layout(num_seqs, cap);
   hipStream_t s = (hipStream_t)stream;

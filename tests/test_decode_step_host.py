@@ -120,7 +120,7 @@ def test_decode_step_argument_checks(pa):
 
     def call(out=fake, ws=fake, ws_bytes=ws_need, dtype=pa.PA_BF16, head_dim=d, groups=None, ng=0, mbps=8,
              dev_staging=fake, scale=0.125, hq=H, hkv=H):
-        return _lib.pa_decode_step(alloc._h, 1, ids.ctypes.data_as(ctypes.c_void_p), out, fake, fake, fake, fake,
+        return _lib.pa_decode_step(alloc._h, 1, ids.ctypes.data_as(ctypes.c_void_p), None, out, fake, fake, fake, fake,
                                    fake, 64, hq, hkv, head_dim, dtype, scale, groups, ng, mbps,
                                    host.ctypes.data_as(ctypes.c_void_p), dev_staging, host.nbytes, ws, ws_bytes,
                                    None, None)
@@ -171,3 +171,52 @@ def test_stage_with_streaming_sequences(pa):
         assert list(buf[o_lens:o_qsl].view(np.int32)) == lens, step
         cows += ncow
     assert lens[:2] == [44, 44] and lens[2] == 65 and cows > 0
+
+
+def test_stage_with_prefix_cached_sequences(pa):
+    """Sequences made from token ids (prefix caching on): the step appends each new token
+    through pa_seq_append_tokens.  Three requests share a 2-block prompt prefix; the staged
+    slots, copy pairs, lengths and tables equal the prefix-caching mirror's every step,
+    including the steps where a filled block is registered or replaced by a cached one."""
+    NB, P = 64, 16
+    rng = np.random.default_rng(4)
+    alloc = pa.Allocator(NB, P)
+    alloc.enable_prefix_caching()
+    mirror = mirror_alloc.PrefixCachingAllocator(NB, P)
+    prompt = list(rng.integers(0, 1000, size=2 * P + 5))
+    for s in (0, 1, 2):
+        toks = prompt if s < 2 else prompt[:2 * P] + [7, 7, 7]
+        assert alloc.create_tokens(s, toks) == mirror.create_tokens(s, toks)
+    ids = [0, 1, 2]
+    switched = 0
+    M = 8
+    buf = np.zeros(pa.pa_decode_step_staging_bytes(len(ids), M), np.uint8)
+    for step in range(40):
+        t01, t2 = (int(x) for x in rng.integers(0, 3, size=2))
+        new = [t01, t01, t2]              # sequences 0 and 1 fill equal blocks: the second switches to the first's
+        before = [list(mirror.block_table(s)) for s in ids]
+        ncow, mx, cols, used = pa.pa_decode_step_stage(alloc, ids, M, buf, token_ids=new)
+        want_slots, want_pairs = [], []
+        for s, tkn in zip(ids, new):
+            sl, cow = mirror.append_token(s, tkn)
+            want_slots.append(sl)
+            if cow:
+                want_pairs.append(cow)
+        o_lens, o_qsl, o_pairs, o_tab, end = layout(len(ids), cols)
+        assert list(buf[:o_lens].view(np.int64)) == want_slots, step
+        assert [tuple(x) for x in buf[o_pairs:o_pairs + 8 * ncow].view(np.int32).reshape(-1, 2)] == want_pairs
+        assert list(buf[o_lens:o_qsl].view(np.int32)) == [mirror.ntok[s] for s in ids], step
+        want_tab = np.full((len(ids), cols), -1, np.int32)
+        for i, s in enumerate(ids):
+            t = mirror.block_table(s)
+            want_tab[i, :len(t)] = t
+        assert np.array_equal(buf[o_tab:end].view(np.int32).reshape(len(ids), cols), want_tab), step
+        assert alloc.num_free() == mirror.num_free()
+        switched += sum(1 for i, s in enumerate(ids)
+                        if len(before[i]) == len(mirror.block_table(s)) and before[i] != list(mirror.block_table(s)))
+    assert switched > 0
+    with pytest.raises(pa.PAError) as e:                       # a token per sequence
+        pa.pa_decode_step_stage(alloc, ids, M, buf, token_ids=[1])
+    assert e.value.status == pa.PA_ERR_INVALID
+    with pytest.raises(pa.PAError):                            # these sequences take token ids
+        pa.pa_decode_step_stage(alloc, ids, M, buf)
