@@ -250,6 +250,18 @@ def test_many_sequences(pa):
     run_and_check(pa, w, label="5000 sequences")
 
 
+def test_very_long_contexts(pa):
+    """Contexts of 131,072 keys: 256 VALU partitions (MHA decode, bf16 and float32) and
+    512 MFMA partitions (GQA decode) merged per row, plus a 130-row prefill chunk at the
+    end of a 40,000-key context (40 tile partitions per row, two row tiles)."""
+    for dt, hq, hkv, d, ql, cl in [("bf16", 2, 2, 128, [1, 1], [131072, 5]),
+                                   ("f32", 2, 2, 64, [1], [131072]),
+                                   ("bf16", 16, 2, 128, [1, 1], [131072, 700]),
+                                   ("bf16", 2, 2, 128, [130], [40000])]:
+        w = W.random_ragged(77, dt, hq, hkv, d, ql, cl)
+        run_and_check(pa, w, label=f"long {dt} Hq={hq} Hkv={hkv} d={d} q={ql} L={cl}")
+
+
 def test_nan_poison_outside_context(pa):
     w = W.random_ragged(7, "bf16", 16, 4, 128, [1, 5, 1, 1], [37, 600, 1000, 1])
     run_and_check(pa, w, poison=True, label="nan-poison GQA")
