@@ -748,3 +748,43 @@ def test_decode_step_native(pa, shared):
                                 float(np.float32(scale)), "bf16")
     assert_close(to_f64(out_b), ref, "bf16", "native decode step, last step")
     say(f"  {spec.steps} steps bit-identical to the composed calls; copy-on-write pairs {copies}")
+
+
+def test_forward_replayed_from_a_hip_graph(pa):
+    """A cache write + pa_forward captured once in a HIP graph (torch.cuda.CUDAGraph) and
+    replayed with new q, new K/V and eager work and synchronisations between replays:
+    every replay's output equals the eager calls' on the same inputs bit for bit, and
+    the oracle on the last one.  Nothing in the path allocates, copies from the host or
+    clears memory with a memset node (the planner zeroes its counters in a kernel)."""
+    w = W.random_ragged(41, "bf16", 16, 4, 128, [1, 1, 24, 1, 200], [700, 33, 1100, 3000, 2300], with_slots=True)
+    say(f"[case] HIP graph replay: S={w.num_seqs} T={w.num_tokens} GQA 16/4, chunks of 24 and 200 rows")
+    check_tables_in_pool(w)
+    q, kc, vc, nk, nv = W.make_values(w, DEV)
+    r = Run(w)
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):              # warm-up off the default stream, as capture expects
+        r.write(nk, nv, kc, vc)
+        r.forward(q, kc, vc, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        r.write(nk, nv, kc, vc)
+        r.forward(q, kc, vc, out)
+    gen = torch.Generator(device=DEV).manual_seed(3)
+    for rep in range(4):
+        W.fill_normal(q, gen)                  # eager work between the replays
+        W.fill_normal(nk, gen)
+        W.fill_normal(nv, gen)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        r.write(nk, nv, kc, vc)                # the same two calls, eagerly
+        ref_out = r.forward(q, kc, vc)
+        r.check_status()
+        assert torch.equal(got.view(torch.int16), ref_out.view(torch.int16)), f"replay {rep} differs"
+    rows, ref = oracle_rows(w, q, kc, vc, range(w.num_seqs))
+    assert_close(to_f64(got.index_select(0, torch.from_numpy(rows).to(DEV))), ref, "bf16", "graph replay")
