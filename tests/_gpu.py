@@ -1,4 +1,5 @@
 """Helpers for GPU parity tests: device inputs, host readback, oracle comparison."""
+import os
 import sys
 
 import numpy as np
@@ -113,3 +114,65 @@ def assert_close(got_f64, ref, dtype, what=""):
         i = np.unravel_index(np.argmax(err - bound), err.shape)
         raise AssertionError(f"{what}: {bad.sum()} elements out of tolerance; worst at {i}: "
                              f"gpu {got_f64[i]!r} ref {ref[i]!r}")
+
+
+def host_workers():
+    """Threads for oracle work: the cores this process may run on, at most 16."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+_POOL = None
+
+
+def oracle_pool():
+    """The session's oracle worker processes (started on first use, shut down at exit)."""
+    global _POOL
+    if _POOL is None:
+        import atexit
+        from tests._oracle_pool import OraclePool
+        _POOL = OraclePool(host_workers())
+        atexit.register(_POOL.__exit__, None, None, None)
+    return _POOL
+
+
+def oracle_rows_all(w: W.Workload, q, k_cache, v_cache, seqs=None, batch_blocks=8000):
+    """fp64 oracle output for every query row of the listed sequences (default: all),
+    one oracle call per sequence, spread over worker processes.  Pages are read back
+    in batches of at most batch_blocks blocks, so host memory stays bounded for pools
+    of tens of GB.  Returns (rows, ref) like oracle_rows, rows in sequence order."""
+    seqs = list(range(w.num_seqs)) if seqs is None else list(seqs)
+    qsl = w.query_start_loc
+    seqs = [s for s in seqs if qsl[s + 1] > qsl[s]]
+    if not seqs:
+        return np.zeros(0, np.int64), np.zeros((0, w.num_q_heads, w.head_dim))
+    groups, cur, cur_n = [], [], 0
+    for s in seqs:
+        n = (int(w.context_lens[s]) + 15) // 16
+        if cur and cur_n + n > batch_blocks:
+            groups.append(cur)
+            cur, cur_n = [], 0
+        cur.append(s)
+        cur_n += n
+    groups.append(cur)
+    rows_all, refs = [], []
+    qh_all = host_raw(q)
+    pool = oracle_pool()
+    for grp in groups:
+        need = np.unique(np.concatenate(
+            [w.block_tables[s, :(int(w.context_lens[s]) + 15) // 16] for s in grp]).astype(np.int64))
+        idx = torch.from_numpy(need).to(DEV)
+        kp = host_raw(k_cache.index_select(0, idx))
+        vp = host_raw(v_cache.index_select(0, idx))
+        remap = np.full(w.num_blocks, -1, np.int64)
+        remap[need] = np.arange(len(need))
+        tasks = []
+        for s in grp:
+            L = int(w.context_lens[s])
+            tab = remap[w.block_tables[s, :(L + 15) // 16].astype(np.int64)].astype(np.int32)
+            a, b = int(qsl[s]), int(qsl[s + 1])
+            tasks.append((qh_all[a:b], tab, L, w.scale, w.dtype))
+        for s, ref in zip(grp, pool.run(kp, vp, tasks)):
+            rows_all.append(np.arange(qsl[s], qsl[s + 1], dtype=np.int64))
+            refs.append(ref)
+        del kp, vp
+    return np.concatenate(rows_all), np.concatenate(refs)

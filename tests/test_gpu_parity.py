@@ -5,7 +5,8 @@ import torch
 
 import workloads as W
 from oracle import cache_ops
-from tests._gpu import DEV, Run, assert_close, check_tables_in_pool, host_raw, oracle_rows, say, to_f64
+from tests._gpu import (DEV, Run, assert_close, check_tables_in_pool, host_raw, oracle_rows, oracle_rows_all,
+                        say, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -18,7 +19,8 @@ def pa():
 
 
 def run_and_check(pa, w, seqs=None, poison=False, label=None):
-    """Draw the workload's values, run (cache write +) forward, compare the listed sequences."""
+    """Draw the workload's values, run (cache write +) forward, compare every row of the
+    listed sequences (default: all of them) with the oracle."""
     label = label or w.name
     say(f"[case] {label}: S={w.num_seqs} T={w.num_tokens} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
         f"d={w.head_dim} {w.dtype} NB={w.num_blocks} maxL={w.max_context_len}")
@@ -31,8 +33,7 @@ def run_and_check(pa, w, seqs=None, poison=False, label=None):
         r.write(nk, nv, kc, vc)
     out = r.forward(q, kc, vc)
     r.check_status()
-    seqs = range(w.num_seqs) if seqs is None else seqs
-    rows, ref = oracle_rows(w, q, kc, vc, seqs)
+    rows, ref = oracle_rows_all(w, q, kc, vc, seqs)
     got = to_f64(out.index_select(0, torch.from_numpy(rows).to(DEV)))
     assert np.isfinite(got).all()
     assert_close(got, ref, w.dtype, label)
@@ -135,8 +136,7 @@ def test_tiny_decode_fp32(pa):
 # of an item, leaving lanes 1..63 in an inner loop with a stale item (a hang)
 # and reading a block id from the inactive lane 0 (the fault).  The workers now
 # have no per-lane branches (checked on the compiled code by
-# test_kernel_resources).  float32 with head_dim 128 stays unsupported: its
-# kernel needed more registers than it could hold without spilling.
+# test_kernel_resources), and both cases run.
 REJECTED = {}  # cases the host refuses (index -> message); none at present
 
 RAGGED = [
@@ -364,11 +364,11 @@ def test_batch_invariance(pa):
 # ---------------------------------------------------------------- the benchmark workloads
 
 def test_llama7b_decode_batch64(pa):
-    run_and_check(pa, W.llama7b_decode(0), seqs=[0, 1, 2, 17, 31, 40, 63])
+    run_and_check(pa, W.llama7b_decode(0))
 
 
 def test_gqa70b_decode_batch32(pa):
-    run_and_check(pa, W.gqa70b_decode(0), seqs=[0, 5, 31])
+    run_and_check(pa, W.gqa70b_decode(0))
 
 
 def test_gqa70b_decode_long_32k(pa):
@@ -376,9 +376,37 @@ def test_gqa70b_decode_long_32k(pa):
 
 
 def test_splitfuse_mixed_pass(pa):
-    # both prefill chunks (all 1024 rows) plus a spread of decode rows, after the cache write
+    # every row: both prefill chunks (1024 rows) and all 1024 decode rows, after the cache write
     w = W.splitfuse_mixed(0)
-    run_and_check(pa, w, seqs=[0, 1, 2, 3, 500, 1025])
+    run_and_check(pa, w)
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (16, 2)])
+def test_chunk_last_row_equals_decode_row(pa, hq, hkv):
+    """The last row of a prefill chunk and a decode query at the same position, over the
+    same cache, give the same attention (the prefill tile worker against the decode
+    workers: VALU for one query head per KV head, MFMA for GQA), each within tolerance
+    of the oracle and of each other."""
+    say(f"[case] chunk last row = decode row, Hq={hq} Hkv={hkv}")
+    w = W.random_ragged(51, "bf16", hq, hkv, 128, [300, 1], [2900, 700])
+    r = Run(w)
+    q, kc, vc, _, _ = W.make_values(w, DEV)
+    out = r.forward(q, kc, vc)
+    r.check_status()
+    last = int(w.query_start_loc[1]) - 1                 # the chunk's last row sits at position L - 1
+    wd = W.Workload(**{**w.__dict__})
+    wd.context_lens = w.context_lens[:1].copy()
+    wd.block_tables = w.block_tables[:1].copy()
+    wd.query_start_loc = np.array([0, 1], np.int32)
+    rd = Run(wd)
+    qd = q[last:last + 1].contiguous()
+    outd = rd.forward(qd, kc, vc)
+    rd.check_status()
+    rows, ref = oracle_rows_all(wd, qd, kc, vc)
+    got_chunk, got_dec = to_f64(out[last:last + 1]), to_f64(outd)
+    assert_close(got_dec, ref, "bf16", "decode row")
+    assert_close(got_chunk, ref, "bf16", "chunk last row")
+    assert_close(got_chunk, got_dec, "bf16", "chunk last row vs decode row")
 
 
 def test_parallel_sampling_workflow(pa):
