@@ -210,6 +210,31 @@ size_t pa_forward_shared_workspace_bytes(int32_t num_seqs, int32_t num_groups, i
                                          int32_t max_q_len, int32_t num_q_heads, int32_t num_kv_heads,
                                          int32_t head_dim, int32_t max_context_len, pa_dtype dtype);
 
+/* pa_forward_noalloc — pa_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, with the workspace taken from a
+ * static array the library holds on each GPU instead of a caller buffer.
+ * Arguments as pa_forward without workspace/workspace_bytes.  The array holds
+ * pa_forward_noalloc_max_workspace_bytes() bytes (64 MiB); a batch whose
+ * pa_forward_workspace_bytes(...) exceeds it fails with PA_ERR_INVALID and
+ * nothing is enqueued.  Nothing is allocated: the array lives in the library's
+ * device data from load until the process ends, one per GPU; its device
+ * address is looked up once per device (hipGetSymbolAddress, the first call
+ * with that device current).  Every call on one GPU uses the same array, and
+ * nothing in it needs clearing between calls (the first kernel of the pass
+ * writes every counter it reads); calls that may overlap in time on one GPU
+ * (other streams, other threads) race on it and must be ordered by the
+ * caller.  The caller still owns and passes inputs and outputs. */
+pa_status pa_forward_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, const int32_t* query_start_loc,
+                             int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                             int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                             pa_dtype dtype, int32_t* dev_status, void* stream);
+/* Size of pa_forward_noalloc's static workspace, in bytes. */
+size_t pa_forward_noalloc_max_workspace_bytes(void);
+
 /* Measurement hook, for timing only (changes nothing that is computed).
  * pa_forward runs five stages on its stream: 0 planner, 1 VALU worker (decode
  * rows with one query head per KV head), 2 MFMA worker (GQA decode rows and

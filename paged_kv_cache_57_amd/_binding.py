@@ -55,6 +55,9 @@ _SIGS = {
     "pa_forward_shared": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                  _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _vp, _vp]),
     "pa_forward_shared_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
+    "pa_forward_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                  _i32, _i32, _i32, _f32, _i32, _vp, _vp]),
+    "pa_forward_noalloc_max_workspace_bytes": (_sz, []),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pa_set_stage_events": (_i32, [_vp, _i32]),
     "pa_read_pages": (_i32, [_vp, _i64, _vp, _i32, _vp, _i32, _vp, _vp]),
@@ -207,6 +210,29 @@ def pa_forward(out, q, k_cache, v_cache, block_tables, context_lens, query_start
         S, T, int(max_q_len), int(max_context_len), hq, hkv, d, blk, nb, float(scale), _dtype_code(q),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _dev(dev_status, "dev_status", torch.int32), _stream(q, stream)))
+
+
+def pa_forward_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, max_q_len,
+                       max_context_len, scale, dev_status=None, stream=None):
+    """pa_forward with the library's static per-GPU workspace (no workspace argument)."""
+    import torch
+    nb, hkv, d, blk = _pool_dims(k_cache, v_cache)
+    T, hq, dq = q.shape
+    if dq != d or tuple(out.shape) != (T, hq, d):
+        raise PAError(PA_ERR_INVALID, "q/out must be [total_q_tokens, num_q_heads, head_dim]")
+    S = context_lens.shape[0]
+    if tuple(query_start_loc.shape) != (S + 1,) or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise PAError(PA_ERR_INVALID, "context_lens [S], query_start_loc [S+1], block_tables [S, M]")
+    _check(_lib.pa_forward_noalloc(
+        _dev(out, "out", q.dtype), _dev(q, "q", k_cache.dtype), _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(block_tables, "block_tables", torch.int32), block_tables.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), _dev(query_start_loc, "query_start_loc", torch.int32),
+        S, T, int(max_q_len), int(max_context_len), hq, hkv, d, blk, nb, float(scale), _dtype_code(q),
+        _dev(dev_status, "dev_status", torch.int32), _stream(q, stream)))
+
+
+def pa_forward_noalloc_max_workspace_bytes() -> int:
+    return int(_lib.pa_forward_noalloc_max_workspace_bytes())
 
 
 def pa_forward_shared(out, q, k_cache, v_cache, block_tables, context_lens, query_start_loc, groups, max_q_len,

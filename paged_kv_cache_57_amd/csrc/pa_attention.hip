@@ -31,6 +31,7 @@
 //    rescaling rule above.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -1436,4 +1437,64 @@ extern "C" pa_status pa_set_stage_events(void* const* events, int32_t num_events
   g_stage_events = num_events ? events : nullptr;
   g_num_stage_events = num_events;
   return ok();
+}
+
+// ---------------------------------------------------------------- without allocation
+// Workspace of pa_forward_noalloc: one array per GPU, in the code object's
+// device data, held from the library's load until the process ends.  Host code
+// never passes the array's own name to a kernel (on the host it is only a
+// stand-in); it takes the device address from hipGetSymbolAddress, once per
+// device with that device current, and passes that.
+namespace {
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+pa_status scratch_of_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PA_ERR_UNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(PA_ERR_HIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return ok();
+}
+}  // namespace
+
+extern "C" size_t pa_forward_noalloc_max_workspace_bytes(void) { return kScratchBytes; }
+
+extern "C" pa_status pa_forward_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, const int32_t* query_start_loc,
+                                        int32_t num_seqs, int32_t total_q_tokens, int32_t max_q_len,
+                                        int32_t max_context_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                                        pa_dtype dtype, int32_t* dev_status, void* stream) {
+  const char* fn = "pa_forward_noalloc";
+  const size_t need = pa_forward_workspace_bytes(num_seqs, total_q_tokens, max_q_len, num_q_heads, num_kv_heads,
+                                                 head_dim, max_context_len, dtype);
+  if (need > kScratchBytes)
+    return fail(PA_ERR_INVALID, "%s: this batch needs %zu bytes of workspace, the static workspace holds %zu", fn,
+                need, kScratchBytes);
+  void* ws = nullptr;
+  if (num_seqs > 0 && total_q_tokens > 0) {
+    const pa_status st = scratch_of_current_device(fn, &ws);
+    if (st != PA_OK) return st;
+  }
+  return forward_impl(fn, out, q, k_cache, v_cache, block_tables, max_blocks_per_seq, context_lens, query_start_loc,
+                      nullptr, 0, num_seqs, total_q_tokens, max_q_len, max_context_len, num_q_heads, num_kv_heads,
+                      head_dim, block_size, num_blocks, scale, dtype, ws, kScratchBytes, dev_status, stream);
 }
