@@ -32,6 +32,7 @@
 #include <algorithm>
 #include <cmath>
 #include <mutex>
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -43,13 +44,14 @@ enum { CLS_NONE = 0, CLS_VALU = 1, CLS_MFMA = 2, CLS_TILE = 3 };
 constexpr int kPartValu = 512;          // keys per VALU partition
 constexpr int kPartMfmaDecode = 256;    // keys per partition of a one-row GQA decode tile
 constexpr int kPartMfmaPrefill = 1024;  // keys per partition of a small multi-row tile
-constexpr int kPartTile = 1024;         // keys per partition of a 128-row tile
+constexpr int kPartTile = 1024;         // keys per partition of a 256-row tile
 constexpr int kTileRows = 16;           // query rows per MFMA item
-constexpr int kTileWaves = 4;           // wavefronts per TILE workgroup, 32 rows each
+constexpr int kTileWaves = 8;           // wavefronts per TILE workgroup, 32 rows each
 constexpr int kTileStages = 3;          // LDS stages of the TILE worker's load pipeline
 constexpr int kBigRows = 32 * kTileWaves;  // query rows per TILE item
 constexpr int kMaxWorkerGroups = 2048;  // persistent workgroups per worker launch
-constexpr int kMaxTileGroups = 512;     // TILE workgroups (two per compute unit)
+constexpr int kMaxTileGroups = 256;     // TILE workgroups (one per compute unit)
+constexpr int kXcds = 8;                // XCDs (each with its own L2); TILE items are sliced per XCD
 constexpr float kLazyRescale = 8.f;     // MFMA worker: raise the exponent reference only past this growth (log2)
 constexpr float kTileLazyRescale = 7.f; // TILE worker: the same, bounded so that 2^8 p stays below the half maximum
 constexpr int kMergeSplitParts = 32;    // partitions per row from which four wavefronts merge a row
@@ -116,7 +118,7 @@ struct AttnParams {
   int32_t Hq, Hkv, G, num_blocks;
   float scale_log2;
   int32_t is_f32;
-  int32_t* ctrl;  // [2] VALU items, [3] MFMA items, [4] TILE items, [5] rows to merge, [6] TILE tickets
+  int32_t* ctrl;  // [2] VALU items, [3] MFMA items, [4] TILE items, [5] rows to merge, [8..15] TILE tickets per XCD slice
   int32_t* pre_v;  // exclusive prefix over sequences of VALU items, [S + 1]
   int32_t* pre_m;  // ... of MFMA items
   int32_t* pre_t;  // ... of TILE items
@@ -369,7 +371,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
     p.ctrl[3] = carry[1];
     p.ctrl[4] = carry[2];
     p.ctrl[5] = carry[3];
-    p.ctrl[6] = 0;  // TILE work tickets handed out so far
+    for (int x = 0; x < kXcds; ++x) p.ctrl[8 + x] = 0;  // TILE tickets handed out so far, per XCD slice
   }
 }
 
@@ -794,308 +796,383 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------- TILE worker
-// One workgroup per item: kBigRows query rows sharing one KV head x one key
-// partition.  Each wavefront owns 32 rows (two 16-row MFMA tiles); the
-// products and lane layouts are those of the MFMA worker: lane l = r + 16g
-// holds the scores of its row for keys 8g .. 8g+7 of a 32-key step, key
-// operands come with the permuted row order that gives that layout, and the
-// value operand of lane l is one 16-byte piece of one page.
-// Memory: every thread loads its 16-byte pieces of a step two steps before
-// the step is computed (two register sets) and stores them into a
-// three-stage LDS ring one step before; the LDS image of a step holds the
-// operands in the order the lanes read them (piece 64 i + l is lane l's
-// operand i), so every operand read is 64 consecutive 16-byte pieces and
-// every wavefront reads the same image.  One barrier per step publishes the
-// stored stage and frees the stage read two steps earlier.
-// Scores stay unscaled until the exponent: p = 2^(s·c − m) with
-// c = |scale|·log2 e is one FMA per score (a negative scale flips the sign
-// bits of q instead, which is exact).  The exponent reference m of a row is
-// raised only when the row's maximum grows past it by more than
-// kTileLazyRescale: all weights stay below 2^kTileLazyRescale, O and l share
-// the reference, and O / l is unchanged.
-// P·V runs on the half-precision MFMA: the weights enter as p·2^8 rounded to
-// half (below 2^15; relative error 2^-11, as accurate as splitting p into two
-// bfloat16 parts, with one MFMA instead of two), the values as v·2^-8 in half,
-// converted once per workgroup when a step is stored to LDS (exact for
-// |v| < 2^24 up to an absolute 2^-16 on tiny magnitudes), so the products are
-// p·v.  The row sum l comes from the same MFMA with an all-ones value
-// operand: it adds exactly the rounded weights that P·V used.
-// Workgroup g starts with item g and then takes tickets from a counter the
-// planner zeroes: one atomic per item, by one lane, with barriers on both
-// sides of the shared ticket (items differ in length near the diagonal, and
-// a fixed stride left the slowest workgroup with a whole item more than the
-// mean).  The lane-0 region is the only per-lane branch of the worker; the
-// barriers keep the compiler from moving anything of the work across it.
+// One workgroup of kTileWaves wavefronts per item: kBigRows query rows sharing
+// one KV head x one key partition; wavefront w owns rows 32w .. 32w+31 of the
+// item.  Every product is a 32x32x16 MFMA (v_mfma_f32_32x32x16_*):
+//  Scores, transposed: Sᵀ[key][row] = K · Qᵀ, 32 keys x 32 rows per MFMA,
+//  D/16 MFMAs over the head dimension.  Lane l holds row l%32 and, in
+//  accumulator j, the key tile_key(j, l/32) of the 32-key step: the key
+//  operand's rows are loaded in a permuted order (bits 2 and 3 of the key
+//  index swapped) so that each lane ends with 8 consecutive keys per 16-key
+//  block, which is the layout P·V needs for its B operand, with no exchange.
+//  Output, transposed: Oᵀ[dim][row] += Vᵀ · Pᵀ, 32 dims x 32 rows x 16 keys
+//  per MFMA; the value operand of lane l is 8 consecutive keys of dim l%32,
+//  i.e. one 16-byte piece of a value page [D][16].
+// Each lane's row statistics: the two lane halves l, l+32 hold the same row
+// for different keys, so a row max is a 16-value max and one lane swap.
+// Steps of 32 keys: all operands of a step (8 KiB of keys, 8 KiB of values at
+// D = 128) are staged in LDS in the order the lanes read them (piece 64b + l is
+// lane l's operand of block b), so every operand read is 64 consecutive
+// 16-byte pieces.  Every wavefront loads two 1 KiB blocks of each step, three
+// steps ahead into one of two register sets, and stores them two steps ahead
+// into a three-stage ring; one barrier per step publishes the stored stage and
+// frees the stage read two steps earlier.  The 256 rows of an item share every
+// key and value piece it reads from HBM (or L2).
+// Softmax ("第 15 章" §15.1 recurrence): scores stay unscaled until the
+// exponent (p = 2^(s·c − m) with c = |scale|·log2 e, one FMA; a negative scale
+// flips the sign bits of q instead, which is exact), and a row's reference m
+// is raised only when its maximum grows past it by more than
+// kTileLazyRescale (O and l share the reference, so O / l is unchanged).
+// P·V precision: the weights enter the half-precision MFMA as 2^8 p rounded
+// to half (relative error 2^-11; 2^8 p < 2^15 by the lazy-rescale bound) and
+// the values as half, converted once per workgroup when they are stored to
+// LDS (exact for bfloat16 values of magnitude below 2^16 down to 2^-17); the
+// row sum adds exactly the rounded weights (v_dot2_f32_f16), and 2^8 scales O
+// and l alike.  A bfloat16 value of magnitude 2^16 or more would overflow
+// half: the converting lanes check every value they stage, and an item that
+// met one is computed again with the values left in bfloat16 and the weights
+// split into a bfloat16 high and low part (two MFMAs, weights exact to about
+// 2^-16), which holds for every finite input.
+// Work distribution: items are numbered so that the row tiles of one (KV
+// head, partition) are consecutive; the item list is cut into eight equal
+// slices, one per XCD (each XCD has its own L2), and the workgroups of an XCD
+// take tickets from their slice first, then from the other slices in turn.
+// Row tiles sharing keys and values therefore run at about the same time on
+// one L2, which serves the second read.  One atomic per item, by one thread
+// between two barriers: the one per-lane branch of the worker.
 template <int D>
-__global__ __launch_bounds__(64 * kTileWaves, 2) void tile_attn_kernel(AttnParams p) {
-  constexpr int KS = D / 32;              // k-steps of the score product
-  constexpr int NJ = D / 16;              // 16-dim column blocks of the output
-  constexpr int NI = 2 * KS + NJ;         // 1 KiB operand blocks per step: keys (2 chains x KS), then values
-  constexpr int IPW = NI / kTileWaves;    // blocks each wavefront loads per step
-  static_assert(NI % kTileWaves == 0, "the blocks of a step split evenly over the wavefronts");
-  static_assert(IPW == 2 || IPW == 4, "loads pair the page halves of two blocks of one kind");
+struct TileShape {
+  static constexpr int KB = D / 16;           // key operand blocks per step (one per score MFMA)
+  static constexpr int DB = D / 32;           // 32-dim blocks of the output
+  static constexpr int VB = 2 * DB;           // value operand blocks per step: dim block x 16-key block
+  static constexpr int NB = KB + VB;          // 1 KiB operand blocks per step
+  static constexpr int BPW = NB / kTileWaves; // blocks each wavefront loads per step
+  static_assert(NB % kTileWaves == 0 && BPW >= 1, "the blocks of a step split evenly over the wavefronts");
+};
+
+// Marks a rarely taken, wave-uniform branch that must stay a branch: the
+// compiler would otherwise run its body on every pass with neutral values
+// (for example multiply the output by a rescale factor of 1), which costs more
+// than the branch.  An empty volatile asm cannot be executed speculatively.
+__device__ inline void keep_branch() { asm volatile(""); }
+
+// In-step key of accumulator j of a score MFMA for lane half h.
+__device__ inline int tile_key(int j, int h) { return 16 * (j >> 3) + 8 * h + (j & 7); }
+
+constexpr int kHwRegXccId = (3 << 11) | 20;  // s_getreg operand: HW_REG_XCC_ID, bits 3:0
+
+template <int D>
+__global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParams p) {
+  using TS = TileShape<D>;
+  constexpr int KB = TS::KB, DB = TS::DB, NB = TS::NB, BPW = TS::BPW;
   static_assert(kPartTile % 32 == 0 && kPartTile <= 64 * kBlock, "a partition is whole steps of at most 64 pages");
-  __shared__ u32x4 stage[kTileStages][NI * 64];
+  __shared__ u32x4 stage[kTileStages][NB * 64];
   __shared__ int skip[kSkip];
+  __shared__ int ticket;
+  __shared__ int wave_flag[kTileWaves];
 
   const int lane = threadIdx.x & 63;
   const int wv = wave_uniform((int)(threadIdx.x >> 6));
-  const int r = lane & 15, g4 = lane >> 4;
+  const int n = lane & 31, h = lane >> 5;
   const int total = wave_uniform(p.ctrl[4]);
   const bf16_t* __restrict__ kc = (const bf16_t*)p.k_cache;
   const bf16_t* __restrict__ vc = (const bf16_t*)p.v_cache;
-  const int64_t page_elems = (int64_t)kBlock * D;
-  const int64_t blk_elems = (int64_t)p.Hkv * page_elems;
+  const int blk_elems = p.Hkv * kBlock * D;  // elements of one physical block (all KV heads), below 2^31
   const float csc = fmaxf(fabsf(p.scale_log2), 1e-30f);  // scale 0 gives equal weights, as it should
   const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
-  const f16x8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
   const SkipTable tab = stage_skip(skip, p.pre_t, p.num_ent);
+  const int xcc = wave_uniform(__builtin_amdgcn_s_getreg(kHwRegXccId) & (kXcds - 1));
+  const int per_q = (total + kXcds - 1) / kXcds;  // items per slice
 
-  __shared__ int ticket;
+  // Next item: from this XCD's slice, then the following slices in turn; -1 when all are done.
+  int qi = 0;
   auto next_item = [&]() {
-    __syncthreads();  // every thread has read the previous ticket
-    if (threadIdx.x == 0) ticket = atomicAdd(p.ctrl + 6, 1);
-    __syncthreads();
-    return wave_uniform(ticket) + (int)gridDim.x;
+#pragma clang loop unroll(disable)
+    while (qi < kXcds) {
+      const int qq = (xcc + qi) & (kXcds - 1);
+      __syncthreads();  // every thread has read the previous ticket (and is done with the stages)
+      if (threadIdx.x == 0) ticket = atomicAdd(p.ctrl + 8 + qq, 1);
+      __syncthreads();
+      const int t = wave_uniform(ticket);
+      const int first = qq * per_q;
+      if (t < min(per_q, total - first)) return first + t;
+      ++qi;
+    }
+    return -1;
   };
-  for (int item = (int)blockIdx.x; item < total; item = next_item()) {
+
+  for (;;) {
+    const int item = next_item();
+    if (item < 0) break;
     const SeqHit hit = find_seq(skip, tab, p.pre_t, p.num_ent, item);
     const int s = hit.s;
     const int local = item - hit.first;
     const SeqInfo si = seq_record(p, s);
     const SeqWork w = seq_work(false, p.G, p.Hq, p.Hkv, si.q_len, si.L);
-    const int pidx = local % w.nparts;
-    const int rest = local / w.nparts;
-    const int kvh = rest % p.Hkv;
-    const int tile = rest / p.Hkv;
     const int rows_total = si.q_len * p.G;
+    const int ntiles = (rows_total + kBigRows - 1) / kBigRows;
+    const int tile = local % ntiles;  // row tiles of one (KV head, partition) are consecutive items
+    const int rest = local / ntiles;
+    const int pidx = rest % w.nparts;
+    const int kvh = rest / w.nparts;
     const int first = si.L - si.q_len;  // position of query row 0
     const int tile_last = min(tile * kBigRows + kBigRows - 1, rows_total - 1);
     const int kv_lo = pidx * w.part;
     const int kv_hi = min(kv_lo + w.part, first + tile_last / p.G + 1);
     if (kv_lo >= kv_hi) continue;  // no row of the tile sees this partition: the merge skips it
 
-    // this wavefront's rows; padding rows repeat the last row (see the MFMA worker)
+    // this wavefront's rows; padding rows repeat the last row (they store the same bytes to its address)
     const int row0 = tile * kBigRows + 32 * wv;
     const bool active = row0 < rows_total;
     const int w_pos_lo = first + min(row0, rows_total - 1) / p.G;
-    const int w_kv_hi = min(kv_hi, first + min(row0 + 31, rows_total - 1) / p.G + 1);
-    int pos_r[2], tok[2], hh[2];
-    bf16x8 qop[2][KS];
+    const int w_kv_hi = active ? min(kv_hi, first + min(row0 + 31, rows_total - 1) / p.G + 1) : kv_lo;
+    const int R = min(row0 + n, rows_total - 1);
+    const int hh = kvh * p.G + R % p.G;
+    const int tok = si.a + R / p.G;
+    const int pos_r = first + R / p.G;
+    bf16x8 qop[KB];
+    {
+      const bf16_t* qrow = (const bf16_t*)p.q + ((int64_t)tok * p.Hq + hh) * D;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int R = min(row0 + 16 * t + r, rows_total - 1);
-      const int qi = R / p.G;
-      hh[t] = kvh * p.G + R % p.G;
-      tok[t] = si.a + qi;
-      pos_r[t] = first + qi;
-      const bf16_t* qrow = (const bf16_t*)p.q + ((int64_t)tok[t] * p.Hq + hh[t]) * D;
-#pragma unroll
-      for (int k = 0; k < KS; ++k) {
-        const u32x4 qw = ld16(qrow + 32 * k + 8 * g4);
-        qop[t][k] = __builtin_bit_cast(bf16x8, u32x4{qw[0] ^ qflip, qw[1] ^ qflip, qw[2] ^ qflip, qw[3] ^ qflip});
+      for (int kk = 0; kk < KB; ++kk) {
+        const u32x4 qw = ld16(qrow + 16 * kk + 8 * h);
+        qop[kk] = __builtin_bit_cast(bf16x8, u32x4{qw[0] ^ qflip, qw[1] ^ qflip, qw[2] ^ qflip, qw[3] ^ qflip});
       }
     }
 
     const int nblk = (kv_hi - kv_lo + kBlock - 1) / kBlock;
     const int bidv = load_block_ids(p, s, kv_lo / kBlock, nblk, lane);
     const int nsteps = (kv_hi - kv_lo + 31) / 32;
+    const int nw = (w_kv_hi - kv_lo + 31) / 32;  // steps this wavefront computes (a prefix of the item's)
+    const int head_off = kvh * kBlock * D;  // element offset of the KV head inside a block (below 2^31)
 
-    // The pieces of a step: key block (mm, k) holds, for compute lane
-    // l = r + 16g, key 8((r/4)%2) + 4mm + r%4 of page r/8, dims 32k + 8g ..;
-    // value block j holds column 16j + r, keys 8(g%2) .. of page g/2.  This
-    // wavefront stores blocks ii(u) (u < IPW; blocks of one pair u = 2j, 2j+1
-    // are both keys or both values), and each of its loads reads ONE page:
-    // load q takes page q%2 of the pair q/2, loading lane λ fetching the piece
-    // of block u = 2(q/2) + λ/32 for the (λ%32)-th compute lane on that page
-    // and storing it at that lane's place in the LDS image.  A load's address
-    // is then a wave-uniform page base plus a constant 32-bit lane offset.
-    // Pages past the last one (odd counts) read the last page again: their
-    // scores are masked, their values zeroed, and every address stays inside
-    // the pool.
-    auto block_of = [&](int u) { return IPW == 4 ? wv + kTileWaves * u : IPW * wv + u; };  // wave-uniform
-    uint32_t loff[IPW];
-    int ldst[IPW];
+    // The blocks this wavefront loads: block b = wv + kTileWaves u; b < KB is key block b
+    // (lane l: key of in-step index π(l%32) with bits 2 and 3 swapped, dims 16b + 8(l/32) ..),
+    // else value block b - KB = 2 db + kb (lane l: dim 32 db + l%32, keys 16 kb + 8(l/32) ..).
+    uint32_t loff[BPW];
+    bool second_page[BPW];
 #pragma unroll
-    for (int q = 0; q < IPW; ++q) {
-      const int pq = q & 1, ii = block_of(2 * (q >> 1) + (lane >> 5)), m = lane & 31;
-      if (ii < 2 * KS) {  // key block
-        const int rr = 8 * pq + (m & 7), gg = m >> 3;
-        const int kr = 8 * ((rr >> 2) & 1) + (rr & 3);
-        loff[q] = (uint32_t)((gg * kBlock + kr) * 8 + ((ii % KS) * 4 * kBlock + 4 * (ii / KS)) * 8);
-        ldst[q] = ii * 64 + rr + 16 * gg;
-      } else {  // value block
-        const int l = 32 * pq + m;
-        loff[q] = (uint32_t)((l & 15) * kBlock + 8 * ((l >> 4) & 1) + (ii - 2 * KS) * 16 * kBlock);
-        ldst[q] = ii * 64 + l;
+    for (int u = 0; u < BPW; ++u) {
+      const int b = wv + kTileWaves * u;
+      // element offset inside the block's (physical block, KV head) page run, KV head included
+      if (b < KB) {
+        const int kp = 8 * ((n >> 2) & 1) + 4 * ((n >> 3) & 1) + (n & 3);
+        loff[u] = (uint32_t)(head_off + ((2 * b + h) * kBlock + kp) * 8);
+        second_page[u] = n >= 16;
+      } else {
+        const int vb = b - KB;
+        loff[u] = (uint32_t)(head_off + (32 * (vb >> 1) + n) * kBlock + 8 * h);
+        second_page[u] = (vb & 1) != 0;
       }
     }
-    const int64_t head_off = (int64_t)kvh * page_elems;
-    auto fetch = [&](int st, u32x4 (&reg)[IPW]) {
-      const int64_t pg0 = (int64_t)readlane(bidv, min(2 * st, nblk - 1)) * blk_elems + head_off;
-      const int64_t pg1 = (int64_t)readlane(bidv, min(2 * st + 1, nblk - 1)) * blk_elems + head_off;
+    auto fetch = [&](int st, u32x4 (&reg)[BPW]) {
+      const int64_t pg0 = (int64_t)readlane(bidv, min(2 * st, nblk - 1)) * (int64_t)blk_elems;
+      const int64_t pg1 = (int64_t)readlane(bidv, min(2 * st + 1, nblk - 1)) * (int64_t)blk_elems;
 #pragma unroll
-      for (int q = 0; q < IPW; ++q) {
-        const bool key = block_of(2 * (q >> 1)) < 2 * KS;  // wave-uniform
-        const bf16_t* base = (key ? kc : vc) + ((q & 1) ? pg1 : pg0);
-        reg[q] = ld16(base + loff[q]);
-      }
-    };
-    // values enter LDS already as half x 2^-8 (each converted once per workgroup)
-    auto put = [&](const u32x4 (&reg)[IPW], int stg) {
-#pragma unroll
-      for (int q = 0; q < IPW; ++q) {
-        const bool key = block_of(2 * (q >> 1)) < 2 * KS;
-        stage[stg][ldst[q]] = key ? reg[q] : bf16x8_to_f16x8_scaled(reg[q]);
+      for (int u = 0; u < BPW; ++u) {
+        const bool key = wv + kTileWaves * u < KB;  // wave-uniform
+        reg[u] = ld16((key ? kc : vc) + (second_page[u] ? pg1 : pg0) + loff[u]);
       }
     };
 
-    float m_used[2] = {kNegInf, kNegInf};
-    f32x4 oacc[2][NJ], lacc[2];  // lacc: row sums of the weights x 2^8, four equal copies
+    auto pass = [&](auto exact_tag) {
+      constexpr bool kExact = decltype(exact_tag)::value;
+      bool out_of_range = false;
+      // Stage step st: keys as loaded; values zeroed past kv_hi (the pool there may hold
+      // anything), then converted to half unless kExact, with their magnitudes checked.
+      auto put = [&](u32x4 (&reg)[BPW], int st) {
+        u32x4* img = stage[st % kTileStages];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      lacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int u = 0; u < BPW; ++u) {
+          const int b = wv + kTileWaves * u;
+          u32x4 v = reg[u];
+          if (b >= KB) {
+            if (kv_lo + 32 * st + 32 > kv_hi) {  // wave-uniform: the step reaches past the partition
+              const int kfirst = kv_lo + 32 * st + 16 * ((b - KB) & 1) + 8 * h;  // key of the piece's first value
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) oacc[t][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-    auto compute_step = [&](int st) {
-      const int kbase = kv_lo + 32 * st;
-      if (!active || kbase >= w_kv_hi) return;  // wave-uniform: this wavefront's rows see no key of the step
-      const u32x4* img = stage[st % kTileStages];
-      f32x4 c[2][2];  // [tile][chain]
+              for (int e = 0; e < 4; ++e)
+                v[e] &= (kfirst + 2 * e < kv_hi ? 0x0000ffffu : 0u) | (kfirst + 2 * e + 1 < kv_hi ? 0xffff0000u : 0u);
+            }
+            if constexpr (!kExact) {
+              float mx = 0.f;
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
-        bf16x8 kop[KS];
-#pragma unroll
-        for (int k = 0; k < KS; ++k) kop[k] = __builtin_bit_cast(bf16x8, img[(mm * KS + k) * 64 + lane]);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          c[t][mm] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int k = 0; k < KS; ++k)
-            c[t][mm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[k], qop[t][k], c[t][mm], 0, 0, 0);
-        }
-      }
-      // unscaled scores of row r of tile t for keys kbase + 8 g4 + e
-      float sc[2][8];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sc[t][e] = c[t][e >> 2][e & 3];
-      if (kbase + 31 > w_pos_lo) {  // some key of the step lies past some row's position
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) sc[t][e] = kbase + 8 * g4 + e <= pos_r[t] ? sc[t][e] : kNegInf;
-      }
-      float mloc[2];
-      bool grow = false;
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        float mx = fmaxf(fmaxf(fmaxf(sc[t][0], sc[t][1]), fmaxf(sc[t][2], sc[t][3])),
-                         fmaxf(fmaxf(sc[t][4], sc[t][5]), fmaxf(sc[t][6], sc[t][7])));
-        mx = max_over_rows(mx);
-        mloc[t] = mx * csc;  // -inf stays -inf (csc > 0)
-        grow = grow || mloc[t] > m_used[t] + kTileLazyRescale;
-      }
-      if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const float m_new = fmaxf(m_used[t], mloc[t]);
-          const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_used[t] - m_new);
-          lacc[t] *= alpha;
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) oacc[t][j] *= alpha;
-          m_used[t] = m_new;
-        }
-      }
-      f16x8 pw[2];  // weights x 2^8 in half, keys 8 g4 + e of the lane's row
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const float nmu = (m_used[t] == kNegInf ? 0.f : -m_used[t]) + 8.f;  // a row that sees no key yet has weights 0
-        uint32_t w4[4];
-#pragma unroll
-        for (int e = 0; e < 8; e += 2)
-          w4[e >> 1] = pack_f16x2(fast_exp2(fmaf(sc[t][e], csc, nmu)), fast_exp2(fmaf(sc[t][e + 1], csc, nmu)));
-        pw[t] = __builtin_bit_cast(f16x8, u32x4{w4[0], w4[1], w4[2], w4[3]});
-      }
-      u32x4 vraw[NJ];
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) vraw[j] = img[(2 * KS + j) * 64 + lane];
-      if (kbase + 32 > kv_hi) {
-        // keys at or past kv_hi may hold anything (even NaN): zero them in the value operand
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const int key = kbase + 8 * g4 + e;
-          const uint32_t keep = (key < kv_hi ? 0x0000ffffu : 0u) | (key + 1 < kv_hi ? 0xffff0000u : 0u);
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) vraw[j][e >> 1] &= keep;
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-          oacc[t][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vraw[j]), pw[t], oacc[t][j], 0, 0, 0);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) lacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ones, pw[t], lacc[t], 0, 0, 0);
-    };
-
-    // The loop is unrolled by two so that each register set stays in fixed
-    // registers, and every half requests one step (past the last step it
-    // requests the last one again): the number of loads in flight is then
-    // the same on every path, and the compiler waits for exactly the set
-    // being stored.  The loop has a single exit, at its top: exits in the
-    // middle of the body reach the loop head in the compiler's control flow
-    // with the other set's loads still pending, and it then waited for all
-    // loads at the head of every pass, which made the prefetch one step deep.
-    u32x4 rset0[IPW], rset1[IPW];
-    __syncthreads();  // every wavefront is done with the stages of the previous item
-    fetch(0, rset0);
-    fetch(min(1, nsteps - 1), rset1);
-    put(rset0, 0);
-    __syncthreads();
-    int st = 0;
-    for (; st + 2 < nsteps; st += 2) {
-      fetch(st + 2, rset0);
-      compute_step(st);
-      put(rset1, (st + 1) % kTileStages);
-      __syncthreads();
-      fetch(min(st + 3, nsteps - 1), rset1);
-      compute_step(st + 1);
-      put(rset0, (st + 2) % kTileStages);
-      __syncthreads();
-    }
-    // the last one or two steps: stage st holds step st, rset1 step st + 1
-    compute_step(st);
-    if (st + 1 < nsteps) {
-      put(rset1, (st + 1) % kTileStages);
-      __syncthreads();
-      compute_step(st + 1);
-    }
-
-    if (active) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const float l = lacc[t][0] * 0.00390625f;  // undo the 2^8 of the weights
-        if (w.nparts == 1) {
-          bf16_t* orow = (bf16_t*)p.out + ((int64_t)tok[t] * p.Hq + hh[t]) * D;
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            const u32x2 pk = {pack_bf16x2(oacc[t][j][0] / l, oacc[t][j][1] / l),
-                              pack_bf16x2(oacc[t][j][2] / l, oacc[t][j][3] / l)};
-            *reinterpret_cast<u32x2*>(orow + 16 * j + 4 * g4) = pk;
+              for (int e = 0; e < 4; ++e) {
+                const float lo = bf16_lo(v[e]), hi = bf16_hi(v[e]);
+                mx = fmaxf(mx, fmaxf(fabsf(lo), fabsf(hi)));
+                v[e] = pack_f16x2(lo, hi);
+              }
+              out_of_range |= !(mx < 65536.f);
+            }
           }
-        } else {
-          float* slot = p.partials + (((int64_t)tok[t] * p.Hq + hh[t]) * p.maxparts + pidx) * slot_floats(D);
+          img[b * 64 + lane] = v;
+        }
+      };
+
+      float m_used = kNegInf, lsum = 0.f;
+      f32x16 oacc[DB];
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) *reinterpret_cast<f32x4*>(slot + 16 * j + 4 * g4) = oacc[t][j];
-          slot[D] = m_used[t];
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) oacc[db][j] = 0.f;
+
+      auto scores = [&](int st, f32x16& c) {
+        const u32x4* img = stage[st % kTileStages];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) c[j] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk)
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, img[kk * 64 + lane]), qop[kk], c, 0,
+                                                      0, 0);
+      };
+
+      // softmax of step st (scores in c) and its P·V
+      auto softmax_pv = [&](int st, f32x16& c) {
+        const int kbase = kv_lo + 32 * st;
+        float sc[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) sc[j] = c[j];
+        if (kbase + 31 > w_pos_lo || kbase + 32 > kv_hi) {  // some key lies past some row's position or the partition
+          keep_branch();
+          // in-step key 16(j/8) + 8h + j%8 is visible iff it is <= lim
+          const int lim = min(kv_hi - 1, pos_r) - kbase - 8 * h;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) sc[j] = 16 * (j >> 3) + (j & 7) <= lim ? sc[j] : kNegInf;
+        }
+        float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11])),
+                             fmaxf(fmaxf(sc[12], sc[13]), fmaxf(sc[14], sc[15]))));
+        {
+          typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+          const u32x2v sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float mloc = mx * csc;  // -inf stays -inf (csc > 0)
+        if (__builtin_amdgcn_ballot_w64(mloc > m_used + kTileLazyRescale)) {
+          keep_branch();
+          const float m_new = fmaxf(m_used, mloc);
+          const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_used - m_new);
+          lsum *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+          m_used = m_new;
+        }
+        // a row that sees no key yet has weights 0; the half path carries 2^8 p
+        const float nmu = (m_used == kNegInf ? 0.f : -m_used) + (kExact ? 0.f : 8.f);
+        const u32x4* img = stage[st % kTileStages];
+        if constexpr (!kExact) {
+          f16x8 pw[2];
+          const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            uint32_t w4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              w4[e] = pack_f16x2(fast_exp2(fmaf(sc[8 * kb + 2 * e], csc, nmu)),
+                                 fast_exp2(fmaf(sc[8 * kb + 2 * e + 1], csc, nmu)));
+              lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w4[e]), ones, lsum, false);
+            }
+            pw[kb] = __builtin_bit_cast(f16x8, u32x4{w4[0], w4[1], w4[2], w4[3]});
+          }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                  __builtin_bit_cast(f16x8, img[(KB + 2 * db + kb) * 64 + lane]), pw[kb], oacc[db], 0, 0, 0);
+        } else {
+          bf16x8 phi[2], plo[2];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            uint32_t hw[4], lw[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float p0 = fast_exp2(fmaf(sc[8 * kb + 2 * e], csc, nmu));
+              const float p1 = fast_exp2(fmaf(sc[8 * kb + 2 * e + 1], csc, nmu));
+              hw[e] = pack_bf16x2(p0, p1);
+              lw[e] = pack_bf16x2(p0 - bf16_lo(hw[e]), p1 - bf16_hi(hw[e]));
+              lsum += p0 + p1;
+            }
+            phi[kb] = __builtin_bit_cast(bf16x8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+            plo[kb] = __builtin_bit_cast(bf16x8, u32x4{lw[0], lw[1], lw[2], lw[3]});
+          }
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+              const bf16x8 va = __builtin_bit_cast(bf16x8, img[(KB + 2 * db + kb) * 64 + lane]);
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, phi[kb], oacc[db], 0, 0, 0);
+              oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, plo[kb], oacc[db], 0, 0, 0);
+            }
+        }
+      };
+
+      // One step of the loop, unrolled by two so that each register set stays in fixed
+      // registers: set rs_put holds step st+2 (stored at the end), set rs_fetch receives
+      // step st+3.  Fetches past the last step read the last step again, so the number of
+      // loads in flight is the same on every path.
+      auto step = [&](int st, u32x4 (&rs_fetch)[BPW], u32x4 (&rs_put)[BPW]) {
+        __syncthreads();  // stage st+1 is stored; stage st-1 is free
+        fetch(min(st + 3, nsteps - 1), rs_fetch);
+        if (st < nw) {
+          f32x16 c;
+          scores(st, c);
+          softmax_pv(st, c);
+        }
+        put(rs_put, st + 2);
+      };
+
+      u32x4 rset0[BPW], rset1[BPW];
+      __syncthreads();  // every wavefront is done with the stages of the previous item (or pass)
+      fetch(0, rset0);
+      fetch(min(1, nsteps - 1), rset1);
+      put(rset0, 0);
+      fetch(min(2, nsteps - 1), rset0);
+      put(rset1, 1);
+      __syncthreads();
+      int st = 0;
+      for (; st + 2 <= nsteps; st += 2) {
+        step(st, rset1, rset0);
+        step(st + 1, rset0, rset1);
+      }
+      if (st < nsteps) step(st, rset1, rset0);
+
+      if (active) {
+        typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+        const u32x2v sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
+        const float l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);  // the row's two lane halves
+        if (w.nparts == 1) {
+          bf16_t* orow = (bf16_t*)p.out + ((int64_t)tok * p.Hq + hh) * D;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const u32x2 pk = {pack_bf16x2(oacc[db][4 * i] / l, oacc[db][4 * i + 1] / l),
+                                pack_bf16x2(oacc[db][4 * i + 2] / l, oacc[db][4 * i + 3] / l)};
+              *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * i + 4 * h) = pk;
+            }
+        } else {
+          float* slot = p.partials + (((int64_t)tok * p.Hq + hh) * p.maxparts + pidx) * slot_floats(D);
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              *reinterpret_cast<f32x4*>(slot + 32 * db + 8 * i + 4 * h) =
+                  f32x4{oacc[db][4 * i], oacc[db][4 * i + 1], oacc[db][4 * i + 2], oacc[db][4 * i + 3]};
+          // the half path's O and l carry 2^8: the state (m − 8, l, O) is the same softmax state
+          slot[D] = m_used == kNegInf ? kNegInf : m_used - (kExact ? 0.f : 8.f);
           slot[D + 1] = l;
         }
       }
-    }
+      return out_of_range;
+    };
+
+    const bool oor = pass(std::false_type{});
+    wave_flag[wv] = __builtin_amdgcn_ballot_w64(oor) != 0 ? 1 : 0;  // every lane writes the wave's value
+    __syncthreads();
+    int any = 0;
+#pragma unroll
+    for (int k = 0; k < kTileWaves; ++k) any |= wave_flag[k];
+    if (wave_uniform(any)) pass(std::true_type{});
   }
 }
 

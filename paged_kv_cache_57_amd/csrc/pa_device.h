@@ -14,6 +14,7 @@ constexpr int kWave = 64;   // CDNA wavefront width
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -62,20 +63,6 @@ __device__ inline uint32_t pack_f16x2(float a, float b) {
 // Low / high bfloat16 of a packed pair, widened to float32 (exact).
 __device__ inline float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ inline float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Eight bfloat16 values (one 16-byte piece) as IEEE half, each multiplied by
-// 2^-8 first: the power-of-two factor is exact, so every |v| below 2^24 keeps
-// its bfloat16 value up to the half rounding of tiny magnitudes (absolute
-// error below 2^-16); larger magnitudes overflow to infinity.
-__device__ inline u32x4 bf16x8_to_f16x8_scaled(u32x4 w) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t wi = w[i];
-    r[i] = pack_f16x2(bf16_lo(wi) * 0.00390625f, bf16_hi(wi) * 0.00390625f);
-  }
-  return r;
-}
 
 // a.lo*b.lo + a.hi*b.hi + c on two packed bfloat16 pairs (v_dot2_f32_bf16).
 // The pairs arrive as 32-bit words copied into locals: a bit cast applied

@@ -39,6 +39,7 @@ struct Wave {
   uint64_t slot[64];
   uint16_t a[64][8], b[64][8];
   float c[64][4];
+  float c16[64][16];
 };
 
 struct Fiber {
@@ -203,6 +204,37 @@ void mfma_16x16x32_f16(const uint16_t a[8], const uint16_t b[8], const float c[4
     d[i] = (float)(acc + w.c[l][i]);
   }
   arrive(w.bar);
+}
+
+// D = A(32x16) B(16x32) + C with the lane layout of v_mfma_f32_32x32x16_{bf16,f16}
+// (checked on the GPU): lane l holds A[l%32][8(l/32)..+8], B[8(l/32)..+8][l%32],
+// D[8(j/4) + 4(l/32) + j%4][l%32] in its accumulator j.
+static void mfma_32x32x16(const uint16_t a[8], const uint16_t b[8], const float c[16], float d[16], bool half) {
+  Wave& w = my_wave();
+  const int l = tl_lane;
+  std::memcpy(w.a[l], a, 16);
+  std::memcpy(w.b[l], b, 16);
+  std::memcpy(w.c16[l], c, 64);
+  arrive(w.bar);
+  const int n = l % 32;
+  for (int j = 0; j < 16; ++j) {
+    const int m = 8 * (j / 4) + 4 * (l / 32) + j % 4;
+    double acc = 0;
+    for (int k = 0; k < 16; ++k) {
+      const uint16_t ua = w.a[m + 32 * (k / 8)][k % 8], ub = w.b[n + 32 * (k / 8)][k % 8];
+      acc += half ? (double)hf(ua) * hf(ub) : (double)bf(ua) * bf(ub);
+    }
+    d[j] = (float)(acc + w.c16[l][j]);
+  }
+  arrive(w.bar);
+}
+
+void mfma_32x32x16_bf16(const uint16_t a[8], const uint16_t b[8], const float c[16], float d[16]) {
+  mfma_32x32x16(a, b, c, d, false);
+}
+
+void mfma_32x32x16_f16(const uint16_t a[8], const uint16_t b[8], const float c[16], float d[16]) {
+  mfma_32x32x16(a, b, c, d, true);
 }
 
 void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* ctx) {

@@ -47,6 +47,8 @@ uint64_t exchange(uint64_t mine, int src_lane);          // value of src_lane
 uint64_t ballot(bool pred);
 void mfma_16x16x32_bf16(const uint16_t a[8], const uint16_t b[8], const float c[4], float d[4]);
 void mfma_16x16x32_f16(const uint16_t a[8], const uint16_t b[8], const float c[4], float d[4]);
+void mfma_32x32x16_bf16(const uint16_t a[8], const uint16_t b[8], const float c[16], float d[16]);
+void mfma_32x32x16_f16(const uint16_t a[8], const uint16_t b[8], const float c[16], float d[16]);
 void run_grid(dim3 grid, dim3 block, void (*body)(void*), void* ctx);
 
 template <typename T>
@@ -173,6 +175,28 @@ inline F4 emu_mfma_f16(V8 a, V8 b, F4 c, int, int, int) {
 }
 
 #define __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, x, y, z) emu_mfma_f16((a), (b), (c), (x), (y), (z))
+
+template <typename V8, typename F16>
+inline F16 emu_mfma32(V8 a, V8 b, F16 c, bool half) {
+  uint16_t ua[8], ub[8];
+  float fc[16], fd[16];
+  std::memcpy(ua, &a, 16);
+  std::memcpy(ub, &b, 16);
+  for (int i = 0; i < 16; ++i) fc[i] = c[i];
+  if (half) emu::mfma_32x32x16_f16(ua, ub, fc, fd);
+  else emu::mfma_32x32x16_bf16(ua, ub, fc, fd);
+  F16 d;
+  for (int i = 0; i < 16; ++i) d[i] = fd[i];
+  return d;
+}
+#define __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, x, y, z) emu_mfma32((a), (b), (c), false)
+#define __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, x, y, z) emu_mfma32((a), (b), (c), true)
+#define __builtin_amdgcn_fdot2(a, b, c, cl) emu_fdot2((a), (b), (c), (cl))
+// hardware register reads: only XCC_ID (hwreg 20) is used; workgroups go to the eight XCDs in turn
+inline int emu_getreg(int) { return (int)(emu::tl_blockIdx.x % 8); }
+#define __builtin_amdgcn_s_getreg(r) emu_getreg((r))
+#define __builtin_amdgcn_s_setprio(p) ((void)0)
+#define __builtin_amdgcn_sched_barrier(m) ((void)0)
 #define __builtin_amdgcn_readlane(v, l) emu_readlane((v), (l))
 #define __builtin_amdgcn_readfirstlane(v) emu_readfirstlane((v))
 #define __builtin_amdgcn_ballot_w64(p) emu_ballot((p))

@@ -71,12 +71,15 @@ def test_many_sequences(emu):
     check(w, q, kp, vp, out, "2100 sequences")
 
 
-def test_large_value_magnitudes(emu):
-    # values near 2^20: the prefill tile stages them as half x 2^-8, exact below 2^24
+@pytest.mark.parametrize("k", [20, 24, 30])
+def test_large_value_magnitudes(emu, k):
+    # values scaled by 2^k: the prefill tile stages values as half when every staged
+    # magnitude is below 2^16, and recomputes an item in bfloat16 (weights split in a
+    # high and low part) when one is not; every worker must stay within tolerance
     w = W.random_ragged(21, "bf16", 8, 2, 64, [1, 40, 1], [300, 170, 45])
     rng = np.random.default_rng(6)
     kp, vp = empty_pools(rng, "bf16", w.num_blocks, 2, 64)
-    big = raw(layout.to_f64(vp, "bf16").astype(np.float32) * np.float32(2.0 ** 20), "bf16")
+    big = raw(layout.to_f64(vp, "bf16").astype(np.float32) * np.float32(2.0 ** k), "bf16")
     q = raw(rng.standard_normal((w.num_tokens, 8, 64)).astype(np.float32), "bf16")
     out, st = emu.forward(w, q, kp, big)
     assert st == 0
@@ -84,8 +87,24 @@ def test_large_value_magnitudes(emu):
     ref = oattn.paged_attention(q, kp, big, w.block_tables, w.context_lens, w.query_start_loc, w.scale, "bf16")
     got = layout.to_f64(out, "bf16")
     a, r = TOL["bf16"]
-    ratio = (np.abs(got - ref) / 2.0 ** 20 / (a + r * np.abs(ref) / 2.0 ** 20)).max()
-    assert np.isfinite(got).all() and ratio <= 1.0, f"large values: worst err/bound {ratio:.3f}"
+    ratio = (np.abs(got - ref) / 2.0 ** k / (a + r * np.abs(ref) / 2.0 ** k)).max()
+    assert np.isfinite(got).all() and ratio <= 1.0, f"large values 2^{k}: worst err/bound {ratio:.3f}"
+
+
+def test_huge_value_on_a_causally_masked_key(emu):
+    # one key inside a prefill chunk holds values of 2^30: the rows before it must not see
+    # it (no 0 x inf), the rows after it must weigh it exactly
+    for hq, hkv, ql, cl, pos in [(4, 4, [40], [40], 5), (8, 2, [1, 40], [90, 170], 140)]:
+        w = W.random_ragged(24, "bf16", hq, hkv, 64, ql, cl)
+        rng = np.random.default_rng(24)
+        kp, vp = empty_pools(rng, "bf16", w.num_blocks, hkv, 64)
+        s = len(ql) - 1
+        b = int(w.block_tables[s, pos // 16])
+        vp[b, :, :, pos % 16] = raw(np.float32(2.0 ** 30), "bf16")
+        q = raw(rng.standard_normal((w.num_tokens, hq, 64)).astype(np.float32), "bf16")
+        out, st = emu.forward(w, q, kp, vp)
+        assert st == 0
+        check(w, q, kp, vp, out, f"2^30 at key {pos}")
 
 
 def test_float32_head_dim_128_decode_and_prefill(emu):

@@ -283,21 +283,43 @@ def test_scale_sign_and_size(pa, scale):
         run_and_check(pa, w, label=f"scale {scale} Hq={hq} Hkv={hkv} q={ql} L={cl}")
 
 
-def test_large_value_magnitudes(pa):
-    # values near 2^20 in magnitude: the prefill tile stages them as half x 2^-8 (exact below 2^24)
+@pytest.mark.parametrize("k", [20, 24, 30])
+def test_large_value_magnitudes(pa, k):
+    # values scaled by 2^k: the prefill tile stages values as half when every staged
+    # magnitude is below 2^16 and recomputes an item in bfloat16 (weights split in a high
+    # and a low part) when one is not; every worker stays within tolerance, never NaN
     w = W.random_ragged(21, "bf16", 8, 8, 128, [1, 150, 1], [700, 1200, 40])
-    say("[case] large value magnitudes (V x 2^20, K x 4)")
+    say(f"[case] large value magnitudes (V x 2^{k}, K x 4)")
     r = Run(w)
     q, kc, vc, _, _ = W.make_values(w, DEV)
-    vc.mul_(2.0 ** 20)
+    vc.mul_(2.0 ** k)
     kc.mul_(4.0)
     out = r.forward(q, kc, vc)
     r.check_status()
-    rows, ref = oracle_rows(w, q, kc, vc, range(w.num_seqs))
+    rows, ref = oracle_rows_all(w, q, kc, vc)
     got = to_f64(out.index_select(0, torch.from_numpy(rows).to(DEV)))
     assert np.isfinite(got).all()
     # the output scales with the values (an exact power of two): compare at the scale of N(0, 1) values
-    assert_close(got / 2.0 ** 20, ref / 2.0 ** 20, "bf16", "large value magnitudes (/2^20)")
+    assert_close(got / 2.0 ** k, ref / 2.0 ** k, "bf16", f"large value magnitudes (/2^{k})")
+
+
+def test_huge_value_on_a_causally_masked_key(pa):
+    # one key inside a prefill chunk holds values of 2^30: the rows before it must not see it
+    # (no 0 x inf in the P.V of a step), the rows after it weigh it exactly
+    for hq, hkv, ql, cl, pos in [(4, 4, [200], [200], 5), (16, 4, [1, 90], [300, 700], 650)]:
+        w = W.random_ragged(24, "bf16", hq, hkv, 128, ql, cl)
+        say(f"[case] 2^30 on key {pos}: Hq={hq} Hkv={hkv} q={ql} L={cl}")
+        r = Run(w)
+        q, kc, vc, _, _ = W.make_values(w, DEV)
+        s = len(ql) - 1
+        b = int(w.block_tables[s, pos // 16])
+        vc[b, :, :, pos % 16] = 2.0 ** 30
+        out = r.forward(q, kc, vc)
+        r.check_status()
+        rows, ref = oracle_rows_all(w, q, kc, vc)
+        got = to_f64(out.index_select(0, torch.from_numpy(rows).to(DEV)))
+        assert np.isfinite(got).all()
+        assert_close(got, ref, "bf16", f"2^30 at key {pos}")
 
 
 def test_single_key_and_equal_scores(pa):
