@@ -23,7 +23,8 @@ inputs resident in device memory before timing starts:
   write (pa_rope_reshape_and_cache rotates q and the new keys at their
   positions; the forward reads the rotated q).
 * copy / read: calibration lines, not the path — a 4 GiB device copy, and
-  every 4 KiB page of a 4 GiB pool read once in random order (pa_read_pages),
+  every 4 KiB page of a 4 GiB pool read once in random order (the measurement
+  library's pa_probe_read_pages),
   the attainable HBM rates the kernels' fractions are set against.
 
 The roofline object describes the dominant kernel, timed with HIP events
@@ -239,15 +240,44 @@ def copy_calibration(torch, dev, args, nbytes=4 << 30):
                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}), flush=True)
 
 
-def read_calibration(torch, pa, dev, args, nbytes=4 << 30, grid=2048):
-    """4 KiB pages of a 4 GiB pool read in a seeded random order, 16-byte loads, two
-    pages per wavefront in flight: the rate the decode workers' page reads could
-    reach if they did no arithmetic.  By default a step reads every page once;
-    with --read-mib M a step reads the next M MiB of the order (successive steps
-    take disjoint slices, so none finds its pages in the 256 MB Infinity Cache),
-    the rate a pass of that size can reach.  With --read-chunk-pages N the order is
-    a random permutation of runs of N consecutive pages (0: every page in address
-    order), read by neighbouring wavefronts at the same time."""
+class ProbeLib:
+    """ctypes face of libpa_probe.so, the measurement-only page-read probe."""
+
+    def __init__(self):
+        import ctypes
+        path = os.path.join(ROOT, "paged_kv_cache_57_amd", "libpa_probe.so")
+        if not os.path.exists(path):
+            raise SystemExit(f"{path} is not built")
+        self.lib = ctypes.CDLL(path)
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        self.lib.pa_probe_read_pages.restype = i32
+        self.lib.pa_probe_read_pages.argtypes = [vp, i64, vp, i32, vp, i32, i32, i32, vp, vp]
+        self.lib.pa_probe_last_error.restype = ctypes.c_char_p
+
+    def read_pages(self, torch, pool, page_ids, sink, grid, pages_in_flight, mode, status):
+        st = self.lib.pa_probe_read_pages(pool.data_ptr(), pool.numel() * pool.element_size(), page_ids.data_ptr(),
+                                          page_ids.numel(), sink.data_ptr(), grid, pages_in_flight, mode,
+                                          status.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(self.lib.pa_probe_last_error().decode())
+
+
+READ_MODES = {0: "plain", 1: "nontemporal", 2: "into_lds"}
+
+
+def read_calibration(torch, pa, dev, args, nbytes=4 << 30):
+    """4 KiB pages of a 4 GiB pool read in a seeded random order with 16-byte loads,
+    --read-pif pages per wavefront in flight (default 2, the decode workers' depth),
+    --read-mode loads (0 plain, 1 non-temporal, 2 into LDS): the rate the decode
+    workers' page reads could reach if they did no arithmetic.  By default a step
+    reads every page once; with --read-mib M a step reads the next M MiB of the
+    order (successive steps take disjoint slices, so none finds its pages in the
+    256 MB Infinity Cache), the rate a pass of that size can reach.  With
+    --read-chunk-pages N the order is a random permutation of runs of N consecutive
+    pages (0: every page in address order), read by neighbouring wavefronts at the
+    same time.  --read-grid sets the workgroups (0: one wavefront per
+    pages-in-flight run of the slice, at most 2048 workgroups)."""
+    probe = ProbeLib()
     pool = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(7)
     npages = nbytes // 4096
     run = args.read_chunk_pages
@@ -262,30 +292,35 @@ def read_calibration(torch, pa, dev, args, nbytes=4 << 30, grid=2048):
     per = npages if not args.read_mib else min(npages, args.read_mib * 256)
     nslices = npages // per
     slices = [order[i * per:(i + 1) * per] for i in range(nslices)]
-    g = grid if per == npages else min(grid, max(1, (per + 7) // 8))
-    sink = torch.empty(grid * 256, dtype=torch.int32, device=dev)
+    pif, mode = args.read_pif, args.read_mode
+    g = args.read_grid or min(2048, max(1, (per + 4 * pif - 1) // (4 * pif)))
+    sink = torch.empty(g * 256, dtype=torch.int32, device=dev)
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     for i in range(args.warmup):
-        pa.pa_read_pages(pool, slices[i % nslices], sink, g, status)
+        probe.read_pages(torch, pool, slices[i % nslices], sink, g, pif, mode, status)
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
+    times = []
     for i in range(args.steps):
-        pa.pa_read_pages(pool, slices[(args.warmup + i) % nslices], sink, g, status)
-    t1.record()
-    torch.cuda.synchronize()
+        t0.record()
+        probe.read_pages(torch, pool, slices[(args.warmup + i) % nslices], sink, g, pif, mode, status)
+        t1.record()
+        t1.synchronize()
+        times.append(t0.elapsed_time(t1))
     if int(status.item()) != 0:
-        raise RuntimeError(f"pa_read_pages flagged status {int(status.item())}")
-    ms = t0.elapsed_time(t1) / args.steps
+        raise RuntimeError(f"pa_probe_read_pages flagged status {int(status.item())}")
+    ms = float(np.median(times))
     gbps = per * 4096 / (ms * 1e-3) / 1e9
     name = "read_pages_4GiB" if per == npages else f"read_pages_{per * 4096 >> 20}MiB_of_4GiB"
     if run != 1:
         name += "_in_address_order" if run == 0 else f"_runs_of_{run}"
     print(json.dumps({"metric": "random 4 KiB page reads GB/s", "value": round(gbps, 1), "unit": "GB/s",
                       "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+                      "ms_min": round(min(times), 4), "ms_max": round(max(times), 4),
                       "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
-                      "data": "synthetic", "config": {"workload": name, "pages": per, "grid": g},
+                      "data": "synthetic", "config": {"workload": name, "pages": per, "grid": g,
+                                                      "pages_in_flight_per_wave": pif, "loads": READ_MODES[mode]},
                       "frac_of_peak": round(gbps / HBM_PEAK_GBPS, 4)}), flush=True)
 
 
@@ -436,6 +471,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--read-mib", type=int, default=0, help="read workload: MiB per step (0: the whole 4 GiB pool)")
+    ap.add_argument("--read-pif", type=int, default=2, help="read workload: pages per wavefront in flight (1, 2, 4, 8)")
+    ap.add_argument("--read-mode", type=int, default=0, help="read workload: 0 plain, 1 non-temporal, 2 into-LDS loads")
+    ap.add_argument("--read-grid", type=int, default=0, help="read workload: workgroups (0: by the slice size)")
     ap.add_argument("--read-chunk-pages", type=int, default=1,
                     help="read workload: pages per run of consecutive pages in the random order (0: address order)")
     ap.add_argument("--shared-prefix", action="store_true",

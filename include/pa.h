@@ -247,19 +247,6 @@ size_t pa_forward_noalloc_max_workspace_bytes(void);
  * num_events 0 (events may be NULL) turns recording off. */
 pa_status pa_set_stage_events(void* const* events, int32_t num_events);
 
-/* Measurement only (not part of the attention path): reads every byte of the
- * listed 4096-byte pages of `pool` with 16-byte loads, two pages per
- * wavefront at a time, the access pattern of the decode workers without
- * their arithmetic, so that the rate of random page reads on this GPU can be
- * set beside theirs.  Writes one uint32 per thread to sink.
- *   pool        device, pool_bytes bytes (a multiple of 4096)
- *   page_ids    device, int32 [num_pages]; ids outside the pool read page 0
- *               and set PA_DEV_BAD_BLOCK
- *   sink        device, uint32 [grid * 256]
- *   grid        workgroups of 256 threads */
-pa_status pa_read_pages(const void* pool, int64_t pool_bytes, const int32_t* page_ids, int32_t num_pages,
-                        uint32_t* sink, int32_t grid, int32_t* dev_status, void* stream);
-
 /* ------------------------------------------------------------------ copy-on-write
  * pa_copy_blocks — for each pair (src, dst) = block_pairs[2i], block_pairs[2i+1],
  * copy the whole key and value page of block src (all KV heads) onto block dst,

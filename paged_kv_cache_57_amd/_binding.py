@@ -60,7 +60,6 @@ _SIGS = {
     "pa_forward_noalloc_max_workspace_bytes": (_sz, []),
     "pa_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
     "pa_set_stage_events": (_i32, [_vp, _i32]),
-    "pa_read_pages": (_i32, [_vp, _i64, _vp, _i32, _vp, _i32, _vp, _vp]),
     "pa_alloc_create": (_i32, [_i32, _i32, _f64, _vp, ctypes.POINTER(_vp)]),
     "pa_alloc_destroy": (None, [_vp]),
     "pa_alloc_num_free": (_i32, [_vp]),
@@ -274,15 +273,6 @@ def pa_copy_blocks(k_cache, v_cache, block_pairs, dev_status=None, stream=None):
         _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(block_pairs, "block_pairs", torch.int32),
         block_pairs.shape[0], nb, hkv, d, blk, _dtype_code(k_cache),
         _dev(dev_status, "dev_status", torch.int32), _stream(k_cache, stream)))
-
-
-def pa_read_pages(pool, page_ids, sink, grid, dev_status=None, stream=None):
-    """Measurement only: read the listed 4 KiB pages of `pool` (any device tensor)."""
-    import torch
-    _check(_lib.pa_read_pages(_dev(pool, "pool"), pool.numel() * pool.element_size(),
-                              _dev(page_ids, "page_ids", torch.int32), page_ids.numel(),
-                              _dev(sink, "sink", torch.int32), grid, _dev(dev_status, "dev_status", torch.int32),
-                              _stream(pool, stream)))
 
 
 def pa_set_stage_events(events):

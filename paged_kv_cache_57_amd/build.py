@@ -14,6 +14,9 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libpa.so")
+# measurement-only probes (not part of the attention path), a library of their own
+PROBE_LIB = os.path.join(HERE, "libpa_probe.so")
+PROBE_SOURCES = [os.path.join("measure", "pa_probe.hip")]
 SOURCES = ["pa_status.cpp", "pa_alloc.cpp", "pa_splitfuse.cpp", "pa_step.cpp", "pa_cache.hip", "pa_attention.hip"]
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.environ.get("HIPCC", os.path.join(ROCM, "bin", "hipcc"))
@@ -28,7 +31,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function"]
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libpa.so; returns its path. Always rebuilds."""
+    """Compile every source and link libpa.so (and the measurement library libpa_probe.so);
+    returns libpa.so's path. Always rebuilds."""
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     objs = []
@@ -45,6 +49,14 @@ def build(verbose: bool = False) -> str:
     tmp = LIB + ".tmp"
     _run([HIPCC, "-shared", "-fPIC", *DEVICE_FLAGS, *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
+    pobjs = []
+    for src in PROBE_SOURCES:
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        _run([HIPCC, "-x", "hip", *DEVICE_FLAGS, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        pobjs.append(obj)
+    tmp = PROBE_LIB + ".tmp"
+    _run([HIPCC, "-shared", "-fPIC", *DEVICE_FLAGS, *pobjs, "-o", tmp], verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

@@ -31,6 +31,7 @@
 //    rescaling rule above.
 #include <algorithm>
 #include <cmath>
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -133,6 +134,9 @@ struct AttnParams {
   const int32_t* groups;
   int32_t num_groups;
   i32x4* seqx;  // per entry: key offset, shared partitions before the own ones, member flag, table row
+  // One-pass GQA decode: completion counters per (sequence, KV head) and the call's tag.
+  unsigned long long* dec_ctr;
+  uint32_t call_tag;
 };
 
 // Entry flags.  A group entry's rows are its members' single decode rows,
@@ -478,10 +482,10 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
             const T* vp = vc + page;
 #pragma unroll
             for (int k = 0; k < NIK; ++k)
-              kr[j][k] = ld16(kp + ((4 * k + (lane >> 4)) * kBlock + (lane & 15)) * X);
+              kr[j][k] = ld16_stream(kp + ((4 * k + (lane >> 4)) * kBlock + (lane & 15)) * X);
 #pragma unroll
             for (int k = 0; k < NIV; ++k)
-              vr[j][k] = ld16(vp + (RPI * k + lane / LPR) * kBlock + (lane % LPR) * X);
+              vr[j][k] = ld16_stream(vp + (RPI * k + lane / LPR) * kBlock + (lane % LPR) * X);
           } else {
 #pragma unroll
             for (int k = 0; k < NIK; ++k) kr[j][k] = u32x4{0, 0, 0, 0};
@@ -579,8 +583,8 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
 
 // ---------------------------------------------------------------- MFMA worker
 // One wavefront per item: 16 query rows sharing one KV head x one key
-// partition, 64 keys (four pages) per step on v_mfma_f32_16x16x32_bf16; all
-// four key and value pages of a step are requested before it computes.
+// partition, 32 keys (two pages) per step on v_mfma_f32_16x16x32_bf16, the
+// pages of two steps requested before either computes.
 //  Scores, transposed: Sᵀ[key][row] = K · Qᵀ with K as the A operand (lane l:
 //  key l%16 of the page, 8 head dims per lane, straight from the key page)
 //  and Q as the B operand (lane l: row l%16).  The result gives lane l the
@@ -596,20 +600,189 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
 // per weight), masks are applied only on steps that reach past the context
 // or past a row's position, and a row's exponent reference is raised only
 // when its maximum grows by more than kLazyRescale.
+// One MFMA tile: the 16 rows of one KV head held by lanes r = lane % 16 (row r at
+// token t, query head hh, position pos_r; pos_lo is the tile's lowest position)
+// over keys [kv_lo, kv_hi), whose pages the block-table row trow lists.  Leaves
+// each lane its row's exponent reference m_r, its share lsum of the row sum and
+// the unnormalised output columns 16j + 4(lane/16) .. +3 in oacc[j].
+// PIPE: the next step's pages are in flight while a step computes.  That takes
+// twice the registers for pages, so the query operand then lives in qs, a
+// wavefront-private LDS area of D/32 x 64 entries, and is read back each step.
+template <int D, bool PIPE>
+__device__ inline void mfma_tile(const AttnParams& p, int trow, int kvh, int t, int hh, int pos_r, int pos_lo,
+                                 int kv_lo, int kv_hi, float& m_r, float& lsum, f32x4 (&oacc)[D / 16],
+                                 bf16x8* qs = nullptr) {
+  constexpr int KS = D / 32;  // k-steps of the score product
+  constexpr int NJ = D / 16;  // 16-dim column blocks of the output
+  const int lane = threadIdx.x & 63;
+  const int r = lane & 15, g4 = lane >> 4;
+  const bf16_t* __restrict__ kc = (const bf16_t*)p.k_cache;
+  const bf16_t* __restrict__ vc = (const bf16_t*)p.v_cache;
+  const int64_t page_elems = (int64_t)kBlock * D;
+  const float csc = fmaxf(fabsf(p.scale_log2), 1e-30f);  // scale 0 gives equal weights, as it should
+  const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
+  if (kv_lo < kv_hi) {
+    const int nblk = (kv_hi - kv_lo + kBlock - 1) / kBlock;
+    const int bidv = load_block_ids(p, trow, kv_lo / kBlock, nblk, lane);
+
+    bf16x8 qop[KS];
+    {
+      const bf16_t* qrow = (const bf16_t*)p.q + ((int64_t)t * p.Hq + hh) * D;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const u32x4 qw = ld16(qrow + 32 * k + 8 * g4);
+        qop[k] = __builtin_bit_cast(bf16x8, u32x4{qw[0] ^ qflip, qw[1] ^ qflip, qw[2] ^ qflip, qw[3] ^ qflip});
+      }
+      if constexpr (PIPE) {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) qs[64 * k + lane] = qop[k];
+      }
+    }
+
+    // 32 keys (two pages) per step, double-buffered: the next step's pages are
+    // requested before the current step computes, so one step's loads are in
+    // flight while the other's MFMAs run.  A page past the last one (odd page
+    // counts, the partition's tail) reads the last page again: its scores are
+    // masked and its values zeroed, and every address stays inside the pool.
+    struct Step {
+      bf16x8 k0[KS], k1[KS];
+      uint32_t vw[NJ][4];  // value operand words: keys 4*g4 + 0..3 of page 0, then of page 1
+    };
+    auto load = [&](Step& st, int base) {
+      const int jb = (base - kv_lo) / kBlock;
+      const int64_t pg0 = ((int64_t)readlane(bidv, min(jb, nblk - 1)) * p.Hkv + kvh) * page_elems;
+      const int64_t pg1 = ((int64_t)readlane(bidv, min(jb + 1, nblk - 1)) * p.Hkv + kvh) * page_elems;
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const int off = ((4 * k + g4) * kBlock + r) * 8;
+        st.k0[k] = __builtin_bit_cast(bf16x8, ld16_stream(kc + pg0 + off));
+        st.k1[k] = __builtin_bit_cast(bf16x8, ld16_stream(kc + pg1 + off));
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int off = (16 * j + r) * kBlock + 4 * g4;
+        const u32x2 lo = ld8_stream(vc + pg0 + off);
+        const u32x2 hi = ld8_stream(vc + pg1 + off);
+        st.vw[j][0] = lo[0];
+        st.vw[j][1] = lo[1];
+        st.vw[j][2] = hi[0];
+        st.vw[j][3] = hi[1];
+      }
+    };
+    auto compute = [&](Step& st, int base) {
+      // unscaled scores of row r for keys base + 16 (e >> 2) + 4 g4 + (e & 3)
+      f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
+      // (a compiler-only fence: the query operand is read from LDS here, not kept in registers)
+      if constexpr (PIPE) __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+      for (int k = 0; k < KS; ++k) {
+        const bf16x8 qk = PIPE ? qs[64 * k + lane] : qop[k];
+        c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.k0[k], qk, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(st.k1[k], qk, c1, 0, 0, 0);
+      }
+      float sc[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sc[e] = c0[e];
+        sc[4 + e] = c1[e];
+      }
+      if (base + 32 > kv_hi || base + 31 > pos_lo) {  // wave-uniform
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = base + (e >> 2) * kBlock + 4 * g4 + (e & 3);
+          sc[e] = (key < kv_hi && key <= pos_r) ? sc[e] : kNegInf;
+        }
+      }
+      float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      mx = max_over_rows(mx);
+      const float mloc = mx * csc;  // -inf stays -inf (csc > 0)
+      if (__builtin_amdgcn_ballot_w64(mloc > m_r + kLazyRescale)) {
+        const float m_new = fmaxf(m_r, mloc);
+        const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_r - m_new);
+        lsum *= alpha;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) oacc[j] *= alpha;
+        m_r = m_new;
+      }
+      const float nmu = m_r == kNegInf ? 0.f : -m_r;  // a row that sees no key yet has weights 0
+      uint32_t phw[4], plw[4];
+      float psum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = fast_exp2(fmaf(sc[e], csc, nmu));
+        const float p1 = fast_exp2(fmaf(sc[e + 1], csc, nmu));
+        const uint32_t hw = pack_bf16x2(p0, p1);
+        phw[e >> 1] = hw;
+        plw[e >> 1] = pack_bf16x2(p0 - bf16_lo(hw), p1 - bf16_hi(hw));
+        psum += p0 + p1;
+      }
+      const bf16x8 pop_hi = __builtin_bit_cast(bf16x8, u32x4{phw[0], phw[1], phw[2], phw[3]});
+      const bf16x8 pop_lo = __builtin_bit_cast(bf16x8, u32x4{plw[0], plw[1], plw[2], plw[3]});
+      lsum += psum;
+      if (base + 32 > kv_hi) {
+        // keys past kv_hi may hold anything (even NaN): zero them in the value operand
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = base + (e >> 2) * kBlock + 4 * g4 + (e & 3);
+          const uint32_t keep = key < kv_hi ? 0xffffffffu : (e & 1) ? 0x0000ffffu : 0xffff0000u;  // a select
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) st.vw[j][e >> 1] &= keep;
+        }
+      }
+      // the high parts first, then the low parts: no MFMA waits on the one before it
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{st.vw[j][0], st.vw[j][1], st.vw[j][2], st.vw[j][3]});
+        oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_hi, oacc[j], 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{st.vw[j][0], st.vw[j][1], st.vw[j][2], st.vw[j][3]});
+        oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo, oacc[j], 0, 0, 0);
+      }
+    };
+    Step sa, sb;
+    if constexpr (PIPE) {
+      // Two register sets in turn (unrolled by two: no copies between them);
+      // the loop conditions are wave-uniform.  The scheduling barriers keep
+      // the next step's loads ahead of the current step's arithmetic.
+      load(sa, kv_lo);
+      for (int base = kv_lo;; base += 64) {
+        if (base + 32 >= kv_hi) {
+          compute(sa, base);
+          break;
+        }
+        load(sb, base + 32);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sa, base);
+        if (base + 64 >= kv_hi) {
+          compute(sb, base + 32);
+          break;
+        }
+        load(sa, base + 64);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sb, base + 32);
+      }
+    } else {
+      // 64 keys requested, then computed: half the registers of the pipelined loop
+      for (int base = kv_lo; base < kv_hi; base += 64) {
+        load(sa, base);
+        load(sb, base + 32);
+        compute(sa, base);
+        if (base + 32 < kv_hi) compute(sb, base + 32);
+      }
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
-  constexpr int KS = D / 32;  // k-steps of the score product
   constexpr int NJ = D / 16;  // 16-dim column blocks of the output
   const int lane = threadIdx.x & 63;
   const int r = lane & 15, g4 = lane >> 4;
   const int wave_id = wave_uniform((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
   const int nwaves = (int)gridDim.x * 4;
   const int total = wave_uniform(p.ctrl[3]);
-  const bf16_t* __restrict__ kc = (const bf16_t*)p.k_cache;
-  const bf16_t* __restrict__ vc = (const bf16_t*)p.v_cache;
-  const int64_t page_elems = (int64_t)kBlock * D;
-  const float csc = fmaxf(fabsf(p.scale_log2), 1e-30f);  // scale 0 gives equal weights, as it should
-  const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
   __shared__ int skip[kSkip];
   const SkipTable tab = stage_skip(skip, p.pre_m, p.num_ent);
 
@@ -644,139 +817,9 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < NJ; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (kv_lo < kv_hi) {
-      const int nblk = (kv_hi - kv_lo + kBlock - 1) / kBlock;
-      const int bidv = load_block_ids(p, ex.trow, kv_lo / kBlock, nblk, lane);  // a group reads its first member's table
-
-      bf16x8 qop[KS];
-      {
-        const bf16_t* qrow = (const bf16_t*)p.q + ((int64_t)t * p.Hq + hh) * D;
-#pragma unroll
-        for (int k = 0; k < KS; ++k) {
-          const u32x4 qw = ld16(qrow + 32 * k + 8 * g4);
-          qop[k] = __builtin_bit_cast(bf16x8, u32x4{qw[0] ^ qflip, qw[1] ^ qflip, qw[2] ^ qflip, qw[3] ^ qflip});
-        }
-      }
-
-      // Pages past the last one (odd counts, the tail) read the last page
-      // again: their scores are masked and their values zeroed, and every
-      // address stays inside the pool.
-      constexpr int NH = 2;  // 32-key halves per step
-      const int pos_lo = grp ? si.L - 1 : si.L - si.q_len + (tile * kTileRows) / p.G;  // lowest row position
-      for (int base = kv_lo; base < kv_hi; base += 32 * NH) {
-        bf16x8 k0[NH][KS], k1[NH][KS];
-        uint32_t vw[NH][NJ][4];  // value operand words: keys 4*g4 + 0..3 of the half's page 0, then of its page 1
-#pragma unroll
-        for (int hp = 0; hp < NH; ++hp) {
-          const int jb = (base - kv_lo) / kBlock + 2 * hp;
-          const int64_t pg0 = ((int64_t)readlane(bidv, min(jb, nblk - 1)) * p.Hkv + kvh) * page_elems;
-          const int64_t pg1 = ((int64_t)readlane(bidv, min(jb + 1, nblk - 1)) * p.Hkv + kvh) * page_elems;
-#pragma unroll
-          for (int k = 0; k < KS; ++k) {
-            const int off = ((4 * k + g4) * kBlock + r) * 8;
-            k0[hp][k] = __builtin_bit_cast(bf16x8, ld16(kc + pg0 + off));
-            k1[hp][k] = __builtin_bit_cast(bf16x8, ld16(kc + pg1 + off));
-          }
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            const int off = (16 * j + r) * kBlock + 4 * g4;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vc + pg0 + off);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vc + pg1 + off);
-            vw[hp][j][0] = lo[0];
-            vw[hp][j][1] = lo[1];
-            vw[hp][j][2] = hi[0];
-            vw[hp][j][3] = hi[1];
-          }
-        }
-        // unscaled scores of row r for keys base + 32 hp + 16 (e >> 2) + 4 g4 + (e & 3)
-        float sc[NH][8];
-#pragma unroll
-        for (int hp = 0; hp < NH; ++hp) {
-          f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int k = 0; k < KS; ++k) {
-            c0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k0[hp][k], qop[k], c0, 0, 0, 0);
-            c1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k1[hp][k], qop[k], c1, 0, 0, 0);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sc[hp][e] = c0[e];
-            sc[hp][4 + e] = c1[e];
-          }
-        }
-        const bool edge = base + 32 * NH > kv_hi || base + 32 * NH - 1 > pos_lo;  // wave-uniform
-        if (edge) {
-#pragma unroll
-          for (int hp = 0; hp < NH; ++hp)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int key = base + 32 * hp + (e >> 2) * kBlock + 4 * g4 + (e & 3);
-              sc[hp][e] = (key < kv_hi && key <= pos_r) ? sc[hp][e] : kNegInf;
-            }
-        }
-        float mx = kNegInf;
-#pragma unroll
-        for (int hp = 0; hp < NH; ++hp)
-          mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sc[hp][0], sc[hp][1]), fmaxf(sc[hp][2], sc[hp][3])),
-                               fmaxf(fmaxf(sc[hp][4], sc[hp][5]), fmaxf(sc[hp][6], sc[hp][7]))));
-        mx = max_over_rows(mx);
-        const float mloc = mx * csc;  // -inf stays -inf (csc > 0)
-        if (__builtin_amdgcn_ballot_w64(mloc > m_r + kLazyRescale)) {
-          const float m_new = fmaxf(m_r, mloc);
-          const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_r - m_new);
-          lsum *= alpha;
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) oacc[j] *= alpha;
-          m_r = m_new;
-        }
-        const float nmu = m_r == kNegInf ? 0.f : -m_r;  // a row that sees no key yet has weights 0
-        bf16x8 pop_hi[NH], pop_lo[NH];
-        float psum = 0.f;
-#pragma unroll
-        for (int hp = 0; hp < NH; ++hp) {
-          uint32_t phw[4], plw[4];
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const float p0 = fast_exp2(fmaf(sc[hp][e], csc, nmu));
-            const float p1 = fast_exp2(fmaf(sc[hp][e + 1], csc, nmu));
-            const uint32_t hw = pack_bf16x2(p0, p1);
-            phw[e >> 1] = hw;
-            plw[e >> 1] = pack_bf16x2(p0 - bf16_lo(hw), p1 - bf16_hi(hw));
-            psum += p0 + p1;
-          }
-          pop_hi[hp] = __builtin_bit_cast(bf16x8, u32x4{phw[0], phw[1], phw[2], phw[3]});
-          pop_lo[hp] = __builtin_bit_cast(bf16x8, u32x4{plw[0], plw[1], plw[2], plw[3]});
-        }
-        lsum += psum;
-        if (base + 32 * NH > kv_hi) {
-          // keys past kv_hi may hold anything (even NaN): zero them in the value operand
-#pragma unroll
-          for (int hp = 0; hp < NH; ++hp)
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const int key = base + 32 * hp + (e >> 2) * kBlock + 4 * g4 + (e & 3);
-                if (key >= kv_hi) vw[hp][j][e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-              }
-        }
-        // the high parts first, then the low parts: no MFMA waits on the one before it
-#pragma unroll
-        for (int hp = 0; hp < NH; ++hp)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{vw[hp][j][0], vw[hp][j][1], vw[hp][j][2], vw[hp][j][3]});
-            oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_hi[hp], oacc[j], 0, 0, 0);
-          }
-#pragma unroll
-        for (int hp = 0; hp < NH; ++hp)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) {
-            const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{vw[hp][j][0], vw[hp][j][1], vw[hp][j][2], vw[hp][j][3]});
-            oacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pop_lo[hp], oacc[j], 0, 0, 0);
-          }
-      }
-    }
+    const int pos_lo = grp ? si.L - 1 : si.L - si.q_len + (tile * kTileRows) / p.G;  // lowest row position
+    // a group reads its first member's table
+    mfma_tile<D, false>(p, ex.trow, kvh, t, hh, pos_r, pos_lo, kv_lo, kv_hi, m_r, lsum, oacc);
     const float l = sum_over_rows(lsum);
     if (!grp && ex.nps == 0 && w.nparts == 1) {
       bf16_t* orow = (bf16_t*)p.out + ((int64_t)t * p.Hq + hh) * D;
@@ -793,6 +836,193 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
       slot[D + 1] = l;
     }
   }
+}
+
+// ---------------------------------------------------------------- one-pass GQA decode
+// Batches whose every row is a single-position decode, with 2..16 query heads
+// per KV head (the MFMA worker's GQA rows), skip the planner and the merge
+// kernel.  One workgroup of kDecWaves wavefronts takes a chunk of
+// kDecWaves x kDecPart keys of one (sequence, KV head): wavefront w
+// computes partition w of the chunk as an MFMA tile (rows = the G query heads),
+// and the chunk's partial states are merged through LDS ("第 15 章" §15.1
+// rescaling applied to finished states).  A context of one chunk writes its
+// output directly.  A longer context writes one state per chunk; the
+// workgroup that completes the last chunk of its (sequence, KV head) merges
+// them.  It knows it is last from a completion counter in the workspace: a
+// 64-bit word whose high half holds a tag of the call and whose low half
+// counts the chunks done; a word whose tag is not this call's counts as zero,
+// and the merging workgroup leaves (tag, 0) behind, so neither an
+// uninitialised workspace nor a replay of a captured call with the same tag
+// sees stale counts.  Items come from the host-known bounds only (no sequence
+// is read by the host): workgroup (s, kvh, chunk) exits at once when the
+// chunk lies past the sequence's context.
+constexpr int kDecWaves = 8;
+// Keys per wavefront: one fixed length, so a sequence's partitions (and its
+// result) never depend on the rest of the batch.  256 keys keep each
+// wavefront streaming long enough to amortise its start (sequence record,
+// block table, query rows) and its share of the chunk merge.
+constexpr int kDecPart = kPartMfmaDecode;
+__host__ __device__ constexpr int dec_chunks(int L) { return (L + kDecWaves * kDecPart - 1) / (kDecWaves * kDecPart); }
+
+__device__ inline uint32_t dec_tagged_count(unsigned long long* ctr, uint32_t tag) {
+  // one thread: counts this chunk; returns the number of chunks done including it
+  unsigned long long old = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (;;) {
+    if ((uint32_t)(old >> 32) == tag) return (uint32_t)atomicAdd(ctr, 1ull) + 1u;
+    const unsigned long long want = ((unsigned long long)tag << 32) | 1ull;
+    const unsigned long long got = atomicCAS(ctr, old, want);
+    if (got == old) return 1u;
+    old = got;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kDecWaves, 1) void gqa_decode_kernel(AttnParams p) {
+  constexpr int NJ = D / 16;
+  constexpr int SF = slot_floats(D);
+  // one state per wavefront and row: O[D], m, l
+  __shared__ float st_lds[kDecWaves][kTileRows][D + 2];
+  __shared__ bf16x8 q_lds[kDecWaves][D / 32 * 64];  // each wavefront's query operand
+  __shared__ int flag;
+  const int lane = threadIdx.x & 63;
+  const int wv = wave_uniform((int)(threadIdx.x >> 6));
+  const int r = lane & 15, g4 = lane >> 4;
+  const int nchunk_bound = max(1, dec_chunks(p.max_ctx));  // dec_chunks grows with L
+  const int item = (int)blockIdx.x;
+  const int chunk = item % nchunk_bound;
+  const int s = item / nchunk_bound / p.Hkv;
+  const int kvh = item / nchunk_bound % p.Hkv;
+  if (item == 0 && threadIdx.x == 0 && (p.qsl[0] != 0 || p.qsl[p.num_seqs] != p.T))
+    flag_status(p.dev_status, PA_DEV_BAD_LENGTH);
+  SeqInfo si = read_seq(p, s);
+  si.a = wave_uniform(si.a);
+  si.q_len = wave_uniform(si.q_len);
+  si.L = wave_uniform(si.L);
+  const bool ok = wave_uniform((int)si.ok) != 0;
+  if (!ok) {
+    if (chunk == 0 && kvh == 0 && threadIdx.x == 0) flag_status(p.dev_status, PA_DEV_BAD_LENGTH);
+    return;
+  }
+  const int part = kDecPart;
+  const int nchunks = dec_chunks(si.L);
+  if (si.q_len == 0 || chunk >= nchunks) return;  // workgroup-uniform
+  const int t = si.a;
+  const int G = p.G;
+  const int R = min(r, G - 1);  // rows past the last query head repeat it
+  const int hh = kvh * G + R;
+  const int pos = si.L - 1;
+  const int kv_lo = (chunk * kDecWaves + wv) * part;
+  const int kv_hi = min(kv_lo + part, si.L);
+
+  float m_r = kNegInf, lsum = 0.f;
+  f32x4 oacc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (kv_lo < kv_hi)  // wave-uniform
+    mfma_tile<D, true>(p, s, kvh, t, hh, pos, pos, kv_lo, kv_hi, m_r, lsum, oacc, q_lds[wv]);
+  const float l = sum_over_rows(lsum);
+  // every lane of a row stores the same m and l; each lane its own columns
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st_lds[wv][r][16 * j + 4 * g4 + e] = oacc[j][e];
+  st_lds[wv][r][D] = m_r;
+  st_lds[wv][r][D + 1] = l;
+  __syncthreads();
+
+  // merge the chunk's partitions: wavefront w takes rows w, w + kDecWaves, ...; lane c has
+  // columns 2c, 2c + 1 (D = 128) or column c (D = 64)
+  constexpr int CPL = D / 64;  // columns per lane
+  const bool single = nchunks == 1;
+  for (int row = wv; row < G; row += kDecWaves) {
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) M = fmaxf(M, st_lds[w][row][D]);
+    float lt = 0.f, o[CPL] = {};
+#pragma unroll
+    for (int w = 0; w < kDecWaves; ++w) {
+      const float mw = st_lds[w][row][D];
+      const float wt = fast_exp2(mw == kNegInf ? kNegInf : mw - M);  // an empty partition weighs 0
+      lt = fmaf(st_lds[w][row][D + 1], wt, lt);
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) o[c] = fmaf(st_lds[w][row][CPL * lane + c], wt, o[c]);
+    }
+    const int hrow = kvh * G + row;
+    if (single) {
+      bf16_t* orow = (bf16_t*)p.out + ((int64_t)t * p.Hq + hrow) * D;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) orow[CPL * lane + c] = Elem<bf16_t>::from_f32(o[c] / lt);
+    } else {
+      // read back within this dispatch, possibly on another XCD: agent-scope stores
+      float* slot = p.partials + (((int64_t)t * p.Hq + hrow) * p.maxparts + chunk) * SF;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) st_agent(slot + CPL * lane + c, o[c]);
+      if (lane == 0) {
+        st_agent(slot + D, M);
+        st_agent(slot + D + 1, lt);
+      }
+    }
+  }
+  if (single) return;
+
+  // the workgroup that completes the last chunk merges the chunk states
+  wait_stores();  // this workgroup's chunk states are visible before it is counted
+  __syncthreads();
+  unsigned long long* ctr = p.dec_ctr + (int64_t)s * p.Hkv + kvh;
+  if (threadIdx.x == 0) flag = (int)dec_tagged_count(ctr, p.call_tag);
+  __syncthreads();
+  if (wave_uniform(flag) != nchunks) return;
+  // Reached only after every chunk was counted, and each workgroup counted its chunk once
+  // its agent-scope stores were acknowledged: agent-scope loads see them all.
+  // One row per wavefront at a time, 32 chunks per round (an online-softmax merge across
+  // rounds): lane c%32 loads chunk c's m and l, half-wavefront h loads the outputs of
+  // chunks h, h + 2, ..., lane l%32 holding columns l%32 + 32q (q < D/32).  Every load of
+  // a round is issued before any is used, so a round costs one memory round trip.
+  constexpr int CPH = D / 32;  // columns per lane
+  constexpr int RC = 32;       // chunks per round
+  const int half = lane >> 5, cl = lane & 31;
+  for (int row = wv; row < G; row += kDecWaves) {
+    const int hrow = kvh * G + row;
+    const float* base = p.partials + ((int64_t)t * p.Hq + hrow) * p.maxparts * SF;
+    float M = kNegInf, lt = 0.f, o[CPH] = {};
+    for (int c0 = 0; c0 < nchunks; c0 += RC) {
+      const int n = min(RC, nchunks - c0);
+      const float* sm = base + (int64_t)(c0 + min(cl, n - 1)) * SF + D;
+      const float mraw = ld_agent(sm), lc = ld_agent(sm + 1);
+      float v[RC / 2][CPH];
+#pragma unroll
+      for (int i = 0; i < RC / 2; ++i) {
+        const float* sk = base + (int64_t)(c0 + min(half + 2 * i, n - 1)) * SF + cl;
+#pragma unroll
+        for (int q = 0; q < CPH; ++q) v[i][q] = ld_agent(sk + 32 * q);
+      }
+      const float mc = cl < n ? mraw : kNegInf;
+      const float Mn = fmaxf(M, wave_max(mc));
+      const float keep = M == kNegInf ? 0.f : fast_exp2(M - Mn);  // rescales the earlier rounds
+      const float wc = mc == kNegInf ? 0.f : fast_exp2(mc - Mn);   // a state with no finite score weighs 0
+      lt = fmaf(lt, keep, half == 0 ? lc * wc : 0.f);
+#pragma unroll
+      for (int q = 0; q < CPH; ++q) o[q] *= keep;
+#pragma unroll
+      for (int i = 0; i < RC / 2; ++i) {
+        const float wk = __shfl(wc, half + 2 * i, kWave);  // 0 for chunks past n
+#pragma unroll
+        for (int q = 0; q < CPH; ++q) o[q] = fmaf(v[i][q], wk, o[q]);
+      }
+      M = Mn;
+    }
+    lt = wave_sum(lt);
+#pragma unroll
+    for (int q = 0; q < CPH; ++q) o[q] += __shfl_xor(o[q], 32, kWave);
+    if (half == 0) {
+      bf16_t* orow = (bf16_t*)p.out + ((int64_t)t * p.Hq + hrow) * D + cl;
+#pragma unroll
+      for (int q = 0; q < CPH; ++q) orow[32 * q] = Elem<bf16_t>::from_f32(o[q] / lt);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0)  // the next call with this tag starts at zero
+    __hip_atomic_store(ctr, (unsigned long long)p.call_tag << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- TILE worker
@@ -855,9 +1085,6 @@ struct TileShape {
 // (for example multiply the output by a rescale factor of 1), which costs more
 // than the branch.  An empty volatile asm cannot be executed speculatively.
 __device__ inline void keep_branch() { asm volatile(""); }
-
-// In-step key of accumulator j of a score MFMA for lane half h.
-__device__ inline int tile_key(int j, int h) { return 16 * (j >> 3) + 8 * h + (j & 7); }
 
 constexpr int kHwRegXccId = (3 << 11) | 20;  // s_getreg operand: HW_REG_XCC_ID, bits 3:0
 
@@ -1272,7 +1499,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
 
 // ---------------------------------------------------------------- host side
 struct WsLayout {
-  size_t ctrl, pre_v, pre_m, pre_t, pre_g, seqinfo, seqx, partials, total;
+  size_t ctrl, pre_v, pre_m, pre_t, pre_g, seqinfo, seqx, partials, dec_ctr, total;
   int maxparts;
 };
 
@@ -1296,7 +1523,8 @@ WsLayout ws_layout(int S, int NG, int T, int Hq, int Hkv, int D, int max_ctx, bo
   l.seqx = l.seqinfo + align256((size_t)E * 16);
   l.partials = l.seqx + (NG > 0 ? align256((size_t)E * 16) : 0);
   const size_t part_bytes = l.maxparts > 1 ? (size_t)T * Hq * l.maxparts * slot_floats(D) * 4 : 0;
-  l.total = l.partials + align256(part_bytes);
+  l.dec_ctr = l.partials + align256(part_bytes);
+  l.total = l.dec_ctr + align256((size_t)S * Hkv * 8);
   return l;
 }
 
@@ -1308,6 +1536,24 @@ inline void mark(int stage, int edge, hipStream_t stream) {
   const int k = 2 * stage + edge;
   if (g_stage_events && k < g_num_stage_events && g_stage_events[k])
     (void)hipEventRecord((hipEvent_t)g_stage_events[k], stream);
+}
+
+// Tag of each pa_forward call (the one-pass decode's completion counters).
+std::atomic<uint32_t> g_call_tag{1};
+
+template <int D>
+void launch_gqa_decode(const AttnParams& p, int grid, hipStream_t stream) {
+  mark(0, 0, stream);
+  mark(0, 1, stream);
+  mark(1, 0, stream);
+  mark(1, 1, stream);
+  mark(2, 0, stream);
+  hipLaunchKernelGGL((gqa_decode_kernel<D>), dim3(grid), dim3(64 * kDecWaves), 0, stream, p);
+  mark(2, 1, stream);
+  mark(3, 0, stream);
+  mark(3, 1, stream);
+  mark(4, 0, stream);
+  mark(4, 1, stream);
 }
 
 template <typename T, int D>
@@ -1450,6 +1696,22 @@ pa_status forward_impl(const char* fn, void* out, const void* q, const void* k_c
   p.groups = groups;
   p.num_groups = num_groups;
   p.seqx = num_groups > 0 ? (i32x4*)(ws + wl.seqx) : nullptr;
+  p.dec_ctr = (unsigned long long*)(ws + wl.dec_ctr);
+  p.call_tag = g_call_tag.fetch_add(1, std::memory_order_relaxed);
+  hipStream_t s = (hipStream_t)stream;
+
+  // Single-position GQA decode batches run in one dispatch (no planner, no merge kernel).
+  if (!is_f32 && num_groups == 0 && max_q_len == 1 && p.G >= 2 && p.G <= kTileRows) {
+    const int64_t chunks = std::max(1, dec_chunks(max_context_len));
+    const int64_t grid = (int64_t)num_seqs * num_kv_heads * chunks;
+    if (grid > INT32_MAX) return fail(PA_ERR_INVALID, "%s: batch too large", fn);
+    (void)hipGetLastError();
+    if (head_dim == 64) launch_gqa_decode<64>(p, (int)grid, s);
+    else launch_gqa_decode<128>(p, (int)grid, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+    return ok();
+  }
 
   // Which worker classes can receive items (decided from host-known bounds only).
   const bool may_valu = is_f32 || p.G == 1;
@@ -1463,7 +1725,6 @@ pa_status forward_impl(const char* fn, void* out, const void* q, const void* k_c
   const int grid_m = (int)std::min<int64_t>(kMaxWorkerGroups, (bound_m + 3) / 4);
   const int grid_t = (int)std::min<int64_t>(kMaxTileGroups, bound_t);
 
-  hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
   if (is_f32) {
     if (head_dim == 64) launch_attention<float, 64>(p, may_valu, false, false, grid_v, grid_m, grid_t, s);

@@ -157,36 +157,6 @@ void launch_reshape(const void* key, const void* value, void* k_cache, void* v_c
                      (const T*)key, (const T*)value, (T*)k_cache, (T*)v_cache, slots, nb, hkv, st);
 }
 
-// Measurement kernel (not part of the path): every wavefront reads two
-// 4-KiB pages per iteration with 16-byte loads, in the order of a page list,
-// and XORs them into one word per thread so nothing is optimised away: thread
-// (w, l) of wavefront w gets the XOR of 16-byte piece l, l+64, l+128, l+192 of
-// its pages 2w, 2w+1, 2w+2W, ... (W wavefronts).  Page ids outside the pool
-// read page 0 and are flagged.
-__global__ __launch_bounds__(256) void read_pages_kernel(const u32x4* __restrict__ pool, int64_t pool_pages,
-                                                         const int32_t* __restrict__ page_ids, int32_t n,
-                                                         uint32_t* __restrict__ sink, int32_t* dev_status) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
-  const int nwaves = (int)gridDim.x * 4;
-  u32x4 acc = {0, 0, 0, 0};
-  for (int p0 = 2 * wave; p0 < n; p0 += 2 * nwaves) {
-    u32x4 v[2][4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t id = page_ids[min(p0 + j, n - 1)];
-      const bool bad = id < 0 || id >= pool_pages;
-      if (__builtin_amdgcn_ballot_w64(bad)) flag_status(dev_status, PA_DEV_BAD_BLOCK);
-      const int64_t page = bad ? 0 : id;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) v[j][k] = pool[page * 256 + k * 64 + lane];
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) acc ^= v[0][k] ^ (p0 + 1 < n ? v[1][k] : u32x4{0, 0, 0, 0});
-  }
-  sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
-}
-
 }  // namespace
 }  // namespace pa
 
@@ -229,24 +199,6 @@ extern "C" pa_status pa_rope_reshape_and_cache(void* q_out, const void* q, const
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
-
-extern "C" pa_status pa_read_pages(const void* pool, int64_t pool_bytes, const int32_t* page_ids,
-                                   int32_t num_pages, uint32_t* sink, int32_t grid, int32_t* dev_status,
-                                   void* stream) {
-  const char* fn = "pa_read_pages";
-  if (num_pages < 0 || grid <= 0 || pool_bytes < 4096 || pool_bytes % 4096)
-    return fail(PA_ERR_INVALID, "%s: bad sizes (num_pages %d, grid %d, pool_bytes %lld)", fn, num_pages, grid,
-                (long long)pool_bytes);
-  if (num_pages == 0) return ok();
-  if (!pool || !page_ids || !sink) return fail(PA_ERR_INVALID, "%s: NULL device pointer", fn);
-  (void)hipGetLastError();
-  hipLaunchKernelGGL(read_pages_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, (const u32x4*)pool,
-                     pool_bytes / 4096, page_ids, num_pages, sink, dev_status);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
-  return ok();
-}
-
 
 extern "C" pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache,
                                           void* v_cache, const int64_t* slot_mapping,

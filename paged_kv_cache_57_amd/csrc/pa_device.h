@@ -76,11 +76,45 @@ __device__ inline float dot2_bf16(uint32_t a, uint32_t b, float c) {
 
 __device__ inline u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
+// 16 / 8 bytes loaded with the non-temporal hint: for data read once per pass
+// (a decode row's key and value pages), which streams through the caches
+// without displacing what is reused; random 4 KiB page reads reach a higher
+// HBM rate this way on gfx950.
+__device__ inline u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ inline u32x2 ld8_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+
 __device__ inline void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-template <typename T>
-__device__ inline T readlane(T v, int lane) {
-  return __builtin_amdgcn_readlane(v, lane);
+// One word stored / loaded coherently for the whole GPU (relaxed, agent scope): the
+// instruction itself carries the scope bit, so values handed between workgroups of one
+// dispatch that run on different XCDs (each with its own L2) need no fence that writes
+// back or invalidates a whole L2.  Ordering is the caller's: see wait_stores.
+__device__ inline void st_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline float ld_agent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until every store this wavefront has issued is acknowledged (s_waitcnt with all
+// counts zero): an agent-scope store is then visible to the whole GPU.  The signal fences
+// keep the compiler from moving memory accesses across the wait.
+__device__ inline void wait_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Lane `lane`'s value of v (lane wave-uniform).  The builtin works on 32-bit
+// integers, so a float travels as its bit pattern (a plain call would convert
+// the value to an integer and back).
+__device__ inline int readlane(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ inline float readlane(float v, int lane) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), lane));
 }
 
 __device__ inline float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, kWave); }

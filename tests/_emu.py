@@ -33,12 +33,13 @@ def build(force=False):
         if all(os.path.getmtime(f) < t for f in srcs + emu + hdrs):
             return EXE
     os.makedirs(os.path.dirname(EXE), exist_ok=True)
+    tmp = f"{EXE}.{os.getpid()}.tmp"
     cmd = [CLANG, "-std=c++20", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            "-I", os.path.join(ROOT, "tests", "emu"), "-I", os.path.join(ROOT, "include"),
            "-x", "c++", *[os.path.join(CSRC, s) for s in SOURCES_HIP], "-x", "none",
-           os.path.join(CSRC, "pa_status.cpp"), emu[0], emu[1], "-lpthread", "-o", EXE + ".tmp"]
+           os.path.join(CSRC, "pa_status.cpp"), emu[0], emu[1], "-lpthread", "-o", tmp]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
-    os.replace(EXE + ".tmp", EXE)
+    os.replace(tmp, EXE)  # atomic: concurrent test workers each build their own file
     return EXE
 
 
@@ -120,15 +121,6 @@ def rope_reshape_and_cache(dtype, q, key, val, kp, vp, slots, positions, cos, si
     k = np.frombuffer(raw[q.nbytes:q.nbytes + kp.nbytes], kp.dtype).reshape(kp.shape)
     v = np.frombuffer(raw[q.nbytes + kp.nbytes:], vp.dtype).reshape(vp.shape)
     return qo, k, v, st
-
-
-def read_pages(words, ids, grid):
-    """Emulated pa_read_pages over int32 `words` (a whole number of 4 KiB pages)."""
-    words = np.ascontiguousarray(words, np.int32)
-    ids = np.ascontiguousarray(ids, np.int32)
-    hdr = np.array([words.size // 1024, ids.size, grid], np.int32)
-    raw, st = _run("read", [hdr, words, ids], grid * 256 * 4)
-    return np.frombuffer(raw, np.uint32).copy(), st
 
 
 def forward_sparse(w, q, pages_k, pages_v, used):

@@ -195,18 +195,6 @@ int main(int argc, char** argv) {
     wr(vc, pool);
     std::free(q); std::free(key); std::free(val); std::free(kc); std::free(vc); std::free(slots);
     std::free(pos); std::free(cs); std::free(sn);
-  } else if (!std::strcmp(argv[1], "read")) {
-    const int npool = rd_i32(), n = rd_i32(), grid = rd_i32();
-    void* pool = rd_buf((size_t)npool * 4096);
-    auto* ids = (int32_t*)rd_buf((size_t)n * 4);
-    auto* sink = (uint32_t*)std::calloc((size_t)grid * 256, 4);
-    pa_status st = pa_read_pages(pool, (int64_t)npool * 4096, ids, n, sink, grid, &status, nullptr);
-    if (st != PA_OK) {
-      std::fprintf(stderr, "pa_read_pages: %d %s\n", st, pa_last_error());
-      return 3;
-    }
-    wr(sink, (size_t)grid * 256 * 4);
-    std::free(pool); std::free(ids); std::free(sink);
   } else {
     return 2;
   }

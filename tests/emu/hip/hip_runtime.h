@@ -106,6 +106,13 @@ inline T __shfl_xor(T v, int mask, int width = 64) {
   return emu::from_bits<T>(emu::exchange(emu::to_bits(v), emu::tl_lane ^ mask));
 }
 
+// Value of lane (src mod width) of the caller's width-lane segment.
+template <typename T>
+inline T __shfl(T v, int src, int width = 64) {
+  const int lane = (emu::tl_lane & ~(width - 1)) | (src & (width - 1));
+  return emu::from_bits<T>(emu::exchange(emu::to_bits(v), lane));
+}
+
 template <typename T>
 inline T __shfl_up(T v, unsigned delta, int width = 64) {
   (void)width;
@@ -114,16 +121,23 @@ inline T __shfl_up(T v, unsigned delta, int width = 64) {
 }
 
 inline int atomicAdd(int* p, int v) { return __atomic_fetch_add(p, v, __ATOMIC_SEQ_CST); }
+inline unsigned long long atomicAdd(unsigned long long* p, unsigned long long v) {
+  return __atomic_fetch_add(p, v, __ATOMIC_SEQ_CST);
+}
+inline unsigned long long atomicCAS(unsigned long long* p, unsigned long long cmp, unsigned long long val) {
+  __atomic_compare_exchange_n(p, &cmp, val, false, __ATOMIC_SEQ_CST, __ATOMIC_SEQ_CST);
+  return cmp;  // the old value (cmp is overwritten with it on failure)
+}
+inline void __threadfence() { __atomic_thread_fence(__ATOMIC_SEQ_CST); }
 inline int atomicOr(int* p, int v) { return __atomic_fetch_or(p, v, __ATOMIC_SEQ_CST); }
 
-template <typename T>
-inline T emu_readlane(T v, int lane) {
-  return emu::from_bits<T>(emu::exchange(emu::to_bits(v), lane));
+// The device builtins take and return a 32-bit int: any other argument type is
+// converted to int on the way in, as on the device (a float is truncated, not
+// reinterpreted), so a kernel that passes a float sees the same result here.
+inline int emu_readlane(int v, int lane) {
+  return emu::from_bits<int>(emu::exchange(emu::to_bits(v), lane));
 }
-template <typename T>
-inline T emu_readfirstlane(T v) {
-  return emu_readlane(v, 0);
-}
+inline int emu_readfirstlane(int v) { return emu_readlane(v, 0); }
 inline uint64_t emu_ballot(bool p) { return emu::ballot(p); }
 
 // v_permlane16_swap / v_permlane32_swap with old = a, src = b: returns
@@ -197,6 +211,8 @@ inline int emu_getreg(int) { return (int)(emu::tl_blockIdx.x % 8); }
 #define __builtin_amdgcn_s_getreg(r) emu_getreg((r))
 #define __builtin_amdgcn_s_setprio(p) ((void)0)
 #define __builtin_amdgcn_sched_barrier(m) ((void)0)
+#define __HIP_MEMORY_SCOPE_AGENT 3  // the host compiler knows __hip_atomic_load/store, not the macro
+#define __builtin_amdgcn_s_waitcnt(x) ((void)(x))
 #define __builtin_amdgcn_readlane(v, l) emu_readlane((v), (l))
 #define __builtin_amdgcn_readfirstlane(v) emu_readfirstlane((v))
 #define __builtin_amdgcn_ballot_w64(p) emu_ballot((p))

@@ -14,8 +14,7 @@ from oracle import attention as oattn
 from oracle import cache_ops, layout
 from tests import _emu
 from tests._pools import empty_pools, raw
-from tests.test_gpu_parity import (RAGGED, REJECTED, SHARED_CASES, many_sequences_batch, read_probe_case,
-                                   shared_prefix_batch)
+from tests.test_gpu_parity import RAGGED, REJECTED, SHARED_CASES, many_sequences_batch, shared_prefix_batch
 
 pytestmark = pytest.mark.skipif(not _emu.available(), reason="needs the ROCm clang++ for the host build")
 TOL = {"bf16": (2e-3, 1e-2), "f32": (1e-5, 1e-5)}
@@ -89,6 +88,19 @@ def test_large_value_magnitudes(emu, k):
     a, r = TOL["bf16"]
     ratio = (np.abs(got - ref) / 2.0 ** k / (a + r * np.abs(ref) / 2.0 ** k)).max()
     assert np.isfinite(got).all() and ratio <= 1.0, f"large values 2^{k}: worst err/bound {ratio:.3f}"
+
+
+def test_one_pass_gqa_decode_chunks(emu):
+    # decode-only GQA batches run in one dispatch: contexts of one chunk (2048 keys), of two
+    # 2048-key chunks (3000 keys) and of nine 1024-key chunks (9000 keys, 128-key partitions),
+    # merged by the workgroup that completes the last chunk; a sequence with no query row
+    w = W.random_ragged(25, "bf16", 16, 2, 64, [1, 1, 0, 1, 1], [9000, 3000, 40, 17, 2048])
+    rng = np.random.default_rng(25)
+    kp, vp = empty_pools(rng, "bf16", w.num_blocks, 2, 64)
+    q = raw(rng.standard_normal((w.num_tokens, 16, 64)).astype(np.float32), "bf16")
+    out, st = emu.forward(w, q, kp, vp)
+    assert st == 0
+    check(w, q, kp, vp, out, "one-pass GQA decode")
 
 
 def test_huge_value_on_a_causally_masked_key(emu):
@@ -192,13 +204,6 @@ def test_parallel_sampling_workflow_emulated(emu):
                                     heads=2, head_dim=64)
     worst, copies = run_workflow(EmuBackend(pa, spec), spec, checkpoints={0, 1, 7, 19}, say=lambda *_: None)
     assert worst <= 1.0 and copies > 0
-
-
-def test_read_pages_probe_emulated(emu):
-    words, ids, grid, want = read_probe_case()
-    got, st = emu.read_pages(words, ids, grid)
-    assert st == 1  # PA_DEV_BAD_BLOCK for the id outside the pool
-    assert np.array_equal(got, want)
 
 
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 64), ("f32", 128)])

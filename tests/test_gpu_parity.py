@@ -383,6 +383,66 @@ def test_batch_invariance(pa):
         assert torch.equal(one.view(torch.int16), full[s:s + 1].view(torch.int16)), s
 
 
+def test_batch_invariance_gqa_decode(pa):
+    # decode-only GQA batches take the one-pass kernel: a sequence's output is bit-identical
+    # alone and inside a bigger batch (partition lengths follow the sequence's own length)
+    say("[case] batch invariance, one-pass GQA decode")
+    w = W.random_ragged(13, "bf16", 64, 8, 128, [1, 1, 1, 1], [9000, 100, 3000, 2049])
+    r = Run(w)
+    q, kc, vc, _, _ = W.make_values(w, DEV)
+    full = r.forward(q, kc, vc).clone()
+    r.check_status()
+    rows, ref = oracle_rows_all(w, q, kc, vc)
+    assert_close(to_f64(full.index_select(0, torch.from_numpy(rows).to(DEV))), ref, "bf16", "one-pass GQA decode")
+    for s in range(w.num_seqs):
+        ws = W.Workload(**{**w.__dict__})
+        ws.context_lens = w.context_lens[s:s + 1].copy()
+        ws.block_tables = w.block_tables[s:s + 1].copy()
+        ws.query_start_loc = np.array([0, 1], np.int32)
+        rs = Run(ws)
+        one = rs.forward(q[s:s + 1].contiguous(), kc, vc)
+        rs.check_status()
+        assert torch.equal(one.view(torch.int16), full[s:s + 1].view(torch.int16)), s
+
+
+def test_gqa_decode_replayed_from_a_hip_graph(pa):
+    """The one-pass GQA decode (tagged completion counters in the workspace, left at zero by
+    the merging workgroup) captured once and replayed with new inputs: every replay equals
+    the eager call bit for bit, and the oracle on the last one."""
+    w = W.random_ragged(42, "bf16", 64, 8, 128, [1, 1, 1], [9000, 5000, 1500], with_slots=True)
+    say(f"[case] HIP graph replay of the one-pass GQA decode: L={list(w.context_lens)}")
+    check_tables_in_pool(w)
+    q, kc, vc, nk, nv = W.make_values(w, DEV)
+    r = Run(w)
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        r.write(nk, nv, kc, vc)
+        r.forward(q, kc, vc, out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        r.write(nk, nv, kc, vc)
+        r.forward(q, kc, vc, out)
+    gen = torch.Generator(device=DEV).manual_seed(4)
+    for rep in range(4):
+        W.fill_normal(q, gen)
+        W.fill_normal(nk, gen)
+        W.fill_normal(nv, gen)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.clone()
+        r.write(nk, nv, kc, vc)
+        ref_out = r.forward(q, kc, vc)
+        r.check_status()
+        assert torch.equal(got.view(torch.int16), ref_out.view(torch.int16)), f"replay {rep} differs"
+    rows, ref = oracle_rows_all(w, q, kc, vc)
+    assert_close(to_f64(got.index_select(0, torch.from_numpy(rows).to(DEV))), ref, "bf16", "graph replay, one-pass")
+
+
 # ---------------------------------------------------------------- the benchmark workloads
 
 def test_llama7b_decode_batch64(pa):
@@ -680,10 +740,10 @@ def to_f64_bits(bits):
     return layout.to_f64(bits, "bf16")
 
 
-def read_probe_case():
+def read_probe_case(pif):
     """Pages, a page list with one id outside the pool, and the sink the documented
     thread assignment gives: wavefront w XORs piece l, l+64, l+128, l+192 of its
-    pages 2w, 2w+1, 2w+2W, ... into lane l."""
+    pages pif*w .. pif*w+pif-1, pif*(w+W) .. into lane l."""
     rng = np.random.default_rng(11)
     npool, n, grid = 300, 257, 3
     words = rng.integers(0, 2**31 - 1, size=npool * 1024, dtype=np.int64).astype(np.int32)
@@ -693,22 +753,35 @@ def read_probe_case():
     want = np.zeros(grid * 256, dtype=np.uint32)
     nwaves = grid * 4
     for i, pid in enumerate(ids):
-        wave = (i // 2) % nwaves
+        wave = (i // pif) % nwaves
         page = pid if pid < npool else 0
         want[wave * 64:(wave + 1) * 64] ^= np.bitwise_xor.reduce(
             pages[page].transpose(1, 0, 2).reshape(64, 16), axis=1)
     return words, ids, grid, want
 
 
-def test_read_pages_probe(pa):
-    """The measurement-only page reader visits each listed page once, in the documented assignment."""
-    words, ids, grid, want = read_probe_case()
+@pytest.mark.parametrize("pif,mode", [(2, 0), (1, 0), (4, 1), (8, 0), (4, 2)])
+def test_read_pages_probe(pif, mode):
+    """The measurement library's page reader visits each listed page once, in the documented
+    assignment, for every depth and kind of load."""
+    import ctypes
+    from paged_kv_cache_57_amd import build as _b
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.pa_probe_read_pages.restype = ctypes.c_int32
+    lib.pa_probe_read_pages.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_void_p]
+    say(f"[case] page-read probe: {pif} pages in flight, mode {mode}")
+    words, ids, grid, want = read_probe_case(pif)
     pool = torch.from_numpy(words).to(DEV)
+    dids = torch.from_numpy(ids).to(DEV)
     sink = torch.full((grid * 256,), -1, dtype=torch.int32, device=DEV)
     status = torch.zeros(1, dtype=torch.int32, device=DEV)
-    pa.pa_read_pages(pool, torch.from_numpy(ids).to(DEV), sink, grid, status)
+    st = lib.pa_probe_read_pages(pool.data_ptr(), pool.numel() * 4, dids.data_ptr(), dids.numel(), sink.data_ptr(),
+                                 grid, pif, mode, status.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == 0
     torch.cuda.synchronize()
-    assert int(status.item()) == pa.PA_DEV_BAD_BLOCK
+    assert int(status.item()) == 1
     assert np.array_equal(sink.cpu().numpy().view(np.uint32), want)
 
 

@@ -32,6 +32,18 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
 
 
+def test_probe_library_exports_its_header(pa):
+    # the measurement-only page-read probe lives in libpa_probe.so, not in the product library
+    from paged_kv_cache_57_amd import build as _b
+    hdr = open(os.path.join(ROOT, "include", "pa_probe.h")).read()
+    names = set(re.findall(r"\b(pa_probe_\w+)\(", hdr))
+    assert names == {"pa_probe_read_pages", "pa_probe_last_error"}
+    nm = subprocess.run(["nm", "-D", "--defined-only", _b.PROBE_LIB], capture_output=True, text=True).stdout
+    assert names <= set(re.findall(r"\bT (pa_probe_\w+)", nm))
+    main = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True, text=True).stdout
+    assert "read_pages" not in main
+
+
 def test_library_exports_every_declared_function(pa):
     names = declared_functions()
     assert len(names) >= 20
