@@ -95,6 +95,7 @@ int32_t pa_abi_version(void);
  *   key, value    device, [num_tokens][num_kv_heads][head_dim] of dtype
  *   k_cache, v_cache  device, pool layout above, num_blocks blocks
  *   slot_mapping  device, int64 [num_tokens]
+ * PA_ERR_INVALID for num_kv_heads > 65535 (one launch dimension per head).
  */
 pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
@@ -119,6 +120,7 @@ pa_status pa_reshape_and_cache(const void* key, const void* value, void* k_cache
  *   key, value     device, [num_tokens][num_kv_heads][head_dim] of dtype
  *   positions      device, int32 [num_tokens]
  *   cos_table, sin_table  device, float32 [max_position][head_dim / 2]
+ * PA_ERR_INVALID for num_q_heads + num_kv_heads > 65535.
  */
 pa_status pa_rope_reshape_and_cache(void* q_out, const void* q, const void* key, const void* value,
                                     void* k_cache, void* v_cache, const int64_t* slot_mapping,

@@ -7,110 +7,121 @@
 namespace pa {
 namespace {
 
-// One workgroup per new token.  The token's key row is stored as head_dim/X
-// runs of 16 bytes (one per X-element group, 256 bytes apart inside the
-// page), its value row as one element per value column (32 or 64 bytes apart).
+// Workgroup (i, h) moves new tokens 16i .. 16i+15 of KV head h; thread (j, c) =
+// (tid % 16, tid / 16) takes token 16i + j's 16-byte group c of the key row
+// and of the value row.  Lanes that share c write their tokens' page offsets
+// side by side, so a run of tokens that fills a page in order (a prefill
+// chunk) leaves every value store instruction with whole 32-byte runs (16
+// tokens of one column) and every key store with a 256-byte run, and all of
+// a page's bytes pass through one L2 (a page split over several L2s would be
+// written back in pieces).  A token alone in its page (a decode step) still
+// writes one element per value column: the value page keeps each column's 16
+// tokens together for the attention kernels' operand loads.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void reshape_and_cache_kernel(
+__global__ __launch_bounds__(512) void reshape_and_cache_kernel(
     const T* __restrict__ key, const T* __restrict__ value, T* __restrict__ k_cache,
-    T* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int32_t num_blocks,
+    T* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, int32_t num_tokens, int32_t num_blocks,
     int32_t num_kv_heads, int32_t* dev_status) {
-  constexpr int X = Elem<T>::X;
-  constexpr int NCH = D / X;
-  const int t = blockIdx.x;
+  constexpr int X = Elem<T>::X;  // elements per 16 bytes; blockDim.x = 16 D / X
+  const int j = threadIdx.x & 15, c = threadIdx.x >> 4;
+  const int h = blockIdx.y;
+  const int t = blockIdx.x * kBlock + j;
+  if (t >= num_tokens) return;  // the last group's missing tokens (no barrier follows)
   const int64_t slot = slot_mapping[t];
-  if (slot < 0) return;
+  if (slot < 0) return;  // padding token
   if (slot >= (int64_t)num_blocks * kBlock) {
-    if (threadIdx.x == 0) flag_status(dev_status, PA_DEV_BAD_SLOT);
+    if (c == 0 && h == 0) flag_status(dev_status, PA_DEV_BAD_SLOT);
     return;
   }
   const int64_t b = slot / kBlock;
   const int o = (int)(slot % kBlock);
-  const int nq = num_kv_heads * NCH;
-  for (int qi = threadIdx.x; qi < nq; qi += blockDim.x) {
-    const int h = qi / NCH, c = qi % NCH;
-    const int64_t src = ((int64_t)t * num_kv_heads + h) * D + c * X;
-    const int64_t page = (b * num_kv_heads + h) * (int64_t)(kBlock * D);
-    // key: 16-byte run c of token o
-    st16(k_cache + page + ((int64_t)c * kBlock + o) * X, ld16(key + src));
-    // value: X consecutive columns of token o
-    union {
-      u32x4 v;
-      T e[X];
-    } u;
-    u.v = ld16(value + src);
+  const int64_t src = ((int64_t)t * num_kv_heads + h) * D + c * X;
+  const int64_t page = (b * num_kv_heads + h) * (int64_t)(kBlock * D);
+  // key: 16-byte run c of token o
+  st16(k_cache + page + ((int64_t)c * kBlock + o) * X, ld16(key + src));
+  // value: X consecutive columns of token o
+  union {
+    u32x4 v;
+    T e[X];
+  } u;
+  u.v = ld16(value + src);
 #pragma unroll
-    for (int x = 0; x < X; ++x) v_cache[page + (int64_t)(c * X + x) * kBlock + o] = u.e[x];
-  }
+  for (int x = 0; x < X; ++x) v_cache[page + (int64_t)(c * X + x) * kBlock + o] = u.e[x];
 }
 
-// Rotary embedding fused with the cache write: one workgroup per new token.
-// A unit is one 16-byte group c < head_dim/(2X) of one head together with
-// its partner group c + head_dim/(2X): the two hold the pairs (i, i + d/2)
-// that one rotation mixes.  Query units rotate q into q_out (which may be q:
-// every element is read and written by the same thread); key units rotate
-// the key and store both groups into the page and copy the same two value
-// groups.  Rotation in float32: x' = x c − y s, y' = y c + x s, each with one
-// rounded product and one fused multiply-add, then rounded to T.
+// Rotary embedding fused with the cache write.  Workgroup (i, y) takes new
+// tokens 16i .. 16i+15 and head y: query head y < num_q_heads, else KV head
+// y - num_q_heads.  Thread (j, c) takes token 16i + j's unit c < head_dim/(2X):
+// 16-byte group c together with its partner group c + head_dim/(2X), which
+// hold the pairs (i, i + d/2) that one rotation mixes.  A query unit rotates q
+// into q_out (which may be q: every element is read and written by the same
+// thread); a key unit rotates the key, stores both groups into the page and
+// copies the same two value groups, with the page-offset layout of the plain
+// cache write above.  Rotation in float32: x' = x c − y s, y' = y c + x s,
+// each with one rounded product and one fused multiply-add, then rounded to T.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void rope_cache_kernel(
     T* q_out, const T* q, const T* __restrict__ key, const T* __restrict__ value, T* __restrict__ k_cache,
     T* __restrict__ v_cache, const int64_t* __restrict__ slot_mapping, const int32_t* __restrict__ positions,
-    const float* __restrict__ cos_t, const float* __restrict__ sin_t, int32_t max_position, int32_t num_blocks,
-    int32_t num_q_heads, int32_t num_kv_heads, int32_t* dev_status) {
+    const float* __restrict__ cos_t, const float* __restrict__ sin_t, int32_t max_position, int32_t num_tokens,
+    int32_t num_blocks, int32_t num_q_heads, int32_t num_kv_heads, int32_t* dev_status) {
   constexpr int X = Elem<T>::X;
-  constexpr int HC = D / X / 2;  // units per head
-  const int t = blockIdx.x;
+  constexpr int HC = D / X / 2;  // units per head; blockDim.x = 16 HC
+  const int j = threadIdx.x & 15, c = threadIdx.x >> 4;
+  const int y = blockIdx.y;
+  const int t = blockIdx.x * kBlock + j;
+  if (t >= num_tokens) return;  // the last group's missing tokens (no barrier follows)
   const int pos = positions[t];
   if (pos < 0 || pos >= max_position) {
-    if (threadIdx.x == 0) flag_status(dev_status, PA_DEV_BAD_POSITION);
+    if (c == 0 && y == 0) flag_status(dev_status, PA_DEV_BAD_POSITION);
     return;
   }
-  const int64_t slot = slot_mapping[t];
-  const bool bad_slot = slot >= (int64_t)num_blocks * kBlock;
-  if (bad_slot && threadIdx.x == 0) flag_status(dev_status, PA_DEV_BAD_SLOT);
-  const bool write = slot >= 0 && !bad_slot;
-  const int64_t b = write ? slot / kBlock : 0;
-  const int o = write ? (int)(slot % kBlock) : 0;
-  const int nq = num_q_heads * HC;
-  const int nu = nq + (write ? num_kv_heads * HC : 0);
+  const bool isq = y < num_q_heads;
+  const int h = isq ? y : y - num_q_heads;
+  int64_t b = 0;
+  int o = 0;
+  if (!isq) {
+    const int64_t slot = slot_mapping[t];
+    if (slot >= (int64_t)num_blocks * kBlock) {
+      if (c == 0 && h == 0) flag_status(dev_status, PA_DEV_BAD_SLOT);
+      return;
+    }
+    if (slot < 0) return;  // padding token: nothing to store
+    b = slot / kBlock;
+    o = (int)(slot % kBlock);
+  }
   const float* crow = cos_t + (int64_t)pos * (D / 2);
   const float* srow = sin_t + (int64_t)pos * (D / 2);
-  for (int u = threadIdx.x; u < nu; u += blockDim.x) {
-    const bool isq = u < nq;
-    const int uu = isq ? u : u - nq;
-    const int h = uu / HC, c = uu % HC;
-    const int64_t src = ((int64_t)t * (isq ? num_q_heads : num_kv_heads) + h) * D + c * X;
-    const T* in = isq ? q : key;
-    union Grp {
-      u32x4 v;
-      T e[X];
-    } lo, hi;
-    lo.v = ld16(in + src);
-    hi.v = ld16(in + src + D / 2);
+  const int64_t src = ((int64_t)t * (isq ? num_q_heads : num_kv_heads) + h) * D + c * X;
+  const T* in = isq ? q : key;
+  union Grp {
+    u32x4 v;
+    T e[X];
+  } lo, hi;
+  lo.v = ld16(in + src);
+  hi.v = ld16(in + src + D / 2);
+#pragma unroll
+  for (int x = 0; x < X; ++x) {
+    const float cs = crow[c * X + x], sn = srow[c * X + x];
+    const float a = Elem<T>::to_f32(lo.e[x]), bb = Elem<T>::to_f32(hi.e[x]);
+    const float bs = bb * sn, as = a * sn;
+    lo.e[x] = Elem<T>::from_f32(__builtin_fmaf(a, cs, -bs));
+    hi.e[x] = Elem<T>::from_f32(__builtin_fmaf(bb, cs, as));
+  }
+  if (isq) {
+    st16(q_out + src, lo.v);
+    st16(q_out + src + D / 2, hi.v);
+  } else {
+    const int64_t page = (b * num_kv_heads + h) * (int64_t)(kBlock * D);
+    st16(k_cache + page + ((int64_t)c * kBlock + o) * X, lo.v);
+    st16(k_cache + page + ((int64_t)(c + HC) * kBlock + o) * X, hi.v);
+    Grp v0, v1;
+    v0.v = ld16(value + src);
+    v1.v = ld16(value + src + D / 2);
 #pragma unroll
     for (int x = 0; x < X; ++x) {
-      const float cs = crow[c * X + x], sn = srow[c * X + x];
-      const float a = Elem<T>::to_f32(lo.e[x]), bb = Elem<T>::to_f32(hi.e[x]);
-      const float bs = bb * sn, as = a * sn;
-      lo.e[x] = Elem<T>::from_f32(__builtin_fmaf(a, cs, -bs));
-      hi.e[x] = Elem<T>::from_f32(__builtin_fmaf(bb, cs, as));
-    }
-    if (isq) {
-      st16(q_out + src, lo.v);
-      st16(q_out + src + D / 2, hi.v);
-    } else {
-      const int64_t page = (b * num_kv_heads + h) * (int64_t)(kBlock * D);
-      st16(k_cache + page + ((int64_t)c * kBlock + o) * X, lo.v);
-      st16(k_cache + page + ((int64_t)(c + HC) * kBlock + o) * X, hi.v);
-      Grp v0, v1;
-      v0.v = ld16(value + src);
-      v1.v = ld16(value + src + D / 2);
-#pragma unroll
-      for (int x = 0; x < X; ++x) {
-        v_cache[page + (int64_t)(c * X + x) * kBlock + o] = v0.e[x];
-        v_cache[page + (int64_t)(D / 2 + c * X + x) * kBlock + o] = v1.e[x];
-      }
+      v_cache[page + (int64_t)(c * X + x) * kBlock + o] = v0.e[x];
+      v_cache[page + (int64_t)(D / 2 + c * X + x) * kBlock + o] = v1.e[x];
     }
   }
 }
@@ -153,8 +164,9 @@ template <typename T, int D>
 void launch_reshape(const void* key, const void* value, void* k_cache, void* v_cache,
                     const int64_t* slots, int32_t T_, int32_t nb, int32_t hkv, int32_t* st,
                     hipStream_t stream) {
-  hipLaunchKernelGGL((reshape_and_cache_kernel<T, D>), dim3(T_), dim3(256), 0, stream,
-                     (const T*)key, (const T*)value, (T*)k_cache, (T*)v_cache, slots, nb, hkv, st);
+  hipLaunchKernelGGL((reshape_and_cache_kernel<T, D>), dim3((T_ + kBlock - 1) / kBlock, hkv),
+                     dim3(kBlock * (D / Elem<T>::X)), 0, stream, (const T*)key, (const T*)value, (T*)k_cache,
+                     (T*)v_cache, slots, T_, nb, hkv, st);
 }
 
 }  // namespace
@@ -176,7 +188,8 @@ extern "C" pa_status pa_rope_reshape_and_cache(void* q_out, const void* q, const
     return fail(PA_ERR_INVALID, "%s: num_tokens %d, num_q_heads %d, max_position %d", fn, num_tokens,
                 num_q_heads, max_position);
   if (num_tokens == 0) return ok();
-  if (num_tokens > 2147483647 / 2 || (int64_t)num_q_heads * head_dim > (1 << 24))
+  if (num_tokens > 2147483647 / 2 || (int64_t)num_q_heads * head_dim > (1 << 24) ||
+      (int64_t)num_q_heads + num_kv_heads > 65535)
     return fail(PA_ERR_INVALID, "%s: too large", fn);
   if (!q_out || !q || !key || !value || !k_cache || !v_cache || !slot_mapping || !positions || !cos_table ||
       !sin_table)
@@ -184,9 +197,10 @@ extern "C" pa_status pa_rope_reshape_and_cache(void* q_out, const void* q, const
   hipStream_t s = (hipStream_t)stream;
   (void)hipGetLastError();
 #define PA_ROPE_LAUNCH(T, D)                                                                                   \
-  hipLaunchKernelGGL((rope_cache_kernel<T, D>), dim3(num_tokens), dim3(256), 0, s, (T*)q_out, (const T*)q,     \
-                     (const T*)key, (const T*)value, (T*)k_cache, (T*)v_cache, slot_mapping, positions,        \
-                     cos_table, sin_table, max_position, num_blocks, num_q_heads, num_kv_heads, dev_status)
+  hipLaunchKernelGGL((rope_cache_kernel<T, D>), dim3((num_tokens + kBlock - 1) / kBlock, num_q_heads + num_kv_heads), \
+                     dim3(kBlock * (D / Elem<T>::X / 2)), 0, s, (T*)q_out, (const T*)q, (const T*)key,           \
+                     (const T*)value, (T*)k_cache, (T*)v_cache, slot_mapping, positions, cos_table, sin_table,  \
+                     max_position, num_tokens, num_blocks, num_q_heads, num_kv_heads, dev_status)
   if (dtype == PA_BF16) {
     if (head_dim == 64) PA_ROPE_LAUNCH(bf16_t, 64);
     else PA_ROPE_LAUNCH(bf16_t, 128);
@@ -210,6 +224,7 @@ extern "C" pa_status pa_reshape_and_cache(const void* key, const void* value, vo
   pa_status st = check_pool_args(fn, num_blocks, num_kv_heads, head_dim, block_size, dtype);
   if (st != PA_OK) return st;
   if (num_tokens < 0) return fail(PA_ERR_INVALID, "%s: negative num_tokens", fn);
+  if (num_kv_heads > 65535) return fail(PA_ERR_INVALID, "%s: num_kv_heads %d (at most 65535)", fn, num_kv_heads);
   if (num_tokens == 0) return ok();
   if (!key || !value || !k_cache || !v_cache || !slot_mapping)
     return fail(PA_ERR_INVALID, "%s: NULL device pointer", fn);
