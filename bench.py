@@ -29,10 +29,19 @@ inputs resident in device memory before timing starts:
 
 The roofline object describes the dominant kernel, timed with HIP events
 recorded on the stream it runs on (pa_set_stage_events), against MI355X's
-8 TB/s HBM.  cpu_baseline times the fp64 CPU oracle on a bounded sample of
-the same workload on this host.
+8 TB/s HBM (decode workers) or 2.5 PFLOP/s dense bf16 MFMA at 2.4 GHz (the
+prefill tile worker); for a decode worker it also carries the page-read
+probe's rate over passes of the same size, measured in the same run, and the
+kernel's fraction of it.  step_ms gives the median / min / max device time of
+the timed steps, clock the shader clock sampled while they ran.
+cpu_baseline times the fp64 CPU oracle on a bounded sample of the same pass
+(query rows drawn uniformly from the pass's rows) on this host.
 
-    python bench.py [--workload splitfuse] [--steps 20] [--warmup 3] [--gpus 1]
+    python bench.py [--workload splitfuse] [--steps 100] [--warmup 5] [--gpus 1] [--rotate 1]
+
+--rotate 1 keeps one pool for every step: a pass that fits the 256 MB
+Infinity Cache (MALL) then finds its pages there ("kv_residency": "warm");
+by default enough pool copies are cycled that none can ("cold").
 """
 import argparse
 import ctypes
@@ -167,52 +176,78 @@ def work_split(w):
     return work
 
 
+def host_info():
+    """The host the CPU baseline ran on: CPU model, BLAS pools and library versions."""
+    import platform
+
+    import torch
+    info = {"cpu_model": None, "host_cpus": len(os.sched_getaffinity(0)), "python": platform.python_version(),
+            "numpy": np.__version__, "torch": torch.__version__, "blas": []}
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    info["cpu_model"] = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        import threadpoolctl
+        info["blas"] = [{k: p.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer")}
+                        for p in threadpoolctl.threadpool_info()]
+    except Exception:
+        pass
+    return info
+
+
 def cpu_baseline(w, q, kc, vc, budget_s):
-    """fp64 oracle on a bounded sample of the workload's decode sequences (host copies of their bytes)."""
+    """The fp64 oracle on a bounded sample of the pass: query rows drawn uniformly
+    from all of the pass's rows (so prefill-chunk rows and decode rows come in
+    the pass's own proportion), each attended at its position over host copies
+    of its sequence's pages.  Only the oracle calls are timed."""
     import torch
 
     from oracle import attention as oattn
     ql = np.diff(w.query_start_loc)
-    dec = np.flatnonzero(ql == 1)
-    pool = dec if dec.size else np.arange(w.num_seqs)
+    seq_of_row = np.repeat(np.arange(w.num_seqs), ql)
     rng = np.random.default_rng(123)
-    order = rng.permutation(pool)
+    order = rng.permutation(w.num_tokens)
 
     def raw(t):
         t = t.detach().cpu()
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
-    done_tokens = 0
+    pages = {}
     spent = 0.0
+    rows = chunk_rows = 0
     kv_bytes = 0
-    n = 0
-    for s in order:
+    for t in order:
+        s = int(seq_of_row[t])
         Ls = int(w.context_lens[s])
         nb = (Ls + 15) // 16
-        ids = torch.from_numpy(w.block_tables[s, :nb].astype(np.int64)).to(kc.device)
-        kp, vp = raw(kc.index_select(0, ids)), raw(vc.index_select(0, ids))
+        if s in pages:
+            kp, vp = pages[s]
+        else:
+            ids = torch.from_numpy(w.block_tables[s, :nb].astype(np.int64)).to(kc.device)
+            kp, vp = raw(kc.index_select(0, ids)), raw(vc.index_select(0, ids))
+            if ql[s] > 1:
+                pages[s] = (kp, vp)  # a prefill chunk's rows are drawn many times
         a, b = int(w.query_start_loc[s]), int(w.query_start_loc[s + 1])
         qh = raw(q[a:b])
         tab = np.arange(nb, dtype=np.int32)[None]
         t0 = time.perf_counter()
         oattn.paged_attention(qh, kp, vp, tab, np.array([Ls], np.int32), np.array([0, b - a], np.int32),
-                              w.scale, w.dtype)
+                              w.scale, w.dtype, tokens=[int(t) - a])
         spent += time.perf_counter() - t0
-        done_tokens += b - a
-        kv_bytes += Ls * kv_token_bytes(w)
-        n += 1
+        rows += 1
+        chunk_rows += int(ql[s] > 1)
+        kv_bytes += (Ls - (b - 1 - int(t))) * kv_token_bytes(w)  # keys this row sees
         if spent >= budget_s:
             break
-    threads = None
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max((i.get("num_threads", 1) for i in info), default=1)
-    except Exception:
-        pass
-    cores = threads or 1
-    return {"tokens": done_tokens, "seconds": spent, "kv_bytes": kv_bytes, "seqs": n, "cores": cores,
-            "host_cpus": len(os.sched_getaffinity(0))}
+    host = host_info()
+    threads = max([b["num_threads"] or 1 for b in host["blas"]] or [1])
+    return {"rows": rows, "chunk_rows": chunk_rows, "seconds": spent, "kv_bytes": kv_bytes, "cores": threads,
+            "host": host}
 
 
 def copy_calibration(torch, dev, args, nbytes=4 << 30):
@@ -459,11 +494,104 @@ def sampling_workflow(torch, pa, W, dev, args):
         "forward_share_of_step": round(fwd_ms_mean / ms_per_step, 4)}), flush=True)
 
 
+class ClockSampler:
+    """Samples the shader clock (the level sysfs pp_dpm_sclk marks current) every
+    few milliseconds on a thread while the timed steps run."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        import threading
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if paths else None
+        self.period = period_s
+        self.samples = []
+        self.levels = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                lines = f.read().splitlines()
+        except OSError:
+            return None, []
+        cur, levels = None, []
+        for line in lines:
+            try:
+                mhz = int(line.split(":", 1)[1].strip().split("Mhz")[0])
+            except (IndexError, ValueError):
+                continue
+            levels.append(mhz)
+            if line.rstrip().endswith("*"):
+                cur = mhz
+        return cur, levels
+
+    def _run(self):
+        while not self._stop.is_set():
+            cur, levels = self._read()
+            if cur is not None:
+                self.samples.append(cur)
+                self.levels = levels
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.path:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"source": "sysfs pp_dpm_sclk", "samples": 0}
+        x = np.array(self.samples)
+        return {"source": "sysfs pp_dpm_sclk (current level, sampled every 2 ms over the timed steps; "
+                          "a run of a few ms also catches the ramp from idle)",
+                "samples": int(x.size), "median_mhz": int(np.median(x)), "min_mhz": int(x.min()),
+                "max_mhz": int(x.max()), "top_level_mhz": int(max(self.levels)) if self.levels else None,
+                "peak_assumes_mhz": 2400}
+
+
+def probe_ceiling(torch, dev, pass_bytes, steps=12, warmup=2, pif=4, mode=1, pool_bytes=4 << 30):
+    """The page-read probe (non-temporal 16-byte loads, pif pages per wavefront in
+    flight) over passes of the dominant kernel's size: random 4 KiB pages of a
+    4 GiB pool, a different slice each step, timed with a HIP event between
+    consecutive launches (launches back to back).  Returns (GB/s median, bytes per pass)."""
+    probe = ProbeLib()
+    pool = torch.empty(pool_bytes // 4, dtype=torch.int32, device=dev).fill_(7)
+    npages = pool_bytes // 4096
+    per = int(min(npages, max(1, pass_bytes // 4096)))
+    order = torch.from_numpy(np.random.default_rng(5).permutation(npages).astype(np.int32)).to(dev)
+    nslices = max(1, npages // per)
+    g = min(2048, max(1, (per + 4 * pif - 1) // (4 * pif)))
+    sink = torch.empty(g * 256, dtype=torch.int32, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    for i in range(warmup):
+        probe.read_pages(torch, pool, order[(i % nslices) * per:(i % nslices + 1) * per], sink, g, pif, mode, status)
+    # launches back to back, an event between each two (the device time of each)
+    ev[0].record()
+    for i in range(steps):
+        k = (warmup + i) % nslices
+        probe.read_pages(torch, pool, order[k * per:(k + 1) * per], sink, g, pif, mode, status)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError(f"pa_probe_read_pages flagged status {int(status.item())}")
+    ms = float(np.median([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]))
+    del pool
+    torch.cuda.empty_cache()
+    return per * 4096 / (ms * 1e-3) / 1e9, per * 4096
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="splitfuse",
                     choices=["splitfuse", "splitfuse_rope", "llama7b", "gqa70b", "gqa70b_long", "tiny", "copy", "read",
                              "sampling"])
@@ -554,13 +682,19 @@ def main():
     if int(status.item()) != 0:
         raise RuntimeError(f"device status {int(status.item()):#x}")
 
-    # timed steps: nothing but the path itself on the stream
+    # timed steps: nothing but the path itself on the stream (an event between
+    # steps gives each step's device time)
     K = args.steps
-    t0 = time.perf_counter()
-    for k in range(K):
-        step(args.warmup + k)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    step_ev = ev.new(K + 1)
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        ev.record(step_ev[0], stream)
+        for k in range(K):
+            step(args.warmup + k)
+            ev.record(step_ev[k + 1], stream)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    step_ms = np.array([ev.ms(step_ev[k], step_ev[k + 1]) for k in range(K)])
 
     # the same steps again with HIP events around every stage (kernel durations)
     stage_ev = [ev.new(2 * len(STAGES)) for _ in range(K)]
@@ -569,8 +703,8 @@ def main():
         step(args.warmup + K + k, stage_ev[k], write_ev[k])
     torch.cuda.synchronize()
     pa.pa_set_stage_events(None)
-    stage_ms = {name: float(np.mean([ev.ms(e[2 * j], e[2 * j + 1]) for e in stage_ev]))
-                for j, name in enumerate(STAGES)}
+    stage_all = {name: np.array([ev.ms(e[2 * j], e[2 * j + 1]) for e in stage_ev]) for j, name in enumerate(STAGES)}
+    stage_ms = {name: float(np.mean(v)) for name, v in stage_all.items()}
     write_ms = float(np.mean([ev.ms(e[0], e[1]) for e in write_ev])) if slots is not None else 0.0
     ev.close()
     if int(status.item()) != 0:
@@ -589,10 +723,17 @@ def main():
         result.update(value=round(w.num_tokens / (ms_per_step * 1e-3), 1), unit="tokens/s")
     else:
         result.update(value=round(pass_bytes / (ms_per_step * 1e-3) / 1e9, 2), unit="GB/s")
+    result["step_ms"] = {"median": round(float(np.median(step_ms)), 4), "min": round(float(step_ms.min()), 4),
+                         "max": round(float(step_ms.max()), 4), "source": "HIP events between the timed steps"}
     result["config"] = {"workload": w.name, "num_seqs": w.num_seqs, "query_tokens": w.num_tokens,
                         "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
                         "block_size": 16, "max_context_len": w.max_context_len, "pool_blocks": w.num_blocks,
-                        "pool_copies_rotated": rotate}
+                        "pool_copies_rotated": rotate,
+                        "kv_residency": ("cold: pool copies cycled past the 256 MB MALL" if rotate > 1 else
+                                         "warm: one pool every step, the pass fits the 256 MB MALL"
+                                         if pass_bytes <= MALL_BYTES else
+                                         f"one pool every step; the pass ({pass_bytes / 1e6:.0f} MB) exceeds "
+                                         f"the 256 MB MALL")}
     traffic = measured_traffic(w.name, DOMINANT_KERNEL[(dom, w.dtype, w.head_dim)])
     if dom == "tile_worker":
         achieved = work[dom]["flops"] / (stage_ms[dom] * 1e-3) / 1e12
@@ -605,6 +746,22 @@ def main():
         result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                               "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom,
                               "kernel_ms": round(stage_ms[dom], 4), "algorithmic_bytes": work[dom]["bytes"]}
+    dk = stage_all[dom]
+    result["roofline"]["kernel_ms_median_min_max"] = [round(float(np.median(dk)), 4), round(float(dk.min()), 4),
+                                                      round(float(dk.max()), 4)]
+    if dom != "tile_worker":
+        # the attainable rate for a pure page-read loop over passes of the same size
+        probe_gbps, probe_bytes = probe_ceiling(torch, dev, work[dom]["bytes"])
+        long_gbps, long_bytes = (probe_gbps, probe_bytes) if probe_bytes >= 4 << 30 else \
+            probe_ceiling(torch, dev, 4 << 30)
+        result["roofline"]["read_probe"] = {
+            "GBps": round(probe_gbps, 1), "pass_bytes": probe_bytes,
+            "frac_of_probe": round(result["roofline"]["achieved"] / probe_gbps, 4),
+            "GBps_4GiB_pass": round(long_gbps, 1),
+            "frac_of_4GiB_probe": round(result["roofline"]["achieved"] / long_gbps, 4),
+            "probe": "random 4 KiB pages, non-temporal 16-byte loads, 4 pages per wavefront in flight "
+                     "(libpa_probe pa_probe_read_pages), HIP events between back-to-back launches"}
+    result["clock"] = clock.summary()
     result["stages_ms"] = {k: round(v, 4) for k, v in stage_ms.items()}
     if slots is not None:
         result["stages_ms"]["rope_cache_write" if rope else "cache_write"] = round(write_ms, 4)
@@ -623,13 +780,16 @@ def main():
                                                                                    w.head_dim)])}
     if not args.no_cpu_baseline:
         cb = cpu_baseline(w, q, kc, vc, args.cpu_seconds)
+        mixed = args.workload in ("splitfuse", "splitfuse_rope")
         result["cpu_baseline"] = {
-            "value": round(cb["tokens"] / cb["seconds"], 3) if args.workload in ("splitfuse", "splitfuse_rope")
-            else round(cb["kv_bytes"] / cb["seconds"] / 1e9, 4),
-            "unit": "tokens/s" if args.workload in ("splitfuse", "splitfuse_rope") else "GB/s",
+            "value": round(cb["rows"] / cb["seconds"], 3) if mixed else round(cb["kv_bytes"] / cb["seconds"] / 1e9, 4),
+            "unit": "tokens/s" if mixed else "GB/s",
             "cores": cb["cores"], "kind": "oracle",
-            "sample": f"{cb['seqs']} decode sequences of this batch (gather + fp64 attention over host copies "
-                      f"of their pages), {cb['seconds']:.1f} s on {cb['host_cpus']} host CPUs"}
+            "sample": f"{cb['rows']} query rows drawn uniformly from the pass's {w.num_tokens} "
+                      f"({cb['chunk_rows']} prefill-chunk rows, {cb['rows'] - cb['chunk_rows']} decode rows), each "
+                      f"attended at its position by the fp64 oracle (gather + attention over host copies of its "
+                      f"sequence's pages): {cb['seconds']:.1f} s of oracle time",
+            "host": cb["host"]}
     print(json.dumps(result), flush=True)
 
 
