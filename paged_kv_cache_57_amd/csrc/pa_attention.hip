@@ -48,7 +48,7 @@ constexpr int kPartMfmaPrefill = 1024;  // keys per partition of a small multi-r
 constexpr int kPartTile = 1024;         // keys per partition of a 256-row tile
 constexpr int kTileRows = 16;           // query rows per MFMA item
 constexpr int kTileWaves = 8;           // wavefronts per TILE workgroup, 32 rows each
-constexpr int kTileStages = 3;          // LDS stages of the TILE worker's load pipeline
+constexpr int kTileStages = 4;          // LDS stages of the TILE worker's load pipeline (2 per barrier)
 constexpr int kBigRows = 32 * kTileWaves;  // query rows per TILE item
 constexpr int kMaxWorkerGroups = 2048;  // persistent workgroups per worker launch
 constexpr int kMaxTileGroups = 256;     // TILE workgroups (one per compute unit)
@@ -1045,9 +1045,9 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void gqa_decode_kernel(AttnParam
 // lane l's operand of block b), so every operand read is 64 consecutive
 // 16-byte pieces.  Every wavefront loads two 1 KiB blocks of each step, three
 // steps ahead into one of two register sets, and stores them two steps ahead
-// into a three-stage ring; one barrier per step publishes the stored stage and
-// frees the stage read two steps earlier.  The 256 rows of an item share every
-// key and value piece it reads from HBM (or L2).
+// into a four-stage ring; one barrier per two steps publishes the two stages
+// stored since the last one and frees the two read before it.  The 256 rows of
+// an item share every key and value piece it reads from HBM (or L2).
 // Softmax ("第 15 章" §15.1 recurrence): scores stay unscaled until the
 // exponent (p = 2^(s·c − m) with c = |scale|·log2 e, one FMA; a negative scale
 // flips the sign bits of q instead, which is exact), and a row's reference m
@@ -1336,9 +1336,12 @@ __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParam
       // One step of the loop, unrolled by two so that each register set stays in fixed
       // registers: set rs_put holds step st+2 (stored at the end), set rs_fetch receives
       // step st+3.  Fetches past the last step read the last step again, so the number of
-      // loads in flight is the same on every path.
+      // loads in flight is the same on every path.  One barrier per two steps: the one
+      // before an even step st publishes stages st and st+1 (stored in steps st-2 and
+      // st-1) and frees stages st-2 and st-1, which steps st and st+1 overwrite with st+2
+      // and st+3 (a ring of four stages).
       auto step = [&](int st, u32x4 (&rs_fetch)[BPW], u32x4 (&rs_put)[BPW]) {
-        __syncthreads();  // stage st+1 is stored; stage st-1 is free
+        if ((st & 1) == 0) __syncthreads();
         fetch(min(st + 3, nsteps - 1), rs_fetch);
         if (st < nw) {
           f32x16 c;
