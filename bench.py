@@ -734,17 +734,23 @@ def main():
                                          if pass_bytes <= MALL_BYTES else
                                          f"one pool every step; the pass ({pass_bytes / 1e6:.0f} MB) exceeds "
                                          f"the 256 MB MALL")}
-    traffic = measured_traffic(w.name, DOMINANT_KERNEL[(dom, w.dtype, w.head_dim)])
+    # a batch of single-position GQA decodes runs in one dispatch of gqa_decode_kernel (the
+    # library times it as its MFMA-worker stage)
+    G = w.num_q_heads // w.num_kv_heads
+    one_pass = w.dtype == "bf16" and w.max_q_len == 1 and 2 <= G <= 16
+    dom_kernel = f"gqa_decode_kernel<{w.head_dim}>" if one_pass and dom == "mfma_worker" else \
+        DOMINANT_KERNEL[(dom, w.dtype, w.head_dim)]
+    traffic = measured_traffic(w.name, dom_kernel)
     if dom == "tile_worker":
         achieved = work[dom]["flops"] / (stage_ms[dom] * 1e-3) / 1e12
         result["roofline"] = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                              "traffic": traffic, "kernel": dom, "kernel_ms": round(stage_ms[dom], 4),
+                              "traffic": traffic, "kernel": dom_kernel, "kernel_ms": round(stage_ms[dom], 4),
                               "algorithmic_flops": work[dom]["flops"]}
     else:
         achieved = work[dom]["bytes"] / (stage_ms[dom] * 1e-3) / 1e9
         result["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                              "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom,
+                              "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic, "kernel": dom_kernel,
                               "kernel_ms": round(stage_ms[dom], 4), "algorithmic_bytes": work[dom]["bytes"]}
     dk = stage_all[dom]
     result["roofline"]["kernel_ms_median_min_max"] = [round(float(np.median(dk)), 4), round(float(dk.min()), 4),
