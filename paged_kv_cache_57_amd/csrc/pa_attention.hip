@@ -144,6 +144,11 @@ struct AttnParams {
 // its partitions fill the members' partial slots 0 .. nps-1.  A member
 // skips the shared keys and numbers its own partitions from nps on.
 constexpr int kEntValid = 1, kEntGroup = 2, kEntMember = 4;
+// kEntShared: the sequence's first page is also the first page of the sequence
+// before or after it in the batch (forked branches of one prompt, beams):
+// their pages are read by several sequences of the pass, so its workers load
+// them with plain loads that let the other reads hit in the caches.
+constexpr int kEntShared = 8;
 
 struct SeqInfo {
   int a, q_len, L, flags;
@@ -328,6 +333,13 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
           si.flags |= kEntMember;
         }
       }
+      if (si.ok && si.L > 0) {
+        const int32_t first = p.block_tables[(int64_t)s * p.mbps];
+        const bool prev = s > 0 && p.context_lens[s - 1] > 0 && p.block_tables[(int64_t)(s - 1) * p.mbps] == first;
+        const bool next = s + 1 < p.num_seqs && p.context_lens[s + 1] > 0 &&
+                          p.block_tables[(int64_t)(s + 1) * p.mbps] == first;
+        if (prev || next) si.flags |= kEntShared;
+      }
       p.seqinfo[s] = i32x4{si.a, si.q_len, si.L, si.flags};
       if (!si.ok) {
         flag_status(p.dev_status, PA_DEV_BAD_LENGTH);
@@ -460,7 +472,8 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
 #pragma unroll
     for (int k = 0; k < NIV; ++k) acc[k] = 0.f;
 
-    if (kv_lo < kv_hi) {
+    auto attend = [&](auto stream_tag) {
+      constexpr bool kStream = decltype(stream_tag)::value;
       const int nblk = (kv_hi - kv_lo + kBlock - 1) / kBlock;
       const int bidv = load_block_ids(p, s, kv_lo / kBlock, nblk, lane);
 
@@ -482,10 +495,10 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
             const T* vp = vc + page;
 #pragma unroll
             for (int k = 0; k < NIK; ++k)
-              kr[j][k] = ld16_stream(kp + ((4 * k + (lane >> 4)) * kBlock + (lane & 15)) * X);
+              kr[j][k] = ld16_page<kStream>(kp + ((4 * k + (lane >> 4)) * kBlock + (lane & 15)) * X);
 #pragma unroll
             for (int k = 0; k < NIV; ++k)
-              vr[j][k] = ld16_stream(vp + (RPI * k + lane / LPR) * kBlock + (lane % LPR) * X);
+              vr[j][k] = ld16_page<kStream>(vp + (RPI * k + lane / LPR) * kBlock + (lane % LPR) * X);
           } else {
 #pragma unroll
             for (int k = 0; k < NIK; ++k) kr[j][k] = u32x4{0, 0, 0, 0};
@@ -558,6 +571,10 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
         }
         wave_lds_sync();
       }
+    };
+    if (kv_lo < kv_hi) {  // wave-uniform
+      if (si.flags & kEntShared) attend(std::false_type{});
+      else attend(std::true_type{});
     }
     // finish: l over all lanes, each value column over its LPR lanes
     const float l = wave_sum(lsum);
@@ -608,7 +625,7 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
 // PIPE: the next step's pages are in flight while a step computes.  That takes
 // twice the registers for pages, so the query operand then lives in qs, a
 // wavefront-private LDS area of D/32 x 64 entries, and is read back each step.
-template <int D, bool PIPE>
+template <int D, bool PIPE, bool STREAM>
 __device__ inline void mfma_tile(const AttnParams& p, int trow, int kvh, int t, int hh, int pos_r, int pos_lo,
                                  int kv_lo, int kv_hi, float& m_r, float& lsum, f32x4 (&oacc)[D / 16],
                                  bf16x8* qs = nullptr) {
@@ -655,14 +672,14 @@ __device__ inline void mfma_tile(const AttnParams& p, int trow, int kvh, int t, 
 #pragma unroll
       for (int k = 0; k < KS; ++k) {
         const int off = ((4 * k + g4) * kBlock + r) * 8;
-        st.k0[k] = __builtin_bit_cast(bf16x8, ld16_stream(kc + pg0 + off));
-        st.k1[k] = __builtin_bit_cast(bf16x8, ld16_stream(kc + pg1 + off));
+        st.k0[k] = __builtin_bit_cast(bf16x8, ld16_page<STREAM>(kc + pg0 + off));
+        st.k1[k] = __builtin_bit_cast(bf16x8, ld16_page<STREAM>(kc + pg1 + off));
       }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int off = (16 * j + r) * kBlock + 4 * g4;
-        const u32x2 lo = ld8_stream(vc + pg0 + off);
-        const u32x2 hi = ld8_stream(vc + pg1 + off);
+        const u32x2 lo = ld8_page<STREAM>(vc + pg0 + off);
+        const u32x2 hi = ld8_page<STREAM>(vc + pg1 + off);
         st.vw[j][0] = lo[0];
         st.vw[j][1] = lo[1];
         st.vw[j][2] = hi[0];
@@ -819,7 +836,10 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
 
     const int pos_lo = grp ? si.L - 1 : si.L - si.q_len + (tile * kTileRows) / p.G;  // lowest row position
     // a group reads its first member's table
-    mfma_tile<D, false>(p, ex.trow, kvh, t, hh, pos_r, pos_lo, kv_lo, kv_hi, m_r, lsum, oacc);
+    if (!grp && (si.flags & kEntShared))  // wave-uniform; a group's shared pages are read once
+      mfma_tile<D, false, false>(p, ex.trow, kvh, t, hh, pos_r, pos_lo, kv_lo, kv_hi, m_r, lsum, oacc);
+    else
+      mfma_tile<D, false, true>(p, ex.trow, kvh, t, hh, pos_r, pos_lo, kv_lo, kv_hi, m_r, lsum, oacc);
     const float l = sum_over_rows(lsum);
     if (!grp && ex.nps == 0 && w.nparts == 1) {
       bf16_t* orow = (bf16_t*)p.out + ((int64_t)t * p.Hq + hh) * D;
@@ -918,8 +938,17 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void gqa_decode_kernel(AttnParam
   f32x4 oacc[NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) oacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (kv_lo < kv_hi)  // wave-uniform
-    mfma_tile<D, true>(p, s, kvh, t, hh, pos, pos, kv_lo, kv_hi, m_r, lsum, oacc, q_lds[wv]);
+  // pages shared with a neighbouring sequence (forks of one prompt) are loaded plain
+  const int32_t first_blk = p.block_tables[(int64_t)s * p.mbps];
+  const bool shared = (s > 0 && p.context_lens[s - 1] > 0 && p.block_tables[(int64_t)(s - 1) * p.mbps] == first_blk) ||
+                      (s + 1 < p.num_seqs && p.context_lens[s + 1] > 0 &&
+                       p.block_tables[(int64_t)(s + 1) * p.mbps] == first_blk);
+  if (kv_lo < kv_hi) {  // wave-uniform
+    if (wave_uniform((int)shared))
+      mfma_tile<D, true, false>(p, s, kvh, t, hh, pos, pos, kv_lo, kv_hi, m_r, lsum, oacc, q_lds[wv]);
+    else
+      mfma_tile<D, true, true>(p, s, kvh, t, hh, pos, pos, kv_lo, kv_hi, m_r, lsum, oacc, q_lds[wv]);
+  }
   const float l = sum_over_rows(lsum);
   // every lane of a row stores the same m and l; each lane its own columns
 #pragma unroll

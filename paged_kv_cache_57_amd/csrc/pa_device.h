@@ -87,6 +87,20 @@ __device__ inline u32x2 ld8_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 }
 
+// A KV page load: non-temporal when each page of the pass is read once (kStream),
+// plain when other sequences of the same pass read the same pages, so that their
+// reads can hit in L2 or the Infinity Cache.
+template <bool kStream>
+__device__ inline u32x4 ld16_page(const void* p) {
+  if constexpr (kStream) return ld16_stream(p);
+  else return ld16(p);
+}
+template <bool kStream>
+__device__ inline u32x2 ld8_page(const void* p) {
+  if constexpr (kStream) return ld8_stream(p);
+  else return *reinterpret_cast<const u32x2*>(p);
+}
+
 __device__ inline void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // One word stored / loaded coherently for the whole GPU (relaxed, agent scope): the
