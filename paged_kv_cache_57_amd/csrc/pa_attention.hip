@@ -1060,7 +1060,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void gqa_decode_kernel(AttnParam
 // item.  Every product is a 32x32x16 MFMA (v_mfma_f32_32x32x16_*):
 //  Scores, transposed: Sᵀ[key][row] = K · Qᵀ, 32 keys x 32 rows per MFMA,
 //  D/16 MFMAs over the head dimension.  Lane l holds row l%32 and, in
-//  accumulator j, the key tile_key(j, l/32) of the 32-key step: the key
+//  accumulator j, key 16(j/8) + 8(l/32) + j%8 of the 32-key step: the key
 //  operand's rows are loaded in a permuted order (bits 2 and 3 of the key
 //  index swapped) so that each lane ends with 8 consecutive keys per 16-key
 //  block, which is the layout P·V needs for its B operand, with no exchange.
