@@ -53,6 +53,9 @@ constexpr int kBigRows = 32 * kTileWaves;  // query rows per TILE item
 constexpr int kMaxWorkerGroups = 2048;  // persistent workgroups per worker launch
 constexpr int kMaxTileGroups = 256;     // TILE workgroups (one per compute unit)
 constexpr int kXcds = 8;                // XCDs (each with its own L2); TILE items are sliced per XCD
+constexpr int kHwRegXccId = (3 << 11) | 20;  // s_getreg operand: HW_REG_XCC_ID, bits 3:0
+constexpr int kValuGridPerResident = 4;  // VALU grid: this many times the resident workgroups
+constexpr int kValuTicket = 64;         // ctrl word of the VALU ticket counter (bytes 256..259 of the workspace)
 constexpr float kLazyRescale = 8.f;     // MFMA worker: raise the exponent reference only past this growth (log2)
 constexpr float kTileLazyRescale = 7.f; // TILE worker: the same, bounded so that 2^8 p stays below the half maximum
 constexpr int kMergeSplitParts = 32;    // partitions per row from which four wavefronts merge a row
@@ -119,7 +122,9 @@ struct AttnParams {
   int32_t Hq, Hkv, G, num_blocks;
   float scale_log2;
   int32_t is_f32;
-  int32_t* ctrl;  // [2] VALU items, [3] MFMA items, [4] TILE items, [5] rows to merge, [8..15] TILE tickets per XCD slice
+  int32_t* ctrl;  // [2] VALU items, [3] MFMA items, [4] TILE items, [5] rows to merge, [6] some sequence
+                  // shares pages with a neighbour, [8..15] TILE tickets per XCD slice, [kValuTicket] VALU
+                  // tickets (on a 256-byte line of its own)
   int32_t* pre_v;  // exclusive prefix over sequences of VALU items, [S + 1]
   int32_t* pre_m;  // ... of MFMA items
   int32_t* pre_t;  // ... of TILE items
@@ -137,6 +142,8 @@ struct AttnParams {
   // One-pass GQA decode: completion counters per (sequence, KV head) and the call's tag.
   unsigned long long* dec_ctr;
   uint32_t call_tag;
+  // VALU worker: workgroups resident on the device at once (at most the grid)
+  int32_t valu_resident;
 };
 
 // Entry flags.  A group entry's rows are its members' single decode rows,
@@ -211,6 +218,7 @@ __device__ inline SkipTable stage_skip(int* sk, const int32_t* pre, int n) {
   SkipTable t;
   t.stride = (n + kSkip) / kSkip;  // ceil((n + 1) / kSkip)
   t.count = n / t.stride + 1;      // entries i * stride <= n
+#pragma unroll 8
   for (int i0 = 0; i0 < t.count; i0 += (int)blockDim.x) {
     const int i = min(i0 + (int)threadIdx.x, t.count - 1);  // threads past the end repeat the last entry
     sk[i] = pre[i * t.stride];
@@ -312,9 +320,11 @@ __device__ inline void plan_groups(const AttnParams& p, int tid) {
 __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
   __shared__ i32x4 wsum[16];
   __shared__ i32x4 carry;
+  __shared__ int any_shared;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   if (tid == 0) {
     carry = i32x4{0, 0, 0, 0};
+    any_shared = 0;
     if (p.qsl[0] != 0 || p.qsl[p.num_seqs] != p.T) flag_status(p.dev_status, PA_DEV_BAD_LENGTH);
   }
   if (p.num_groups > 0) plan_groups(p, tid);
@@ -338,7 +348,10 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
         const bool prev = s > 0 && p.context_lens[s - 1] > 0 && p.block_tables[(int64_t)(s - 1) * p.mbps] == first;
         const bool next = s + 1 < p.num_seqs && p.context_lens[s + 1] > 0 &&
                           p.block_tables[(int64_t)(s + 1) * p.mbps] == first;
-        if (prev || next) si.flags |= kEntShared;
+        if (prev || next) {
+          si.flags |= kEntShared;
+          any_shared = 1;  // every writer stores the same value
+        }
       }
       p.seqinfo[s] = i32x4{si.a, si.q_len, si.L, si.flags};
       if (!si.ok) {
@@ -387,19 +400,23 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
     p.ctrl[3] = carry[1];
     p.ctrl[4] = carry[2];
     p.ctrl[5] = carry[3];
+    p.ctrl[6] = any_shared;
     for (int x = 0; x < kXcds; ++x) p.ctrl[8 + x] = 0;  // TILE tickets handed out so far, per XCD slice
+    p.ctrl[kValuTicket] = 0;                             // VALU tickets handed out so far
   }
 }
 
 // Work distribution and control flow in the workers: a wavefront walks the
-// items wave_id, wave_id + nwaves, ... with both numbers made uniform by
-// readfirstlane, and nothing inside an item branches on the lane index.
-// Lane-dependent branches around the loop (for example "lane 0 fetches the
-// next item, then everyone reads it back") were merged by the compiler across
-// the loop's back edge into an inner loop that only lane 0 leaves, after which
-// the other lanes ran on with a stale item and read lane values of a lane that
-// was no longer active.  So stores are unconditional (lanes holding the same
-// value write the same address) and loads use clamped, always-valid indices.
+// items wave_id, wave_id + nwaves, ... (or takes them from a ticket counter,
+// below) with the item made uniform by readfirstlane, and nothing inside an
+// item branches on the lane index.  Lane-dependent branches around the loop
+// (for example "lane 0 fetches the next item, then everyone reads it back")
+// were merged by the compiler across the loop's back edge into an inner loop
+// that only lane 0 leaves, after which the other lanes ran on with a stale
+// item and read lane values of a lane that was no longer active.  So stores
+// are unconditional (lanes holding the same value write the same address),
+// loads use clamped, always-valid indices, and a ticket is taken by thread 0
+// between two workgroup barriers and read back from LDS.
 __device__ inline int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Physical block ids of this partition's pages: lane j holds page j (lanes
@@ -421,6 +438,8 @@ __device__ inline void wave_lds_sync() {
 
 // ---------------------------------------------------------------- VALU worker
 // One wavefront per item: one query row x one query head x one key partition.
+// Workgroups of one wavefront, as many as fit on the GPU at once, walk the items
+// (see the item loop for their order).
 // Keys are processed 64 at a time (4 pages).  Lane layout of a key page
 // [D/X][16][X]: load i of page j gives lane l the 16-byte group 4i + l/16 of
 // key l%16, so each lane accumulates a partial dot over D/4 elements and two
@@ -429,7 +448,7 @@ __device__ inline void wave_lds_sync() {
 // X consecutive keys of one value column, so P·V accumulates in-lane and only
 // the lanes sharing a column are summed at the end.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
+__global__ __launch_bounds__(64) void valu_attn_kernel(AttnParams p) {
   constexpr int X = Elem<T>::X;
   constexpr int NCH = D / X;   // 16-byte groups per key row
   constexpr int NIK = NCH / 4; // key loads per page
@@ -437,20 +456,32 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
   constexpr int RPI = 64 / LPR;  // value columns per load
   constexpr int NIV = D / RPI;   // value loads per page
   constexpr bool kBf16 = sizeof(T) == 2;
-  __shared__ float lds_p[4][64];
+  __shared__ float lds_p[64];
   __shared__ int skip[kSkip];
+  __shared__ int ticket;
 
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
-  const int wave_id = wave_uniform((int)(blockIdx.x * 4 + wv));
-  const int nwaves = (int)gridDim.x * 4;
   const int total = wave_uniform(p.ctrl[2]);
+  // Items.  In a batch where sequences share pages with a neighbour (branches of one
+  // prompt), workgroup b takes items π(b), π(b) + grid, ..., and the grid is a few times
+  // the resident workgroups, so items start in dispatch order.  π permutes each block of
+  // 32 workgroups so that XCD x (workgroups go to the XCDs in turn) takes items 4x .. 4x + 3
+  // of the block.  The readers of a page (one head and partition in neighbouring sequences,
+  // Hq x partitions items apart: a multiple of 32 for 32 query heads) then run close in
+  // time on one XCD and share its reads through L2.  Otherwise only the resident
+  // workgroups work: b takes item b, then the resident count plus a ticket from one
+  // counter, so every wavefront stays busy to the end whatever the mix of item lengths.
+  // Thread 0 takes the ticket between two barriers (the workgroup is this one wavefront),
+  // so no lane-dependent branch spans the item loop.
+  const bool strided = wave_uniform(p.ctrl[6]) != 0;
+  if (!strided && (int)blockIdx.x >= p.valu_resident) return;
   const SkipTable tab = stage_skip(skip, p.pre_v, p.num_ent);
   const T* __restrict__ kc = (const T*)p.k_cache;
   const T* __restrict__ vc = (const T*)p.v_cache;
   const int64_t page_elems = (int64_t)kBlock * D;
 
-  for (int item = wave_id; item < total; item += nwaves) {
+  const int b = (int)blockIdx.x;
+  for (int item = wave_uniform(strided ? (b & ~31) + 4 * (b & 7) + ((b >> 3) & 3) : b); item < total;) {
     const SeqHit hit = find_seq(skip, tab, p.pre_v, p.num_ent, item);
     const int s = hit.s;
     const int local = item - hit.first;
@@ -540,7 +571,7 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
 #pragma unroll
         for (int k = 0; k < NIV; ++k) acc[k] *= alpha;
 
-        lds_p[wv][lane] = pr;
+        lds_p[lane] = pr;
         wave_lds_sync();
         const bool tail = base + 64 > kv_hi;
 #pragma unroll
@@ -549,7 +580,7 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
             float pk[X];
 #pragma unroll
             for (int e = 0; e < X; e += 4) {
-              const f32x4 v4 = *reinterpret_cast<const f32x4*>(&lds_p[wv][kBlock * j + (lane % LPR) * X + e]);
+              const f32x4 v4 = *reinterpret_cast<const f32x4*>(&lds_p[kBlock * j + (lane % LPR) * X + e]);
               pk[e] = v4[0]; pk[e + 1] = v4[1]; pk[e + 2] = v4[2]; pk[e + 3] = v4[3];
             }
             // keys past the context may hold anything (even NaN): drop them, not just weight 0
@@ -594,6 +625,14 @@ __global__ __launch_bounds__(256) void valu_attn_kernel(AttnParams p) {
       for (int k = 0; k < NIV; ++k) slot[RPI * k + lane / LPR] = acc[k];
       slot[D] = m;
       slot[D + 1] = l;
+    }
+    if (strided) {
+      item += (int)gridDim.x;
+    } else {
+      __syncthreads();  // every lane has read the previous ticket
+      if (threadIdx.x == 0) ticket = atomicAdd(p.ctrl + kValuTicket, 1);
+      __syncthreads();
+      item = p.valu_resident + wave_uniform(ticket);
     }
   }
 }
@@ -1115,7 +1154,6 @@ struct TileShape {
 // than the branch.  An empty volatile asm cannot be executed speculatively.
 __device__ inline void keep_branch() { asm volatile(""); }
 
-constexpr int kHwRegXccId = (3 << 11) | 20;  // s_getreg operand: HW_REG_XCC_ID, bits 3:0
 
 template <int D>
 __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParams p) {
@@ -1547,7 +1585,7 @@ WsLayout ws_layout(int S, int NG, int T, int Hq, int Hkv, int D, int max_ctx, bo
   // a member of a group adds at most one partition: its shared and own keys are split separately
   l.maxparts = max(1, (max_ctx + part - 1) / part) + (NG > 0 ? 1 : 0);
   l.ctrl = 0;
-  l.pre_v = 256;
+  l.pre_v = 512;  // ctrl words 0..63, then the VALU ticket counter on a line of its own
   l.pre_m = l.pre_v + align256((size_t)(E + 1) * 4);
   l.pre_t = l.pre_m + align256((size_t)(E + 1) * 4);
   l.pre_g = l.pre_t + align256((size_t)(E + 1) * 4);
@@ -1588,15 +1626,38 @@ void launch_gqa_decode(const AttnParams& p, int grid, hipStream_t stream) {
   mark(4, 1, stream);
 }
 
+// Workgroups of the VALU worker (one wavefront each) that are resident on the device at once.
 template <typename T, int D>
-void launch_attention(const AttnParams& p, bool may_valu, bool may_mfma, bool may_tile, int grid_v,
+int valu_resident_groups() {
+  static const int n = [] {
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, valu_attn_kernel<T, D>, 64, 0) != hipSuccess || cus <= 0 ||
+        per <= 0)
+      return 4 * kMaxWorkerGroups;
+    return cus * per;
+  }();
+  return n;
+}
+
+template <typename T, int D>
+void launch_attention(const AttnParams& p, bool may_valu, bool may_mfma, bool may_tile, int64_t bound_v,
                       int grid_m, int grid_t, hipStream_t stream) {
   mark(0, 0, stream);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, p);
   mark(0, 1, stream);
   mark(1, 0, stream);
-  if (may_valu)
-    hipLaunchKernelGGL((valu_attn_kernel<T, D>), dim3(grid_v), dim3(256), 0, stream, p);
+  if (may_valu) {
+    // a strided batch (sequences sharing pages) uses all of the grid, a ticket batch its resident part
+    AttnParams pv = p;
+    const int64_t res = valu_resident_groups<T, D>();
+    // a multiple of 32 (the strided order permutes blocks of 32 workgroups)
+    const int64_t grid = std::min<int64_t>(std::max<int64_t>(32, kValuGridPerResident * res / 32 * 32),
+                                           std::max<int64_t>(32, (bound_v + 31) / 32 * 32));
+    pv.valu_resident = (int32_t)std::min<int64_t>(res, grid);
+    hipLaunchKernelGGL((valu_attn_kernel<T, D>), dim3((unsigned)grid), dim3(64), 0, stream, pv);
+  }
   mark(1, 1, stream);
   mark(2, 0, stream);
   if constexpr (sizeof(T) == 2)
@@ -1753,17 +1814,16 @@ pa_status forward_impl(const char* fn, void* out, const void* q, const void* k_c
   const int64_t bound_m = (int64_t)(num_seqs + num_groups) * num_kv_heads * wl.maxparts;
   const int64_t bound_t =
       ((int64_t)total_q_tokens * p.G / kBigRows + num_seqs) * num_kv_heads * wl.maxparts;
-  const int grid_v = (int)std::min<int64_t>(kMaxWorkerGroups, (bound_v + 3) / 4);
   const int grid_m = (int)std::min<int64_t>(kMaxWorkerGroups, (bound_m + 3) / 4);
   const int grid_t = (int)std::min<int64_t>(kMaxTileGroups, bound_t);
 
   (void)hipGetLastError();
   if (is_f32) {
-    if (head_dim == 64) launch_attention<float, 64>(p, may_valu, false, false, grid_v, grid_m, grid_t, s);
-    else launch_attention<float, 128>(p, may_valu, false, false, grid_v, grid_m, grid_t, s);
+    if (head_dim == 64) launch_attention<float, 64>(p, may_valu, false, false, bound_v, grid_m, grid_t, s);
+    else launch_attention<float, 128>(p, may_valu, false, false, bound_v, grid_m, grid_t, s);
   } else {
-    if (head_dim == 64) launch_attention<bf16_t, 64>(p, may_valu, may_mfma, may_tile, grid_v, grid_m, grid_t, s);
-    else launch_attention<bf16_t, 128>(p, may_valu, may_mfma, may_tile, grid_v, grid_m, grid_t, s);
+    if (head_dim == 64) launch_attention<bf16_t, 64>(p, may_valu, may_mfma, may_tile, bound_v, grid_m, grid_t, s);
+    else launch_attention<bf16_t, 128>(p, may_valu, may_mfma, may_tile, bound_v, grid_m, grid_t, s);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(PA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));

@@ -226,3 +226,14 @@ inline float emu_exp2(float x) {
 #define __builtin_amdgcn_exp2f(x) emu_exp2((x))
 #define __builtin_amdgcn_fence(...) ((void)0)
 #define __builtin_amdgcn_wave_barrier() emu::wave_sync()
+// device queries for launch sizing: a small device (the emulator runs workgroups one at a time)
+enum { hipDeviceAttributeMultiprocessorCount = 16 };
+inline hipError_t hipDeviceGetAttribute(int* v, int attr, int) {
+  *v = attr == hipDeviceAttributeMultiprocessorCount ? 4 : 0;
+  return hipSuccess;
+}
+template <typename F>
+inline hipError_t hipOccupancyMaxActiveBlocksPerMultiprocessor(int* n, F, int, size_t) {
+  *n = 2;
+  return hipSuccess;
+}

@@ -68,11 +68,45 @@ def test_workers_have_no_per_lane_branches(tmp_path):
             continue
         body = f.split(".Lfunc_end")[0]
         n = len(re.findall(r"\bs_and_saveexec_b64|\bs_andn2_saveexec_b64|\bs_or_saveexec_b64", body))
-        if "tile_attn" in m.group(1):
-            # the single exception: lane 0 takes the workgroup's next work ticket, between two barriers
+        if "tile_attn" in m.group(1) or "valu_attn" in m.group(1):
+            # the single exception: thread 0 takes the workgroup's next work ticket, between two
+            # barriers; the region holds the atomic and the store of its result to LDS, and the
+            # mask is restored right after it
             assert n <= 1, f"{m.group(1)} has {n} exec-mask regions"
-            assert n == 0 or re.search(r"global_atomic_add", body), "the one region must be the ticket atomic"
+            if n:
+                ops, restored = _ticket_region(body)
+                assert restored, f"{m.group(1)}: the ticket region's join block does not restore the mask first"
+                assert "global_atomic_add" in ops and "ds_write_b32" in ops, f"{m.group(1)}: {ops}"
+                assert all(o.startswith(("s_", "v_mov", "global_atomic_add", "ds_write_b32")) for o in ops), ops
         else:
             assert n == 0, f"{m.group(1)} has {n} exec-mask regions"
         checked += 1
     assert checked >= 8 and bodies is not None
+
+def _ticket_region(body):
+    """The instructions of the one exec-mask region of a worker (wherever the compiler placed its
+    block), and whether the block it joins starts by restoring the saved mask."""
+    lines = [ln.split(";")[0].strip() for ln in body.splitlines()]  # without comments
+    lines = [ln for ln in lines if ln]
+    i = next(k for k, ln in enumerate(lines) if ln.startswith("s_and_saveexec_b64"))
+    saved = re.match(r"s_and_saveexec_b64\s+(s\[\d+:\d+\])", lines[i]).group(1)
+    skip = re.match(r"s_cbranch_execz\s+(\.LBB\S+)", lines[i + 1])
+    assert skip, lines[i + 1]
+    ops, k, join = [], i + 2, None
+    while k < len(lines):
+        ln = lines[k]
+        if ln.endswith(":") and ln.startswith(".LBB"):  # falls through into the next block
+            join = ln[:-1]
+            break
+        op = ln.split()[0]
+        if op == "s_branch":
+            join = ln.split()[1]
+            break
+        if not op.startswith("."):
+            ops.append(op)
+        k += 1
+    if join != skip.group(1):
+        return ops, False
+    j = lines.index(join + ":")
+    first = next(ln for ln in lines[j + 1:] if not ln.startswith("."))
+    return ops, first.replace(" ", "") == f"s_or_b64exec,exec,{saved}"
