@@ -1176,9 +1176,12 @@ __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParam
   const uint32_t qflip = p.scale_log2 < 0.f ? 0x80008000u : 0u;
   const SkipTable tab = stage_skip(skip, p.pre_t, p.num_ent);
   const int xcc = wave_uniform(__builtin_amdgcn_s_getreg(kHwRegXccId) & (kXcds - 1));
-  const int per_q = (total + kXcds - 1) / kXcds;  // items per slice
 
   // Next item: from this XCD's slice, then the following slices in turn; -1 when all are done.
+  // The items are dealt to the slices in chunks of four (slice x holds chunks x, x + 8, ...),
+  // so each slice holds an even share of every sequence's items, in their order (partition-
+  // major, the short last partitions last), and the row tiles of one (KV head, partition),
+  // consecutive items, mostly fall in one chunk and so share an XCD's L2.
   int qi = 0;
   auto next_item = [&]() {
 #pragma clang loop unroll(disable)
@@ -1188,8 +1191,8 @@ __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParam
       if (threadIdx.x == 0) ticket = atomicAdd(p.ctrl + 8 + qq, 1);
       __syncthreads();
       const int t = wave_uniform(ticket);
-      const int first = qq * per_q;
-      if (t < min(per_q, total - first)) return first + t;
+      const int64_t item = (((int64_t)(t >> 2) * kXcds + qq) << 2) + (t & 3);
+      if (item < total) return (int)item;
       ++qi;
     }
     return -1;
@@ -1205,10 +1208,12 @@ __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParam
     const SeqWork w = seq_work(false, p.G, p.Hq, p.Hkv, si.q_len, si.L);
     const int rows_total = si.q_len * p.G;
     const int ntiles = (rows_total + kBigRows - 1) / kBigRows;
-    const int tile = local % ntiles;  // row tiles of one (KV head, partition) are consecutive items
+    // partition-major: row tiles of one (KV head, partition) are consecutive items, then the
+    // KV heads, then the partitions (the short last partition of a sequence comes last)
+    const int tile = local % ntiles;
     const int rest = local / ntiles;
-    const int pidx = rest % w.nparts;
-    const int kvh = rest / w.nparts;
+    const int kvh = rest % p.Hkv;
+    const int pidx = rest / p.Hkv;
     const int first = si.L - si.q_len;  // position of query row 0
     const int tile_last = min(tile * kBigRows + kBigRows - 1, rows_total - 1);
     const int kv_lo = pidx * w.part;
