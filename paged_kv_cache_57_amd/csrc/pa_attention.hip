@@ -1631,18 +1631,24 @@ void launch_gqa_decode(const AttnParams& p, int grid, hipStream_t stream) {
   mark(4, 1, stream);
 }
 
-// Workgroups of the VALU worker (one wavefront each) that are resident on the device at once.
+// Workgroups of the VALU worker (one wavefront each) that are resident on the current
+// device at once, from the occupancy API (cached per device).
 template <typename T, int D>
 int valu_resident_groups() {
-  static const int n = [] {
-    int dev = 0, cus = 0, per = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, valu_attn_kernel<T, D>, 64, 0) != hipSuccess || cus <= 0 ||
-        per <= 0)
-      return 4 * kMaxWorkerGroups;
-    return cus * per;
-  }();
+  constexpr int kDevices = 64;
+  static std::atomic<int> cached[kDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+  if (dev >= 0 && dev < kDevices) {
+    const int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+  }
+  int cus = 0, per = 0, n = 4 * kMaxWorkerGroups;
+  if (dev >= 0 && hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, valu_attn_kernel<T, D>, 64, 0) == hipSuccess && cus > 0 &&
+      per > 0)
+    n = cus * per;
+  if (dev >= 0 && dev < kDevices) cached[dev].store(n, std::memory_order_relaxed);
   return n;
 }
 
