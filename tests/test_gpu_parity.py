@@ -383,6 +383,31 @@ def test_batch_invariance(pa):
         assert torch.equal(one.view(torch.int16), full[s:s + 1].view(torch.int16)), s
 
 
+def test_item_order_does_not_change_results(pa):
+    # A batch in which neighbouring sequences share pages walks the VALU items in a fixed
+    # strided order with plain page loads; a batch without takes them by ticket with
+    # non-temporal loads.  A sequence's output is bit-identical either way.
+    w = W.random_ragged(14, "bf16", 32, 32, 128, [1, 1, 1, 1], [2049, 3000, 3000, 700])
+    w.block_tables[2, :] = w.block_tables[1, :]  # sequences 1 and 2 read the same pages
+    say("[case] VALU item order: strided (shared pages) vs tickets (alone)")
+    check_tables_in_pool(w)
+    q, kc, vc, _, _ = W.make_values(w, DEV)
+    r = Run(w)
+    full = r.forward(q, kc, vc).clone()
+    r.check_status()
+    rows, ref = oracle_rows_all(w, q, kc, vc)
+    assert_close(to_f64(full.index_select(0, torch.from_numpy(rows).to(DEV))), ref, "bf16", "strided VALU order")
+    for s in range(w.num_seqs):
+        ws = W.Workload(**{**w.__dict__})
+        ws.context_lens = w.context_lens[s:s + 1].copy()
+        ws.block_tables = w.block_tables[s:s + 1].copy()
+        ws.query_start_loc = np.array([0, 1], np.int32)
+        rs = Run(ws)
+        one = rs.forward(q[s:s + 1].contiguous(), kc, vc)
+        rs.check_status()
+        assert torch.equal(one.view(torch.int16), full[s:s + 1].view(torch.int16)), s
+
+
 def test_batch_invariance_gqa_decode(pa):
     # decode-only GQA batches take the one-pass kernel: a sequence's output is bit-identical
     # alone and inside a bigger batch (partition lengths follow the sequence's own length)
