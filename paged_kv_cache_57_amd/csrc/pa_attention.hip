@@ -14,11 +14,13 @@
 //      - a tile of 16 query rows that share one KV head (MFMA class: bfloat16
 //        sequences with at most 16 rows, where a row is one query position
 //        of one of the G query heads of a KV head, e.g. GQA decodes), or
-//      - a tile of 128 such rows (TILE class: bfloat16 prefill chunks).
+//      - a tile of 256 such rows (TILE class: bfloat16 prefill chunks).
 //    Partition sizes depend only on the sequence's own lengths, so a
 //    sequence's result does not depend on the rest of the batch.
-//  * Persistent workers walk the items with a fixed stride (wave w takes
-//    items w, w + W, w + 2W, ...).  Each item streams its pages with 16-byte loads and keeps the running max m, the
+//  * Persistent workers walk the items, with a fixed stride (wave w takes
+//    items w, w + W, w + 2W, ...) or from ticket counters (the TILE worker, and
+//    the VALU worker in batches without shared pages).  Each item streams its
+//    pages with 16-byte loads and keeps the running max m, the
 //    running sum l and the unnormalised output O of the tiled online softmax
 //    ("第 15 章" §15.1 "算法详解": m_new = max(m, rowmax S), α = exp(m − m_new),
 //    P = exp(S − m_new), l = αl + rowsum P, O = diag(α)O + PV), in base 2
