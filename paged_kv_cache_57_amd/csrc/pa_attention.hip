@@ -476,13 +476,14 @@ __global__ __launch_bounds__(64) void valu_attn_kernel(AttnParams p) {
   // Thread 0 takes the ticket between two barriers (the workgroup is this one wavefront),
   // so no lane-dependent branch spans the item loop.
   const bool strided = wave_uniform(p.ctrl[6]) != 0;
-  if (!strided && (int)blockIdx.x >= p.valu_resident) return;
+  const int b = (int)blockIdx.x;
+  // no first item (its block of 32 starts past the end) or, with tickets, not resident: no work
+  if ((b & ~31) >= total || (!strided && b >= p.valu_resident)) return;
   const SkipTable tab = stage_skip(skip, p.pre_v, p.num_ent);
   const T* __restrict__ kc = (const T*)p.k_cache;
   const T* __restrict__ vc = (const T*)p.v_cache;
   const int64_t page_elems = (int64_t)kBlock * D;
 
-  const int b = (int)blockIdx.x;
   for (int item = wave_uniform(strided ? (b & ~31) + 4 * (b & 7) + ((b >> 3) & 3) : b); item < total;) {
     const SeqHit hit = find_seq(skip, tab, p.pre_v, p.num_ent, item);
     const int s = hit.s;
@@ -841,6 +842,7 @@ __global__ __launch_bounds__(256, 2) void mfma_attn_kernel(AttnParams p) {
   const int wave_id = wave_uniform((int)(blockIdx.x * 4 + (threadIdx.x >> 6)));
   const int nwaves = (int)gridDim.x * 4;
   const int total = wave_uniform(p.ctrl[3]);
+  if ((int)blockIdx.x * 4 >= total) return;  // no wavefront of this workgroup has an item
   __shared__ int skip[kSkip];
   const SkipTable tab = stage_skip(skip, p.pre_m, p.num_ent);
 
