@@ -22,9 +22,10 @@ inputs resident in device memory before timing starts:
 * splitfuse_rope: the same pass with the rotary embedding fused into the cache
   write (pa_rope_reshape_and_cache rotates q and the new keys at their
   positions; the forward reads the rotated q).
-* copy / read: calibration lines, not the path — a 4 GiB device copy, and
-  every 4 KiB page of a 4 GiB pool read once in random order (the measurement
-  library's pa_probe_read_pages),
+* copy / read / lds: calibration lines, not the path — a 4 GiB device copy,
+  every 4 KiB page of a pool (4 GiB, or --read-gib) read once in random order
+  (the measurement library's pa_probe_read_pages), and 16-byte LDS reads on
+  every compute unit (pa_probe_lds_read),
   the attainable HBM rates the kernels' fractions are set against.
 
 The roofline object describes the dominant kernel, timed with HIP events
@@ -287,6 +288,8 @@ class ProbeLib:
         vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
         self.lib.pa_probe_read_pages.restype = i32
         self.lib.pa_probe_read_pages.argtypes = [vp, i64, vp, i32, vp, i32, i32, i32, vp, vp]
+        self.lib.pa_probe_lds_read.restype = i32
+        self.lib.pa_probe_lds_read.argtypes = [vp, i32, i32, i32, vp]
         self.lib.pa_probe_last_error.restype = ctypes.c_char_p
 
     def read_pages(self, torch, pool, page_ids, sink, grid, pages_in_flight, mode, status):
@@ -297,10 +300,47 @@ class ProbeLib:
             raise RuntimeError(self.lib.pa_probe_last_error().decode())
 
 
+    def lds_read(self, torch, sink, grid, waves, iters):
+        st = self.lib.pa_probe_lds_read(sink.data_ptr(), grid, waves, iters, torch.cuda.current_stream().cuda_stream)
+        if st != 0:
+            raise RuntimeError(self.lib.pa_probe_last_error().decode())
+
+
 READ_MODES = {0: "plain", 1: "nontemporal", 2: "into_lds"}
+READ_MODES.update({3 + a: f"buffer_cpol_{c}" for a, c in enumerate((0, 1, 2, 3, 16, 17, 18, 19))})
 
 
-def read_calibration(torch, pa, dev, args, nbytes=4 << 30):
+def lds_calibration(torch, dev, args):
+    """LDS read rate: --lds-waves wavefronts per workgroup (4, 8, 16) on one workgroup
+    per CU read 16-byte pieces of a 64 KiB LDS array; bytes read / kernel time."""
+    probe = ProbeLib()
+    props = torch.cuda.get_device_properties(dev)
+    grid, waves, iters = props.multi_processor_count, args.lds_waves, 4096
+    sink = torch.empty(grid * 64 * waves, dtype=torch.int32, device=dev)
+    for _ in range(args.warmup):
+        probe.lds_read(torch, sink, grid, waves, iters)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(args.steps):
+        t0.record()
+        probe.lds_read(torch, sink, grid, waves, iters)
+        t1.record()
+        t1.synchronize()
+        times.append(t0.elapsed_time(t1))
+    ms = float(np.median(times))
+    nbytes = grid * waves * iters * 8 * 1024
+    tbps = nbytes / (ms * 1e-3) / 1e12
+    print(json.dumps({"metric": "LDS read TB/s (16-byte reads, whole GPU)", "value": round(tbps, 2), "unit": "TB/s",
+                      "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
+                      "data": "synthetic", "config": {"workload": f"lds_read_{waves}waves", "workgroups": grid,
+                                                      "waves_per_workgroup": waves, "bytes": nbytes},
+                      "per_cu_GBps": round(tbps * 1e3 / grid, 1)}), flush=True)
+
+
+def read_calibration(torch, pa, dev, args):
     """4 KiB pages of a 4 GiB pool read in a seeded random order with 16-byte loads,
     --read-pif pages per wavefront in flight (default 2, the decode workers' depth),
     --read-mode loads (0 plain, 1 non-temporal, 2 into LDS): the rate the decode
@@ -313,6 +353,7 @@ def read_calibration(torch, pa, dev, args, nbytes=4 << 30):
     same time.  --read-grid sets the workgroups (0: one wavefront per
     pages-in-flight run of the slice, at most 2048 workgroups)."""
     probe = ProbeLib()
+    nbytes = args.read_gib << 30
     pool = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(7)
     npages = nbytes // 4096
     run = args.read_chunk_pages
@@ -347,7 +388,7 @@ def read_calibration(torch, pa, dev, args, nbytes=4 << 30):
         raise RuntimeError(f"pa_probe_read_pages flagged status {int(status.item())}")
     ms = float(np.median(times))
     gbps = per * 4096 / (ms * 1e-3) / 1e9
-    name = "read_pages_4GiB" if per == npages else f"read_pages_{per * 4096 >> 20}MiB_of_4GiB"
+    name = f"read_pages_{args.read_gib}GiB" if per == npages else f"read_pages_{per * 4096 >> 20}MiB_of_{args.read_gib}GiB"
     if run != 1:
         name += "_in_address_order" if run == 0 else f"_runs_of_{run}"
     print(json.dumps({"metric": "random 4 KiB page reads GB/s", "value": round(gbps, 1), "unit": "GB/s",
@@ -593,14 +634,18 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="splitfuse",
-                    choices=["splitfuse", "splitfuse_rope", "llama7b", "gqa70b", "gqa70b_long", "tiny", "copy", "read",
+                    choices=["splitfuse", "splitfuse_rope", "llama7b", "gqa70b", "gqa70b_long", "tiny", "copy", "read", "lds",
                              "sampling"])
     ap.add_argument("--rotate", type=int, default=0, help="pool copies cycled per step (0: enough to exceed the 256 MB MALL)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="time budget of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--read-mib", type=int, default=0, help="read workload: MiB per step (0: the whole 4 GiB pool)")
     ap.add_argument("--read-pif", type=int, default=2, help="read workload: pages per wavefront in flight (1, 2, 4, 8)")
-    ap.add_argument("--read-mode", type=int, default=0, help="read workload: 0 plain, 1 non-temporal, 2 into-LDS loads")
+    ap.add_argument("--read-mode", type=int, default=0,
+                    help="read workload: 0 plain, 1 non-temporal, 2 into-LDS loads, 3..10 buffer loads with the "
+                         "cache-policy bits 0, 1, 2, 3, 16, 17, 18, 19")
+    ap.add_argument("--read-gib", type=int, default=4, help="read workload: pool size in GiB")
+    ap.add_argument("--lds-waves", type=int, default=8, help="lds workload: wavefronts per workgroup (4, 8, 16)")
     ap.add_argument("--read-grid", type=int, default=0, help="read workload: workgroups (0: by the slice size)")
     ap.add_argument("--read-chunk-pages", type=int, default=1,
                     help="read workload: pages per run of consecutive pages in the random order (0: address order)")
@@ -624,6 +669,8 @@ def main():
         return copy_calibration(torch, dev, args)
     if args.workload == "read":
         return read_calibration(torch, pa, dev, args)
+    if args.workload == "lds":
+        return lds_calibration(torch, dev, args)
     if args.workload == "sampling":
         if args.warmup + args.steps > 256:
             print("the sampling workflow runs at most 256 decode steps (warmup + steps)", file=sys.stderr)

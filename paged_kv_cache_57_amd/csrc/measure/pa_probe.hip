@@ -29,7 +29,12 @@ pa_status probe_fail(pa_status st, const char* msg) {
 // l, l+64, l+128, l+192 of every page it reads into one word.  Ids outside the pool
 // read page 0 and set bit 1 of the status word.
 // MODE 0: plain loads; 1: non-temporal loads (streamed past the caches);
-// 2: loads straight into LDS (global_load_lds_dwordx4), read back after a wait.
+// 2: loads straight into LDS (global_load_lds_dwordx4), read back after a wait;
+// kBufferMode + a (a = 0..7): buffer loads through a 4 KiB resource per page with the
+// cache-policy bits kCpol[a] (bit 0 SC0, bit 1 NT, bit 4 SC1).
+constexpr int kBufferMode = 3;
+constexpr int kCpol[8] = {0, 1, 2, 3, 16, 17, 18, 19};
+
 template <int PIF, int MODE>
 __global__ __launch_bounds__(256) void read_pages_kernel(const u32x4* __restrict__ pool, int64_t pool_pages,
                                                          const int32_t* __restrict__ page_ids, int32_t n,
@@ -55,6 +60,11 @@ __global__ __launch_bounds__(256) void read_pages_kernel(const u32x4* __restrict
         const u32x4* src = pool + page * 256 + k * 64 + lane;
         if constexpr (MODE == 0) {
           v[j][k] = *src;
+        } else if constexpr (MODE >= kBufferMode) {
+          // a resource of exactly this page: every offset below is inside it
+          const __amdgpu_buffer_rsrc_t rs =
+              __builtin_amdgcn_make_buffer_rsrc((void*)(pool + page * 256), 0, 4096, 0x00020000);
+          v[j][k] = __builtin_amdgcn_raw_buffer_load_b128(rs, (k * 64 + lane) * 16, 0, kCpol[MODE - kBufferMode]);
         } else if constexpr (MODE == 1) {
           v[j][k] = __builtin_nontemporal_load(src);
         } else {
@@ -79,12 +89,45 @@ __global__ __launch_bounds__(256) void read_pages_kernel(const u32x4* __restrict
   sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
+template <int PIF, int MODE>
+void launch_mode(dim3 g, hipStream_t s, const u32x4* pool, int64_t pages, const int32_t* ids, int32_t n,
+                 uint32_t* sink, int32_t* st) {
+  hipLaunchKernelGGL((read_pages_kernel<PIF, MODE>), g, dim3(256), 0, s, pool, pages, ids, n, sink, st);
+}
+
 template <int PIF>
 void launch(int mode, dim3 g, hipStream_t s, const u32x4* pool, int64_t pages, const int32_t* ids, int32_t n,
             uint32_t* sink, int32_t* st) {
-  if (mode == 0) hipLaunchKernelGGL((read_pages_kernel<PIF, 0>), g, dim3(256), 0, s, pool, pages, ids, n, sink, st);
-  else if (mode == 1) hipLaunchKernelGGL((read_pages_kernel<PIF, 1>), g, dim3(256), 0, s, pool, pages, ids, n, sink, st);
-  else hipLaunchKernelGGL((read_pages_kernel<PIF, 2>), g, dim3(256), 0, s, pool, pages, ids, n, sink, st);
+  switch (mode) {
+    case 0: launch_mode<PIF, 0>(g, s, pool, pages, ids, n, sink, st); break;
+    case 1: launch_mode<PIF, 1>(g, s, pool, pages, ids, n, sink, st); break;
+    case 2: launch_mode<PIF, 2>(g, s, pool, pages, ids, n, sink, st); break;
+    case kBufferMode + 0: launch_mode<PIF, kBufferMode + 0>(g, s, pool, pages, ids, n, sink, st); break;
+    case kBufferMode + 1: launch_mode<PIF, kBufferMode + 1>(g, s, pool, pages, ids, n, sink, st); break;
+    case kBufferMode + 2: launch_mode<PIF, kBufferMode + 2>(g, s, pool, pages, ids, n, sink, st); break;
+    case kBufferMode + 3: launch_mode<PIF, kBufferMode + 3>(g, s, pool, pages, ids, n, sink, st); break;
+    case kBufferMode + 4: launch_mode<PIF, kBufferMode + 4>(g, s, pool, pages, ids, n, sink, st); break;
+    case kBufferMode + 5: launch_mode<PIF, kBufferMode + 5>(g, s, pool, pages, ids, n, sink, st); break;
+    case kBufferMode + 6: launch_mode<PIF, kBufferMode + 6>(g, s, pool, pages, ids, n, sink, st); break;
+    default: launch_mode<PIF, kBufferMode + 7>(g, s, pool, pages, ids, n, sink, st); break;
+  }
+}
+
+// LDS read rate: WAVES wavefronts per workgroup each read iters x 8 pieces of 16 bytes of a
+// 64 KiB LDS array (lane-consecutive addresses, masked into the array), XORed into one word
+// per thread written to sink[blockIdx.x * 64 * WAVES + threadIdx.x].
+template <int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void lds_read_kernel(uint32_t* __restrict__ sink, int32_t iters) {
+  __shared__ u32x4 buf[4096];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int i = tid; i < 4096; i += 64 * WAVES) buf[i] = u32x4{(uint32_t)i, (uint32_t)i * 3u, (uint32_t)i ^ 5u, 7u};
+  __syncthreads();
+  u32x4 acc = {0, 0, 0, 0};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc ^= buf[((it * 8 + k) * 64 + wv * 512 + lane) & 4095];
+  }
+  sink[(int64_t)blockIdx.x * 64 * WAVES + tid] = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
 }
 
 void launch8(int mode, dim3 g, hipStream_t s, const u32x4* pool, int64_t pages, const int32_t* ids, int32_t n,
@@ -102,11 +145,14 @@ extern "C" pa_status pa_probe_read_pages(const void* pool, int64_t pool_bytes, c
                                          int32_t mode, int32_t* dev_status, void* stream) {
   if (num_pages < 0 || grid <= 0 || pool_bytes < 4096 || pool_bytes % 4096)
     return probe_fail(PA_ERR_INVALID, "pa_probe_read_pages: bad sizes");
-  if (mode < 0 || mode > 2) return probe_fail(PA_ERR_INVALID, "pa_probe_read_pages: mode must be 0, 1 or 2");
+  if (mode < 0 || mode > kBufferMode + 7)
+    return probe_fail(PA_ERR_INVALID, "pa_probe_read_pages: mode must be 0 .. 10");
   if (pages_in_flight != 1 && pages_in_flight != 2 && pages_in_flight != 4 && pages_in_flight != 8)
     return probe_fail(PA_ERR_INVALID, "pa_probe_read_pages: pages_in_flight must be 1, 2, 4 or 8");
   if (mode == 2 && pages_in_flight > 4)
     return probe_fail(PA_ERR_UNSUPPORTED, "pa_probe_read_pages: loads into LDS hold at most 4 pages per wavefront");
+  if (mode >= kBufferMode && pages_in_flight != 4)
+    return probe_fail(PA_ERR_UNSUPPORTED, "pa_probe_read_pages: buffer loads run with 4 pages in flight");
   if (num_pages == 0) return PA_OK;
   if (!pool || !page_ids || !sink) return probe_fail(PA_ERR_INVALID, "pa_probe_read_pages: NULL device pointer");
   (void)hipGetLastError();
@@ -121,5 +167,20 @@ extern "C" pa_status pa_probe_read_pages(const void* pool, int64_t pool_bytes, c
     default: launch8(mode, g, s, p, pages, page_ids, num_pages, sink, dev_status); break;
   }
   if (hipGetLastError() != hipSuccess) return probe_fail(PA_ERR_HIP, "pa_probe_read_pages: launch failed");
+  return PA_OK;
+}
+
+extern "C" pa_status pa_probe_lds_read(uint32_t* sink, int32_t grid, int32_t waves_per_group, int32_t iters,
+                                       void* stream) {
+  if (grid <= 0 || iters <= 0 || !sink) return probe_fail(PA_ERR_INVALID, "pa_probe_lds_read: bad arguments");
+  (void)hipGetLastError();
+  hipStream_t s = (hipStream_t)stream;
+  switch (waves_per_group) {
+    case 4: hipLaunchKernelGGL(lds_read_kernel<4>, dim3(grid), dim3(256), 0, s, sink, iters); break;
+    case 8: hipLaunchKernelGGL(lds_read_kernel<8>, dim3(grid), dim3(512), 0, s, sink, iters); break;
+    case 16: hipLaunchKernelGGL(lds_read_kernel<16>, dim3(grid), dim3(1024), 0, s, sink, iters); break;
+    default: return probe_fail(PA_ERR_INVALID, "pa_probe_lds_read: waves_per_group must be 4, 8 or 16");
+  }
+  if (hipGetLastError() != hipSuccess) return probe_fail(PA_ERR_HIP, "pa_probe_lds_read: launch failed");
   return PA_OK;
 }

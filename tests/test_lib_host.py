@@ -33,15 +33,15 @@ def declared_functions():
 
 
 def test_probe_library_exports_its_header(pa):
-    # the measurement-only page-read probe lives in libpa_probe.so, not in the product library
+    # the measurement-only probes (page reads, LDS reads) live in libpa_probe.so, not in the product library
     from paged_kv_cache_57_amd import build as _b
     hdr = open(os.path.join(ROOT, "include", "pa_probe.h")).read()
     names = set(re.findall(r"\b(pa_probe_\w+)\(", hdr))
-    assert names == {"pa_probe_read_pages", "pa_probe_last_error"}
+    assert names == {"pa_probe_read_pages", "pa_probe_lds_read", "pa_probe_last_error"}
     nm = subprocess.run(["nm", "-D", "--defined-only", _b.PROBE_LIB], capture_output=True, text=True).stdout
     assert names <= set(re.findall(r"\bT (pa_probe_\w+)", nm))
     main = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True, text=True).stdout
-    assert "read_pages" not in main
+    assert "read_pages" not in main and "lds_read" not in main
 
 
 def test_library_exports_every_declared_function(pa):
