@@ -785,7 +785,7 @@ def read_probe_case(pif):
     return words, ids, grid, want
 
 
-@pytest.mark.parametrize("pif,mode", [(2, 0), (1, 0), (4, 1), (8, 0), (4, 2)])
+@pytest.mark.parametrize("pif,mode", [(2, 0), (1, 0), (4, 1), (8, 0), (4, 2), (4, 3), (4, 10)])
 def test_read_pages_probe(pif, mode):
     """The measurement library's page reader visits each listed page once, in the documented
     assignment, for every depth and kind of load."""
@@ -808,6 +808,32 @@ def test_read_pages_probe(pif, mode):
     torch.cuda.synchronize()
     assert int(status.item()) == 1
     assert np.array_equal(sink.cpu().numpy().view(np.uint32), want)
+
+
+@pytest.mark.parametrize("waves", [4, 16])
+def test_lds_read_probe(waves):
+    """The LDS read probe folds exactly the documented pieces: thread t of workgroup b reads
+    entries (((i * 8 + k) * 64 + 512 w + l) mod 4096) of the array {e, 3e, e ^ 5, 7}."""
+    import ctypes
+    from paged_kv_cache_57_amd import build as _b
+    lib = ctypes.CDLL(_b.PROBE_LIB)
+    lib.pa_probe_lds_read.restype = ctypes.c_int32
+    lib.pa_probe_lds_read.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+    grid, iters = 3, 5
+    say(f"[case] LDS read probe: {waves} wavefronts per workgroup")
+    sink = torch.full((grid * 64 * waves,), -1, dtype=torch.int32, device=DEV)
+    assert lib.pa_probe_lds_read(sink.data_ptr(), grid, waves, iters, torch.cuda.current_stream().cuda_stream) == 0
+    torch.cuda.synchronize()
+    t = np.arange(64 * waves)
+    wv, lane = t // 64, t % 64
+    want = np.zeros(64 * waves, dtype=np.uint32)
+    for i in range(iters):
+        for k in range(8):
+            e = (((i * 8 + k) * 64 + wv * 512 + lane) & 4095).astype(np.uint32)
+            want ^= e ^ (e * np.uint32(3)) ^ (e ^ np.uint32(5)) ^ np.uint32(7)
+    got = sink.cpu().numpy().view(np.uint32).reshape(grid, -1)
+    assert all(np.array_equal(got[b], want) for b in range(grid))
+    assert lib.pa_probe_lds_read(sink.data_ptr(), grid, 5, iters, None) != 0  # only 4, 8 or 16 wavefronts
 
 
 @pytest.mark.parametrize("shared", [False, True])
