@@ -805,7 +805,7 @@ def main():
     if dom != "tile_worker":
         # the attainable rate for a pure page-read loop over passes of the same size
         probe_gbps, probe_bytes = probe_ceiling(torch, dev, work[dom]["bytes"])
-        long_gbps, long_bytes = (probe_gbps, probe_bytes) if probe_bytes >= 4 << 30 else \
+        long_gbps, _ = (probe_gbps, probe_bytes) if probe_bytes >= 4 << 30 else \
             probe_ceiling(torch, dev, 4 << 30)
         result["roofline"]["read_probe"] = {
             "GBps": round(probe_gbps, 1), "pass_bytes": probe_bytes,
