@@ -6,7 +6,6 @@ points on exact-size heap buffers.  Any out-of-bounds access in a kernel
 aborts with the source line, on the CPU.
 """
 import os
-import shutil
 import subprocess
 import tempfile
 

@@ -2,7 +2,6 @@
 (caller workspace) through the C ABI: two calls in a row, the second on a smaller batch,
 each equal to pa_forward bit for bit and to the fp64 oracle within tolerance; a batch
 whose workspace exceeds the static array is refused on the host."""
-import numpy as np
 import pytest
 import torch
 
