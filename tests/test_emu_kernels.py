@@ -14,7 +14,8 @@ from oracle import attention as oattn
 from oracle import cache_ops, layout
 from tests import _emu
 from tests._pools import empty_pools, raw
-from tests.test_gpu_parity import RAGGED, REJECTED, SHARED_CASES, many_sequences_batch, shared_prefix_batch
+from tests.test_gpu_parity import (DEGENERATE, RAGGED, REJECTED, SHARED_CASES, many_sequences_batch,
+                                   shared_prefix_batch)
 
 pytestmark = pytest.mark.skipif(not _emu.available(), reason="needs the ROCm clang++ for the host build")
 TOL = {"bf16": (2e-3, 1e-2), "f32": (1e-5, 1e-5)}
@@ -45,6 +46,18 @@ def test_ragged_cases_match_oracle(emu, i):
     out, st = emu.forward(w, q, kp, vp)
     assert st == 0
     check(w, q, kp, vp, out, f"ragged[{i}]")
+
+
+@pytest.mark.parametrize("i", range(len(DEGENERATE)))
+def test_idle_slots_and_block_aligned_lengths(emu, i):
+    dt, hq, hkv, d, ql, cl = DEGENERATE[i]
+    w = W.random_ragged(300 + i, dt, hq, hkv, d, ql, cl)
+    rng = np.random.default_rng(300 + i)
+    kp, vp = empty_pools(rng, dt, w.num_blocks, hkv, d)
+    q = raw(rng.standard_normal((w.num_tokens, hq, d)).astype(np.float32), dt)
+    out, st = emu.forward(w, q, kp, vp)
+    assert st == 0
+    check(w, q, kp, vp, out, f"degenerate[{i}]")
 
 
 @pytest.mark.parametrize("scale", [-0.0625, 0.0, 0.75])

@@ -175,6 +175,48 @@ def test_ragged_batches(pa, i):
     run_and_check(pa, w, label=f"ragged[{i}] {dt} Hq={hq} Hkv={hkv} d={d} q={ql} L={cl}")
 
 
+DEGENERATE = [
+    # dtype, Hq, Hkv, d, q_lens, ctx_lens
+    ("bf16", 16, 2, 64, [0, 1, 0, 5, 0, 1], [0, 300, 17, 40, 0, 1]),    # idle slots (no keys, no rows) among live ones
+    ("f32", 4, 4, 128, [0, 2, 0], [0, 1500, 0]),                        # float32, one live sequence between idle slots
+    ("bf16", 4, 4, 64, [0, 32, 16, 0], [0, 32, 1024, 2048]),            # whole prompt from position 0, block-aligned lengths
+]
+
+
+@pytest.mark.parametrize("i", range(len(DEGENERATE)))
+def test_idle_slots_and_block_aligned_lengths(pa, i):
+    # sequences with no query rows (with or without keys) must neither be read nor written;
+    # unreferenced pages hold NaN so a stray read shows up in the live rows
+    dt, hq, hkv, d, ql, cl = DEGENERATE[i]
+    w = W.random_ragged(300 + i, dt, hq, hkv, d, ql, cl)
+    run_and_check(pa, w, poison=True, label=f"degenerate[{i}] {dt} q={ql} L={cl}")
+
+
+def test_batches_without_query_rows(pa):
+    # no rows (every sequence idle) and no sequences at all: the call succeeds, launches
+    # nothing and leaves the status word alone
+    w = W.random_ragged(310, "bf16", 8, 8, 128, [0, 0, 0], [0, 64, 0])
+    r = Run(w)
+    q, kc, vc, _, _ = W.make_values(w, DEV)
+    assert q.shape[0] == 0
+    out = r.forward(q, kc, vc)
+    r.check_status()
+    assert out.shape == (0, 8, 128)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    st = torch.full((1,), 0, **i32)
+    empty_q = torch.empty((0, 8, 128), dtype=torch.bfloat16, device=DEV)
+    pa.pa_forward(torch.empty_like(empty_q), empty_q, kc, vc, torch.empty((0, 1), **i32), torch.empty(0, **i32),
+                  torch.zeros(1, **i32), 0, 0, w.scale, r.workspace, st)
+    pa.pa_reshape_and_cache(torch.empty((0, 8, 128), dtype=torch.bfloat16, device=DEV),
+                            torch.empty((0, 8, 128), dtype=torch.bfloat16, device=DEV), kc, vc,
+                            torch.empty(0, dtype=torch.int64, device=DEV), st)
+    before = host_raw(kc).copy()
+    pa.pa_copy_blocks(kc, vc, torch.empty((0, 2), **i32), st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert np.array_equal(host_raw(kc), before)
+
+
 def many_sequences_batch(n=5000, n_split=12, split_hi=1500, heads=2):
     """n sequences (more than the 2,047 the workers' LDS lookup table holds one by one):
     MHA decodes, some split into partitions, plus short prefill rows and empty-query sequences."""
