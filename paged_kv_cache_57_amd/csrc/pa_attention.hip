@@ -58,8 +58,7 @@ constexpr int kXcds = 8;                // XCDs (each with its own L2); TILE ite
 constexpr int kHwRegXccId = (3 << 11) | 20;  // s_getreg operand: HW_REG_XCC_ID, bits 3:0
 constexpr int kValuGridPerResident = 4;  // VALU grid: this many times the resident workgroups
 constexpr int kValuTicket = 64;         // ctrl word of the VALU ticket counter (bytes 256..259 of the workspace)
-constexpr float kLazyRescale = 8.f;     // MFMA worker: raise the exponent reference only past this growth (log2)
-constexpr float kTileLazyRescale = 7.f; // TILE worker: the same, bounded so that 2^8 p stays below the half maximum
+constexpr float kLazyRescale = 8.f;     // MFMA and TILE workers: raise the exponent reference only past this growth (log2)
 constexpr int kMergeSplitParts = 32;    // partitions per row from which four wavefronts merge a row
 constexpr float kNegInf = -INFINITY;
 
@@ -1122,19 +1121,26 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void gqa_decode_kernel(AttnParam
 // an item share every key and value piece it reads from HBM (or L2).
 // Softmax ("第 15 章" §15.1 recurrence): scores stay unscaled until the
 // exponent (p = 2^(s·c − m) with c = |scale|·log2 e, one FMA; a negative scale
-// flips the sign bits of q instead, which is exact), and a row's reference m
-// is raised only when its maximum grows past it by more than
-// kTileLazyRescale (O and l share the reference, so O / l is unchanged).
-// P·V precision: the weights enter the half-precision MFMA as 2^8 p rounded
-// to half (relative error 2^-11; 2^8 p < 2^15 by the lazy-rescale bound) and
-// the values as half, converted once per workgroup when they are stored to
-// LDS (exact for bfloat16 values of magnitude below 2^16 down to 2^-17); the
-// row sum adds exactly the rounded weights (v_dot2_f32_f16), and 2^8 scales O
-// and l alike.  A bfloat16 value of magnitude 2^16 or more would overflow
-// half: the converting lanes check every value they stage, and an item that
-// met one is computed again with the values left in bfloat16 and the weights
-// split into a bfloat16 high and low part (two MFMAs, weights exact to about
-// 2^-16), which holds for every finite input.
+// flips the sign bits of q instead, which is exact).  A row's reference m is
+// its maximum over the item's first step (every row that sees a key of the
+// item sees its first key; O and l share the reference, so O / l does not
+// depend on it), and the other steps compute their weights against it with
+// no row maximum.
+// P·V precision: the weights enter the half-precision MFMA as p rounded to
+// half (relative error 2^-11; weights more than 2^14 below the first step's
+// maximum become subnormal, an absolute error of at most 2^-25 against a
+// weight of 1), the values as half, converted once per workgroup when they
+// are stored to LDS (exact for bfloat16 values of magnitude below 2^16 down
+// to 2^-17); the row sum adds exactly the rounded weights (v_dot2_f32_f16).
+// A weight of 65520 or more (a row maximum that grew by 16 or more in log2
+// after the first step) or a bfloat16 value of magnitude 65520 or more
+// becomes an infinite half, and the output of every row that uses it becomes
+// infinite or NaN (0 x inf); the wavefronts check their outputs once after
+// the last step, and an item with a non-finite one is computed again with
+// the values left in bfloat16, the row maximum on every step (the reference
+// raised when it grew by more than kLazyRescale), and the weights split into
+// a bfloat16 high and low part (two MFMAs, weights exact to about 2^-16),
+// which holds for every finite input.
 // Work distribution: items are numbered so that the row tiles of one (KV
 // head, partition) are consecutive; the item list is cut into eight equal
 // slices, one per XCD (each XCD has its own L2), and the workgroups of an XCD
@@ -1282,7 +1288,9 @@ __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParam
       constexpr bool kExact = decltype(exact_tag)::value;
       bool out_of_range = false;
       // Stage step st: keys as loaded; values zeroed past kv_hi (the pool there may hold
-      // anything), then converted to half unless kExact, with their magnitudes checked.
+      // anything), then converted to half unless kExact (a magnitude of 65520 or more
+      // becomes an infinite half, which makes the output of every row that uses it
+      // non-finite: checked once per item, after the last step).
       auto put = [&](u32x4 (&reg)[BPW], int st) {
         u32x4* img = stage[st % kTileStages];
 #pragma unroll
@@ -1297,14 +1305,8 @@ __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParam
                 v[e] &= (kfirst + 2 * e < kv_hi ? 0x0000ffffu : 0u) | (kfirst + 2 * e + 1 < kv_hi ? 0xffff0000u : 0u);
             }
             if constexpr (!kExact) {
-              float mx = 0.f;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float lo = bf16_lo(v[e]), hi = bf16_hi(v[e]);
-                mx = fmaxf(mx, fmaxf(fabsf(lo), fabsf(hi)));
-                v[e] = pack_f16x2(lo, hi);
-              }
-              out_of_range |= !(mx < 65536.f);
+              for (int e = 0; e < 4; ++e) v[e] = pack_f16x2(bf16_lo(v[e]), bf16_hi(v[e]));
             }
           }
           img[b * 64 + lane] = v;
@@ -1312,6 +1314,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParam
       };
 
       float m_used = kNegInf, lsum = 0.f;
+      float nmu = 0.f;  // exponent offset: -m_used (0 while m_used is -inf: those rows' weights are 0)
       f32x16 oacc[DB];
 #pragma unroll
       for (int db = 0; db < DB; ++db)
@@ -1328,6 +1331,38 @@ __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParam
                                                       0, 0);
       };
 
+      // Raises each row's reference to the row's maximum when that grew past it by more
+      // than kLazyRescale (the branch is taken when any row of the wavefront needs it).
+      auto raise_reference = [&](const float (&sc)[16]) {
+        // the scores pass through an empty asm so that the maximum is computed here, not
+        // hoisted in front of the branches that lead here
+        float t[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          t[j] = sc[j];
+          asm volatile("" : "+v"(t[j]));
+        }
+        float mx = fmaxf(fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3])), fmaxf(fmaxf(t[4], t[5]), fmaxf(t[6], t[7])));
+        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(t[8], t[9]), fmaxf(t[10], t[11])),
+                             fmaxf(fmaxf(t[12], t[13]), fmaxf(t[14], t[15]))));
+        {
+          typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+          const u32x2v sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float mloc = mx * csc;  // -inf stays -inf (csc > 0)
+        if (__builtin_amdgcn_ballot_w64(mloc > m_used + kLazyRescale)) {
+          keep_branch();
+          const float m_new = fmaxf(m_used, mloc);
+          const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_used - m_new);
+          lsum *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+          m_used = m_new;
+          nmu = m_used == kNegInf ? 0.f : -m_used;
+        }
+      };
+
       // softmax of step st (scores in c) and its P·V
       auto softmax_pv = [&](int st, f32x16& c) {
         const int kbase = kv_lo + 32 * st;
@@ -1341,28 +1376,17 @@ __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParam
 #pragma unroll
           for (int j = 0; j < 16; ++j) sc[j] = 16 * (j >> 3) + (j & 7) <= lim ? sc[j] : kNegInf;
         }
-        float mx = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])), fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(sc[8], sc[9]), fmaxf(sc[10], sc[11])),
-                             fmaxf(fmaxf(sc[12], sc[13]), fmaxf(sc[14], sc[15]))));
-        {
-          typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
-          const u32x2v sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-          mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        const float mloc = mx * csc;  // -inf stays -inf (csc > 0)
-        if (__builtin_amdgcn_ballot_w64(mloc > m_used + kTileLazyRescale)) {
-          keep_branch();
-          const float m_new = fmaxf(m_used, mloc);
-          const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m_used - m_new);
-          lsum *= alpha;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
-          m_used = m_new;
-        }
-        // a row that sees no key yet has weights 0; the half path carries 2^8 p
-        const float nmu = (m_used == kNegInf ? 0.f : -m_used) + (kExact ? 0.f : 8.f);
         const u32x4* img = stage[st % kTileStages];
         if constexpr (!kExact) {
+          // The reference is the rows' maximum over the first step (every row that sees a
+          // key of the item sees key kv_lo) and stays fixed for the item: no row maximum on
+          // the other steps.  A weight p of 65520 or more (the maximum grew by 16 or more
+          // in log2) rounds to an infinite half and makes the row's output non-finite,
+          // which the check after the last step catches.
+          if (st == 0) {
+            keep_branch();
+            raise_reference(sc);
+          }
           f16x8 pw[2];
           const f16x2 ones = {(_Float16)1.f, (_Float16)1.f};
 #pragma unroll
@@ -1383,6 +1407,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParam
               oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
                   __builtin_bit_cast(f16x8, img[(KB + 2 * db + kb) * 64 + lane]), pw[kb], oacc[db], 0, 0, 0);
         } else {
+          raise_reference(sc);
           bf16x8 phi[2], plo[2];
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb) {
@@ -1442,6 +1467,20 @@ __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParam
       }
       if (st < nsteps) step(st, rset1, rset0);
 
+      if constexpr (!kExact) {
+        // an infinite half weight or value reaches the output as inf or NaN (0 x inf);
+        // otherwise every partial sum is finite (p < 2^16 and |v| < 2^16 over at most 1024 keys)
+        float all = 0.f;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int j = 0; j < 16; ++j) all += oacc[db][j];
+        // an integer test of the exponent bits, kept opaque: built without NaNs, the compiler
+        // would otherwise fold it into a float compare with infinity, which a NaN fails
+        uint32_t bits = __float_as_uint(all);
+        asm volatile("" : "+v"(bits));
+        out_of_range = (bits & 0x7f800000u) == 0x7f800000u;
+      }
       if (active) {
         typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
         const u32x2v sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum), false, false);
@@ -1464,8 +1503,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParam
             for (int i = 0; i < 4; ++i)
               *reinterpret_cast<f32x4*>(slot + 32 * db + 8 * i + 4 * h) =
                   f32x4{oacc[db][4 * i], oacc[db][4 * i + 1], oacc[db][4 * i + 2], oacc[db][4 * i + 3]};
-          // the half path's O and l carry 2^8: the state (m − 8, l, O) is the same softmax state
-          slot[D] = m_used == kNegInf ? kNegInf : m_used - (kExact ? 0.f : 8.f);
+          slot[D] = m_used;
           slot[D + 1] = l;
         }
       }

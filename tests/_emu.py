@@ -33,7 +33,10 @@ def build(force=False):
             return EXE
     os.makedirs(os.path.dirname(EXE), exist_ok=True)
     tmp = f"{EXE}.{os.getpid()}.tmp"
-    cmd = [CLANG, "-std=c++20", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+    # -fno-honor-nans as in the device build: the compiler may then assume no float is NaN,
+    # and the kernels' NaN-sensitive tests must survive that assumption here too
+    cmd = [CLANG, "-std=c++20", "-O1", "-g", "-fno-honor-nans", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=all",
            "-I", os.path.join(ROOT, "tests", "emu"), "-I", os.path.join(ROOT, "include"),
            "-x", "c++", *[os.path.join(CSRC, s) for s in SOURCES_HIP], "-x", "none",
            os.path.join(CSRC, "pa_status.cpp"), emu[0], emu[1], "-lpthread", "-o", tmp]
