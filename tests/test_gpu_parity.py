@@ -364,6 +364,26 @@ def test_huge_value_on_a_causally_masked_key(pa):
         assert_close(got, ref, "bf16", f"2^30 at key {pos}")
 
 
+def test_score_jump_after_the_first_step(pa):
+    # one key's vector scaled by 2^6 (exact in bfloat16): its scores jump far above the
+    # maximum of the prefill item's first step; the item's half weights overflow and it is
+    # computed again by the exact pass.  Rows before the key must not see it.
+    for hq, hkv, ql, cl, pos in [(4, 4, [40], [40], 35), (8, 2, [1, 300], [90, 1500], 1300),
+                                 (32, 32, [512], [2000], 1900)]:
+        say(f"[case] key {pos} x 2^6 Hq={hq} Hkv={hkv} q={ql} L={cl}")
+        w = W.random_ragged(26, "bf16", hq, hkv, 128, ql, cl)
+        r = Run(w)
+        q, kc, vc, _, _ = W.make_values(w, DEV)
+        b = int(w.block_tables[len(ql) - 1, pos // 16])
+        kc[b, :, :, pos % 16] *= 64
+        out = r.forward(q, kc, vc)
+        r.check_status()
+        rows, ref = oracle_rows_all(w, q, kc, vc)
+        got = to_f64(out.index_select(0, torch.from_numpy(rows).to(DEV)))
+        assert np.isfinite(got).all()
+        assert_close(got, ref, "bf16", f"key {pos} x 2^6")
+
+
 def test_single_key_and_equal_scores(pa):
     # one key: output is that value row exactly; q = 0: output is the mean of the values
     for dt, hq, hkv, d in [("f32", 4, 4, 64), ("bf16", 32, 32, 128), ("bf16", 64, 8, 128)]:
