@@ -14,7 +14,7 @@ from oracle import attention as oattn
 from oracle import cache_ops, layout
 from tests import _emu
 from tests._pools import empty_pools, raw
-from tests.test_gpu_parity import (DEGENERATE, RAGGED, REJECTED, SHARED_CASES, many_sequences_batch,
+from tests.test_gpu_parity import (DEGENERATE, RAGGED, REJECTED, SHARED_CASES, many_sequences_batch, random_batch,
                                    shared_prefix_batch)
 
 pytestmark = pytest.mark.skipif(not _emu.available(), reason="needs the ROCm clang++ for the host build")
@@ -58,6 +58,18 @@ def test_idle_slots_and_block_aligned_lengths(emu, i):
     out, st = emu.forward(w, q, kp, vp)
     assert st == 0
     check(w, q, kp, vp, out, f"degenerate[{i}]")
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_batches(emu, seed):
+    # smaller random batches than the GPU test's (the emulator runs every lane as a thread)
+    w = random_batch(seed, max_seqs=5, max_ctx=1200, max_chunk=80)
+    rng = np.random.default_rng(3000 + seed)
+    kp, vp = empty_pools(rng, w.dtype, w.num_blocks, w.num_kv_heads, w.head_dim)
+    q = raw(rng.standard_normal((w.num_tokens, w.num_q_heads, w.head_dim)).astype(np.float32), w.dtype)
+    out, st = emu.forward(w, q, kp, vp)
+    assert st == 0
+    check(w, q, kp, vp, out, f"random[{seed}]")
 
 
 @pytest.mark.parametrize("scale", [-0.0625, 0.0, 0.75])

@@ -217,6 +217,22 @@ def test_batches_without_query_rows(pa):
     assert np.array_equal(host_raw(kc), before)
 
 
+def random_batch(seed, max_seqs=10, max_ctx=3000, max_chunk=300):
+    """A seeded random mixed batch: dtype, head dimension, query heads per KV head and a mix
+    of idle sequences, decodes and prefill chunks (prior context 0 .. max_ctx)."""
+    rng = np.random.default_rng(1000 + seed)
+    dt = "f32" if rng.random() < 0.25 else "bf16"
+    d = int(rng.choice([64, 128]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    n = int(rng.integers(1, max_seqs + 1))
+    kind = rng.choice(["idle", "decode", "chunk"], size=n, p=[0.1, 0.55, 0.35])
+    ql = np.where(kind == "idle", 0, np.where(kind == "decode", 1, rng.integers(2, max_chunk + 1, size=n)))
+    cl = ql + rng.integers(0, max_ctx + 1, size=n)
+    cl[kind == "idle"] = rng.integers(0, 50, size=int((kind == "idle").sum()))
+    return W.random_ragged(2000 + seed, dt, G * hkv, hkv, d, [int(x) for x in ql], [int(x) for x in cl])
+
+
 def many_sequences_batch(n=5000, n_split=12, split_hi=1500, heads=2):
     """n sequences (more than the 2,047 the workers' LDS lookup table holds one by one):
     MHA decodes, some split into partitions, plus short prefill rows and empty-query sequences."""
@@ -285,6 +301,15 @@ SHARED_CASES = [  # (seed, hq, hkv, d, groups, bad)
     (3, 4, 4, 64, [(16, 70), (3, 2100)], False),
     (4, 8, 8, 128, [(3, 100), (2, 200)], True),
 ]
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_batches(pa, seed):
+    # every row of a seeded random batch against the oracle, unreferenced pages poisoned
+    w = random_batch(seed)
+    run_and_check(pa, w, poison=True, label=f"random[{seed}] {w.dtype} Hq={w.num_q_heads} Hkv={w.num_kv_heads} "
+                                             f"d={w.head_dim} q={list(np.diff(w.query_start_loc))} "
+                                             f"L={list(w.context_lens)}")
 
 
 def test_many_sequences(pa):
