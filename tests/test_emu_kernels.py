@@ -60,10 +60,10 @@ def test_idle_slots_and_block_aligned_lengths(emu, i):
     check(w, q, kp, vp, out, f"degenerate[{i}]")
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(4))
 def test_random_batches(emu, seed):
     # smaller random batches than the GPU test's (the emulator runs every lane as a thread)
-    w = random_batch(seed, max_seqs=5, max_ctx=1200, max_chunk=80)
+    w = random_batch(seed, max_seqs=4, max_ctx=600, max_chunk=40)
     rng = np.random.default_rng(3000 + seed)
     kp, vp = empty_pools(rng, w.dtype, w.num_blocks, w.num_kv_heads, w.head_dim)
     q = raw(rng.standard_normal((w.num_tokens, w.num_q_heads, w.head_dim)).astype(np.float32), w.dtype)
