@@ -146,23 +146,24 @@ def test_huge_value_on_a_causally_masked_key(emu):
 
 # (chunk q_len, context, position of the key scaled by 2^6) for the score-jump tests: inside
 # the first partition, and in a later partition of a GQA chunk beside a decode row
-SCORE_JUMPS = [(4, 4, [40], [40], 35), (8, 2, [1, 300], [90, 1500], 1300)]
+SCORE_JUMPS = [(4, 4, [40], [40], 35, 6), (8, 2, [1, 300], [90, 1500], 1300, 6)]
 
 
 def test_score_jump_after_the_first_step(emu):
     # one key's vector scaled by 2^6: its scores jump far above the maximum of the item's
-    # first step, so the prefill tile's half weights overflow and the item is computed again
-    for hq, hkv, ql, cl, pos in SCORE_JUMPS:
+    # first step, so the prefill tile's half weights overflow and the item is computed again;
+    # a GQA decode batch with a key scaled by 2^10 (a jump past 2^127 in the weights)
+    for hq, hkv, ql, cl, pos, k in SCORE_JUMPS + [(16, 2, [1, 1], [3000, 700], 2500, 10)]:
         w = W.random_ragged(26, "bf16", hq, hkv, 64, ql, cl)
         rng = np.random.default_rng(26)
         kp, vp = empty_pools(rng, "bf16", w.num_blocks, hkv, 64)
         s = len(ql) - 1
         b = int(w.block_tables[s, pos // 16])
-        kp[b, :, :, pos % 16] = raw(layout.to_f64(kp[b, :, :, pos % 16], "bf16").astype(np.float32) * 64, "bf16")
+        kp[b, :, :, pos % 16] = raw(layout.to_f64(kp[b, :, :, pos % 16], "bf16").astype(np.float32) * 2.0 ** k, "bf16")
         q = raw(rng.standard_normal((w.num_tokens, hq, 64)).astype(np.float32), "bf16")
         out, st = emu.forward(w, q, kp, vp)
         assert st == 0
-        check(w, q, kp, vp, out, f"key {pos} x 2^6")
+        check(w, q, kp, vp, out, f"key {pos} x 2^{k}")
 
 
 def test_float32_head_dim_128_decode_and_prefill(emu):

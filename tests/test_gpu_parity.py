@@ -393,20 +393,24 @@ def test_score_jump_after_the_first_step(pa):
     # one key's vector scaled by 2^6 (exact in bfloat16): its scores jump far above the
     # maximum of the prefill item's first step; the item's half weights overflow and it is
     # computed again by the exact pass.  Rows before the key must not see it.
-    for hq, hkv, ql, cl, pos in [(4, 4, [40], [40], 35), (8, 2, [1, 300], [90, 1500], 1300),
-                                 (32, 32, [512], [2000], 1900)]:
-        say(f"[case] key {pos} x 2^6 Hq={hq} Hkv={hkv} q={ql} L={cl}")
+    # A GQA decode batch (the one-pass kernel) with a key scaled by 2^10: a jump past 2^127 in
+    # the weights of the wavefront that holds it, which is computed again with a row maximum
+    # on every step.
+    for hq, hkv, ql, cl, pos, k in [(4, 4, [40], [40], 35, 6), (8, 2, [1, 300], [90, 1500], 1300, 6),
+                                    (32, 32, [512], [2000], 1900, 6), (64, 8, [1, 1], [32768, 700], 30000, 10),
+                                    (16, 2, [1, 1], [3000, 700], 2500, 10)]:
+        say(f"[case] key {pos} x 2^{k} Hq={hq} Hkv={hkv} q={ql} L={cl}")
         w = W.random_ragged(26, "bf16", hq, hkv, 128, ql, cl)
         r = Run(w)
         q, kc, vc, _, _ = W.make_values(w, DEV)
         b = int(w.block_tables[len(ql) - 1, pos // 16])
-        kc[b, :, :, pos % 16] *= 64
+        kc[b, :, :, pos % 16] *= 2.0 ** k
         out = r.forward(q, kc, vc)
         r.check_status()
         rows, ref = oracle_rows_all(w, q, kc, vc)
         got = to_f64(out.index_select(0, torch.from_numpy(rows).to(DEV)))
         assert np.isfinite(got).all()
-        assert_close(got, ref, "bf16", f"key {pos} x 2^6")
+        assert_close(got, ref, "bf16", f"key {pos} x 2^{k}")
 
 
 def test_single_key_and_equal_scores(pa):
