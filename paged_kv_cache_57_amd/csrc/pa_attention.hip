@@ -44,7 +44,7 @@ namespace pa {
 namespace {
 
 enum { CLS_NONE = 0, CLS_VALU = 1, CLS_MFMA = 2, CLS_TILE = 3 };
-constexpr int kPartValu = 512;          // keys per VALU partition
+constexpr int kPartValu = 1024;         // keys per VALU partition
 constexpr int kPartMfmaDecode = 256;    // keys per partition of a one-row GQA decode tile
 constexpr int kPartMfmaPrefill = 1024;  // keys per partition of a small multi-row tile
 constexpr int kPartTile = 1024;         // keys per partition of a 256-row tile

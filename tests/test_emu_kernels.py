@@ -86,7 +86,7 @@ def test_scale_sign_and_size(emu, scale):
 
 def test_many_sequences(emu):
     # the LDS lookup table holds every second prefix entry; the rest is searched in memory
-    w = many_sequences_batch(2100, n_split=4, split_hi=900, heads=1)
+    w = many_sequences_batch(2100, n_split=4, split_hi=1600, heads=1)
     rng = np.random.default_rng(5)
     kp, vp = empty_pools(rng, "bf16", w.num_blocks, 1, 64)
     q = raw(rng.standard_normal((w.num_tokens, 1, 64)).astype(np.float32), "bf16")
@@ -168,8 +168,8 @@ def test_score_jump_after_the_first_step(emu):
 
 def test_float32_head_dim_128_decode_and_prefill(emu):
     # float32 at head_dim 128 (VALU worker only, values kept in 32 bits): MHA decode rows
-    # with split contexts (512-key partitions) and a 7-row prefill chunk
-    w = W.random_ragged(23, "f32", 4, 4, 128, [1, 7, 1], [900, 40, 17])
+    # with split contexts (1024-key partitions) and a 7-row prefill chunk
+    w = W.random_ragged(23, "f32", 4, 4, 128, [1, 7, 1], [1900, 40, 17])
     rng = np.random.default_rng(23)
     kp, vp = empty_pools(rng, "f32", w.num_blocks, 4, 128)
     q = raw(rng.standard_normal((w.num_tokens, 4, 128)).astype(np.float32), "f32")

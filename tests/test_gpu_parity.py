@@ -154,9 +154,9 @@ RAGGED = [
     ("bf16", 2, 2, 128, [300, 1], [2500, 40]),                    # 128-row tiles: 3 tiles, last one 44 rows
     ("bf16", 16, 2, 64, [40, 17], [40, 1100]),                    # GQA tiles: 320 and 136 rows
     ("bf16", 4, 4, 128, [129, 128, 2], [129, 1152, 2]),           # tile edges: 129 and 128 rows, 2-row MFMA
-    ("bf16", 2, 2, 64, [1, 3], [16500, 700]),                     # >= 32 partitions: four waves merge a row
-    ("f32", 2, 2, 64, [1, 2], [17000, 40]),                       # the same for float32 (512-key partitions)
-    ("f32", 4, 4, 128, [1, 3], [9000, 130]),                      # float32 at head_dim 128: 18 partitions merged
+    ("bf16", 2, 2, 64, [1, 3], [33000, 700]),                     # >= 32 partitions: four waves merge a row
+    ("f32", 2, 2, 64, [1, 2], [33500, 40]),                       # the same for float32 (1024-key partitions)
+    ("f32", 4, 4, 128, [1, 3], [9000, 130]),                      # float32 at head_dim 128: 9 partitions merged
 ]
 
 
