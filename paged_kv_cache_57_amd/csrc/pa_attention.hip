@@ -124,12 +124,23 @@ struct AttnParams {
   float scale_log2;
   int32_t is_f32;
   int32_t* ctrl;  // [2] VALU items, [3] MFMA items, [4] TILE items, [5] rows to merge, [6] some sequence
-                  // shares pages with a neighbour, [8..15] TILE tickets per XCD slice, [kValuTicket] VALU
-                  // tickets (on a 256-byte line of its own)
+                  // shares pages with a neighbour, [7] VALU items before the last partitions, [8..15]
+                  // TILE tickets per XCD slice, [16] sequences in perm_b, [17] VALU tickets in the
+                  // length order, [kValuTicket] VALU tickets (on a 256-byte line of its own)
   int32_t* pre_v;  // exclusive prefix over sequences of VALU items, [S + 1]
   int32_t* pre_m;  // ... of MFMA items
   int32_t* pre_t;  // ... of TILE items
   int32_t* pre_g;  // ... of (query token, query head) rows whose context was split
+  // VALU items in ticket order (batches with no shared pages): first every item that is not
+  // its row's last partition, numbered through pre_a (exclusive prefix over entries of
+  // rows x heads x (partitions - 1)); then the last partitions, sequence by sequence in
+  // perm_b order (longest last partition first, in 16 classes of length), numbered through
+  // pre_b (exclusive prefix of rows x heads over perm_b).  seq_aux: per sequence, its
+  // length class (-1: no VALU items) and its rows x heads, from the planner's first pass.
+  int32_t* pre_a;
+  int32_t* pre_b;
+  int32_t* perm_b;
+  int32_t* seq_aux;
   i32x4* seqinfo;  // per entry: first query row, q_len, context length, flags (kEnt*)
   float* partials;  // [T][Hq][maxparts][D + 4]: O (unnormalised), m, l, 2 pad
   int32_t maxparts;
@@ -145,6 +156,9 @@ struct AttnParams {
   uint32_t call_tag;
   // VALU worker: workgroups resident on the device at once (at most the grid)
   int32_t valu_resident;
+  // the host's bound on VALU items allows the length order (fewer than kLenOrderItems per
+  // resident wavefront): the planner then records what the order needs
+  int32_t len_order_ok;
 };
 
 // Entry flags.  A group entry's rows are its members' single decode rows,
@@ -210,6 +224,8 @@ __device__ inline SeqInfo seq_record(const AttnParams& p, int s) {
 // global loads; only batches larger than kSkip sequences finish the search
 // in global memory, inside one stride.
 constexpr int kSkip = 2048;
+constexpr int kLenClasses = 16;  // length classes of the VALU worker's last partitions
+constexpr int kLenOrderItems = 8;  // the length order is used below this many VALU items per resident wavefront
 
 struct SkipTable {
   int stride, count;
@@ -277,6 +293,15 @@ __device__ inline i32x4 wave_incl_scan(i32x4 v, int lane) {
   return v;
 }
 
+__device__ inline int wave_incl_scan1(int v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
 // With shared-prefix groups it first checks every group — one wavefront per
 // group, the lanes comparing the members' table entries with the first
 // member's — and records the group entries and the members' offsets; a group
@@ -320,11 +345,23 @@ __device__ inline void plan_groups(const AttnParams& p, int tid) {
 
 __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
   __shared__ i32x4 wsum[16];
+  __shared__ int wsum_a[16];
   __shared__ i32x4 carry;
+  __shared__ int carry_a;
   __shared__ int any_shared;
+  // last partitions: sequences and rows x heads per length class, the classes' first slots
+  // (longest class first), and the running (sequences << 32 | rows x heads) per class
+  __shared__ int cls_n[kLenClasses], cls_g[kLenClasses], cls_n0[kLenClasses], cls_g0[kLenClasses];
+  __shared__ unsigned long long cls_run[kLenClasses];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid < kLenClasses) {
+    cls_n[tid] = 0;
+    cls_g[tid] = 0;
+    cls_run[tid] = 0;
+  }
   if (tid == 0) {
     carry = i32x4{0, 0, 0, 0};
+    carry_a = 0;
     any_shared = 0;
     if (p.qsl[0] != 0 || p.qsl[p.num_seqs] != p.T) flag_status(p.dev_status, PA_DEV_BAD_LENGTH);
   }
@@ -333,7 +370,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
   for (int base = 0; base < p.num_ent; base += 1024) {
     const int s = base + tid;
     i32x4 cnt = {0, 0, 0, 0};  // VALU, MFMA, TILE items, rows to merge
+    int cnt_a = 0;  // VALU items that are not their row's last partition
     if (s < p.num_seqs) {
+      if (p.len_order_ok) p.seq_aux[2 * s] = -1;
       SeqInfo si = read_seq(p, s);
       int koff = 0, nps = 0;
       if (p.num_groups > 0) {
@@ -360,7 +399,19 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
       } else {
         const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L - koff);
         const int items = w.groups * w.nparts;
-        if (w.cls == CLS_VALU) cnt[0] = items;
+        if (w.cls == CLS_VALU) {
+          cnt[0] = items;
+        }
+        if (w.cls == CLS_VALU && p.len_order_ok) {
+          cnt_a = items - w.groups;
+          // length class of the last partition (of the last row): longer ones are handed out first
+          const int tail = (si.L - koff - 1) % w.part + 1;
+          const int c = (tail - 1) * kLenClasses / w.part;
+          p.seq_aux[2 * s] = c;
+          p.seq_aux[2 * s + 1] = w.groups;
+          atomicAdd(&cls_n[c], 1);
+          atomicAdd(&cls_g[c], w.groups);
+        }
         else if (w.cls == CLS_MFMA) cnt[1] = items;
         else if (w.cls == CLS_TILE) cnt[2] = items;
         if (nps > 0 || w.nparts > 1) cnt[3] = si.q_len * p.Hq;
@@ -373,24 +424,70 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
       }
     }
     const i32x4 inc = wave_incl_scan(cnt, lane);
-    if (lane == 63) wsum[wv] = inc;
+    const int inc_a = wave_incl_scan1(cnt_a, lane);
+    if (lane == 63) {
+      wsum[wv] = inc;
+      wsum_a[wv] = inc_a;
+    }
     __syncthreads();
     i32x4 before = carry;
-    for (int k = 0; k < wv; ++k) before += wsum[k];
+    int before_a = carry_a;
+    for (int k = 0; k < wv; ++k) {
+      before += wsum[k];
+      before_a += wsum_a[k];
+    }
     if (s < p.num_ent) {
       const i32x4 ex = before + inc - cnt;
       p.pre_v[s] = ex[0];
       p.pre_m[s] = ex[1];
       p.pre_t[s] = ex[2];
       p.pre_g[s] = ex[3];
+      p.pre_a[s] = before_a + inc_a - cnt_a;
     }
     __syncthreads();
     if (tid == 0) {
       i32x4 tot = carry;
-      for (int k = 0; k < 16; ++k) tot += wsum[k];
+      int tot_a = carry_a;
+      for (int k = 0; k < 16; ++k) {
+        tot += wsum[k];
+        tot_a += wsum_a[k];
+      }
       carry = tot;
+      carry_a = tot_a;
     }
     __syncthreads();
+  }
+  // The length order pays where the VALU items are few per resident wavefront (a small
+  // batch's last round of items is most of its time); in a large batch the items left at the
+  // end are a small share and the planner's second pass would cost more than it saves.
+  const bool by_len = p.len_order_ok && any_shared == 0 && carry[0] < kLenOrderItems * p.valu_resident;
+  if (tid == 0) p.ctrl[17] = by_len ? 1 : 0;
+  if (by_len) {
+    // the classes' first slots, longest class first
+    if (tid == 0) {
+      int n0 = 0, g0 = 0;
+      for (int c = kLenClasses - 1; c >= 0; --c) {
+        cls_n0[c] = n0;
+        cls_g0[c] = g0;
+        n0 += cls_n[c];
+        g0 += cls_g[c];
+      }
+      p.pre_b[n0] = g0;
+      p.ctrl[16] = n0;
+    }
+    __syncthreads();
+    // each sequence with VALU items takes the next slot of its class (one atomic gives its
+    // slot and the rows x heads before it in the class together, so pre_b stays increasing)
+    for (int s = tid; s < p.num_seqs; s += 1024) {
+      const int c = p.seq_aux[2 * s];  // written by this thread in the first pass
+      if (c >= 0) {
+        const unsigned long long g = (unsigned long long)p.seq_aux[2 * s + 1];
+        const unsigned long long r = atomicAdd(&cls_run[c], (1ull << 32) | g);
+        const int k = cls_n0[c] + (int)(r >> 32);
+        p.perm_b[k] = s;
+        p.pre_b[k] = cls_g0[c] + (int)(r & 0xffffffffu);
+      }
+    }
   }
   if (tid == 0) {
     p.pre_v[p.num_ent] = carry[0];
@@ -402,6 +499,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(AttnParams p) {
     p.ctrl[4] = carry[2];
     p.ctrl[5] = carry[3];
     p.ctrl[6] = any_shared;
+    p.pre_a[p.num_ent] = carry_a;
+    p.ctrl[7] = carry_a;
     for (int x = 0; x < kXcds; ++x) p.ctrl[8 + x] = 0;  // TILE tickets handed out so far, per XCD slice
     p.ctrl[kValuTicket] = 0;                             // VALU tickets handed out so far
   }
@@ -458,40 +557,72 @@ __global__ __launch_bounds__(64) void valu_attn_kernel(AttnParams p) {
   constexpr int NIV = D / RPI;   // value loads per page
   constexpr bool kBf16 = sizeof(T) == 2;
   __shared__ float lds_p[64];
-  __shared__ int skip[kSkip];
+  __shared__ int skip[kSkip], skip_b[kSkip];
   __shared__ int ticket;
+  __shared__ int order_b[5];  // ticket order: items before the last partitions, sequences in
+                              // perm_b, skip_b's stride and count, perm_b - pre_b (kept here,
+                              // not in scalar registers)
 
   const int lane = threadIdx.x & 63;
   const int total = wave_uniform(p.ctrl[2]);
   // Items.  In a batch where sequences share pages with a neighbour (branches of one
-  // prompt), workgroup b takes items π(b), π(b) + grid, ..., and the grid is a few times
-  // the resident workgroups, so items start in dispatch order.  π permutes each block of
+  // prompt), workgroup b takes items π(b), π(b) + grid, ... in the planner's sequence order
+  // (pre_v: a sequence's items row-head by row-head, partitions innermost), and the grid is
+  // a few times the resident workgroups, so items start in dispatch order.  π permutes each block of
   // 32 workgroups so that XCD x (workgroups go to the XCDs in turn) takes items 4x .. 4x + 3
   // of the block.  The readers of a page (one head and partition in neighbouring sequences,
   // Hq x partitions items apart: a multiple of 32 for 32 query heads) then run close in
   // time on one XCD and share its reads through L2.  Otherwise only the resident
   // workgroups work: b takes item b, then the resident count plus a ticket from one
   // counter, so every wavefront stays busy to the end whatever the mix of item lengths.
+  // Tickets follow the sequence order too, except in batches with few items per resident
+  // wavefront, where the planner orders the rows' last partitions after all other items,
+  // longest first (pre_a, pre_b), so that the items left at the end are the short ones.
   // Thread 0 takes the ticket between two barriers (the workgroup is this one wavefront),
   // so no lane-dependent branch spans the item loop.
   const bool strided = wave_uniform(p.ctrl[6]) != 0;
   const int b = (int)blockIdx.x;
   // no first item (its block of 32 starts past the end) or, with tickets, not resident: no work
   if ((b & ~31) >= total || (!strided && b >= p.valu_resident)) return;
-  const SkipTable tab = stage_skip(skip, p.pre_v, p.num_ent);
+  const bool by_len = !strided && wave_uniform(p.ctrl[17]) != 0;  // the planner's length order
+  const int32_t* const pre = by_len ? p.pre_a : p.pre_v;  // the items' prefix over sequences
+  const SkipTable tab = stage_skip(skip, pre, p.num_ent);
+  if (by_len) {
+    const int num_b = wave_uniform(p.ctrl[16]);
+    const SkipTable tb = stage_skip(skip_b, p.pre_b, num_b);
+    order_b[0] = p.ctrl[7];  // every lane stores the same values
+    order_b[1] = num_b;
+    order_b[2] = tb.stride;
+    order_b[3] = tb.count;
+    order_b[4] = (int)(p.perm_b - p.pre_b);
+  }
   const T* __restrict__ kc = (const T*)p.k_cache;
   const T* __restrict__ vc = (const T*)p.v_cache;
   const int64_t page_elems = (int64_t)kBlock * D;
 
   for (int item = wave_uniform(strided ? (b & ~31) + 4 * (b & 7) + ((b >> 3) & 3) : b); item < total;) {
-    const SeqHit hit = find_seq(skip, tab, p.pre_v, p.num_ent, item);
-    const int s = hit.s;
-    const int local = item - hit.first;
+    // the item's sequence, row-head (rh) and partition
+    int s, local;
+    const int total_a = by_len ? wave_uniform(order_b[0]) : total;
+    const bool last_part = item >= total_a;  // wave-uniform; never in sequence order
+    if (!last_part) {
+      const SeqHit hit = find_seq(skip, tab, pre, p.num_ent, item);
+      s = hit.s;
+      local = item - hit.first;
+    } else {
+      const SkipTable tb{wave_uniform(order_b[2]), wave_uniform(order_b[3])};
+      const SeqHit hit = find_seq(skip_b, tb, p.pre_b, wave_uniform(order_b[1]), item - total_a);
+      s = wave_uniform(p.pre_b[wave_uniform(order_b[4]) + hit.s]);  // perm_b[hit.s]
+      local = item - total_a - hit.first;
+    }
     const SeqInfo si = seq_record(p, s);
     const EntX ex = ent_x(p, s, si.flags);  // a member skips the shared keys
     const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L - ex.koff);
-    const int pidx = local % w.nparts;
-    const int rh = local / w.nparts;
+    // sequence order: partitions innermost; ticket order: the partitions before the last,
+    // innermost, or the last partition of row-head `local`
+    const int np = by_len ? w.nparts - 1 : w.nparts;
+    const int pidx = last_part ? w.nparts - 1 : local % np;
+    const int rh = last_part ? local : local / np;
     const int h = rh % p.Hq;
     const int i = rh / p.Hq;
     const int t = si.a + i;
@@ -1616,7 +1747,7 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
 
 // ---------------------------------------------------------------- host side
 struct WsLayout {
-  size_t ctrl, pre_v, pre_m, pre_t, pre_g, seqinfo, seqx, partials, dec_ctr, total;
+  size_t ctrl, pre_v, pre_m, pre_t, pre_g, pre_a, pre_b, perm_b, seq_aux, seqinfo, seqx, partials, dec_ctr, total;
   int maxparts;
 };
 
@@ -1636,7 +1767,11 @@ WsLayout ws_layout(int S, int NG, int T, int Hq, int Hkv, int D, int max_ctx, bo
   l.pre_m = l.pre_v + align256((size_t)(E + 1) * 4);
   l.pre_t = l.pre_m + align256((size_t)(E + 1) * 4);
   l.pre_g = l.pre_t + align256((size_t)(E + 1) * 4);
-  l.seqinfo = l.pre_g + align256((size_t)(E + 1) * 4);
+  l.pre_a = l.pre_g + align256((size_t)(E + 1) * 4);
+  l.pre_b = l.pre_a + align256((size_t)(E + 1) * 4);
+  l.perm_b = l.pre_b + align256((size_t)(S + 1) * 4);
+  l.seq_aux = l.perm_b + align256((size_t)S * 4);
+  l.seqinfo = l.seq_aux + align256((size_t)S * 8);
   l.seqx = l.seqinfo + align256((size_t)E * 16);
   l.partials = l.seqx + (NG > 0 ? align256((size_t)E * 16) : 0);
   const size_t part_bytes = l.maxparts > 1 ? (size_t)T * Hq * l.maxparts * slot_floats(D) * 4 : 0;
@@ -1697,20 +1832,22 @@ int valu_resident_groups() {
 template <typename T, int D>
 void launch_attention(const AttnParams& p, bool may_valu, bool may_mfma, bool may_tile, int64_t bound_v,
                       int grid_m, int grid_t, hipStream_t stream) {
+  // a strided batch (sequences sharing pages) uses all of the VALU grid, a ticket batch its
+  // resident part; the grid is a multiple of 32 (the strided order permutes blocks of 32)
+  AttnParams pv = p;
+  int64_t grid_v = 32;
+  if (may_valu) {
+    const int64_t res = valu_resident_groups<T, D>();
+    grid_v = std::min<int64_t>(std::max<int64_t>(32, kValuGridPerResident * res / 32 * 32),
+                               std::max<int64_t>(32, (bound_v + 31) / 32 * 32));
+    pv.valu_resident = (int32_t)std::min<int64_t>(res, grid_v);
+    pv.len_order_ok = bound_v < (int64_t)kLenOrderItems * pv.valu_resident ? 1 : 0;
+  }
   mark(0, 0, stream);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, p);
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, pv);
   mark(0, 1, stream);
   mark(1, 0, stream);
-  if (may_valu) {
-    // a strided batch (sequences sharing pages) uses all of the grid, a ticket batch its resident part
-    AttnParams pv = p;
-    const int64_t res = valu_resident_groups<T, D>();
-    // a multiple of 32 (the strided order permutes blocks of 32 workgroups)
-    const int64_t grid = std::min<int64_t>(std::max<int64_t>(32, kValuGridPerResident * res / 32 * 32),
-                                           std::max<int64_t>(32, (bound_v + 31) / 32 * 32));
-    pv.valu_resident = (int32_t)std::min<int64_t>(res, grid);
-    hipLaunchKernelGGL((valu_attn_kernel<T, D>), dim3((unsigned)grid), dim3(64), 0, stream, pv);
-  }
+  if (may_valu) hipLaunchKernelGGL((valu_attn_kernel<T, D>), dim3((unsigned)grid_v), dim3(64), 0, stream, pv);
   mark(1, 1, stream);
   mark(2, 0, stream);
   if constexpr (sizeof(T) == 2)
@@ -1834,6 +1971,10 @@ pa_status forward_impl(const char* fn, void* out, const void* q, const void* k_c
   p.pre_m = (int32_t*)(ws + wl.pre_m);
   p.pre_t = (int32_t*)(ws + wl.pre_t);
   p.pre_g = (int32_t*)(ws + wl.pre_g);
+  p.pre_a = (int32_t*)(ws + wl.pre_a);
+  p.pre_b = (int32_t*)(ws + wl.pre_b);
+  p.perm_b = (int32_t*)(ws + wl.perm_b);
+  p.seq_aux = (int32_t*)(ws + wl.seq_aux);
   p.seqinfo = (i32x4*)(ws + wl.seqinfo);
   p.partials = (float*)(ws + wl.partials);
   p.maxparts = wl.maxparts;
