@@ -1417,7 +1417,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParam
 
     auto pass = [&](auto exact_tag) {
       constexpr bool kExact = decltype(exact_tag)::value;
-      bool out_of_range = false;
+      bool nonfinite = false;
       // Stage step st: keys as loaded; values zeroed past kv_hi (the pool there may hold
       // anything), then converted to half unless kExact (a magnitude of 65520 or more
       // becomes an infinite half, which makes the output of every row that uses it
@@ -1610,7 +1610,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParam
         // would otherwise fold it into a float compare with infinity, which a NaN fails
         uint32_t bits = __float_as_uint(all);
         asm volatile("" : "+v"(bits));
-        out_of_range = (bits & 0x7f800000u) == 0x7f800000u;
+        nonfinite = (bits & 0x7f800000u) == 0x7f800000u;
       }
       if (active) {
         typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
@@ -1638,7 +1638,7 @@ __global__ __launch_bounds__(64 * kTileWaves, 1) void tile_attn_kernel(AttnParam
           slot[D + 1] = l;
         }
       }
-      return out_of_range;
+      return nonfinite;
     };
 
     const bool oor = pass(std::false_type{});
