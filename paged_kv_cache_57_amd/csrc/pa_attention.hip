@@ -1673,12 +1673,26 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
   const int sub = wv % WPR;
   const int total = wave_uniform(p.ctrl[5]);
   const SkipTable tab = stage_skip(skip, p.pre_g, p.num_ent);
-  // row g of the merge list; the WPR wavefronts sharing a row see the same g
-  for (int g = (int)blockIdx.x * RPB + wv / WPR; g < total; g += (int)gridDim.x * RPB) {
-    const SeqHit hit = find_seq(skip, tab, p.pre_g, p.num_ent, g);
-    const SeqInfo si = seq_record(p, hit.s);
-    const EntX ex = ent_x(p, hit.s, si.flags);
-    const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L - ex.koff);
+  // Rows g of the merge list: each group of WPR wavefronts takes a contiguous block of rows
+  // (the heads of consecutive tokens of mostly one sequence, whose record it then looks up
+  // once); the WPR wavefronts sharing a row see the same g.
+  const int nrow_groups = (int)gridDim.x * RPB;
+  const int per = (total + nrow_groups - 1) / nrow_groups;
+  const int g0 = ((int)blockIdx.x * RPB + wv / WPR) * per;
+  const int g1 = min(total, g0 + per);
+  SeqHit hit{0, 0};
+  int hit_end = 0;  // rows [hit.first, hit_end) belong to sequence hit.s
+  SeqInfo si{};
+  EntX ex{};
+  SeqWork w{};
+  for (int g = g0; g < g1; ++g) {
+    if (g >= hit_end) {  // wave-uniform
+      hit = find_seq(skip, tab, p.pre_g, p.num_ent, g);
+      hit_end = wave_uniform(p.pre_g[hit.s + 1]);
+      si = seq_record(p, hit.s);
+      ex = ent_x(p, hit.s, si.flags);
+      w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L - ex.koff);
+    }
     const int local = g - hit.first;
     const int i = local / p.Hq, h = local % p.Hq;
     const int t = si.a + i;
@@ -1686,41 +1700,65 @@ __global__ __launch_bounds__(256) void merge_kernel(AttnParams p) {
     // shared partitions, then the row's own ones; later partitions hold no visible key
     const int np = ex.nps + (w.nparts > 0 ? min(w.nparts, (pos - ex.koff) / w.part + 1) : 0);
     const float* base = p.partials + ((int64_t)t * p.Hq + h) * p.maxparts * SF;
-    // M and l over all partitions; lanes past np read partition 0 and drop it
-    float M = kNegInf;
-    for (int q0 = 0; q0 < np; q0 += 64) {
-      const int q = q0 + lane;
-      const float mq = base[(int64_t)(q < np ? q : 0) * SF + D];
-      M = fmaxf(M, q < np ? mq : kNegInf);
-    }
-    M = wave_max(M);
-    float lsum = 0.f;
-    for (int q0 = 0; q0 < np; q0 += 64) {
-      const int q = q0 + lane;
-      const float* sl = base + (int64_t)(q < np ? q : 0) * SF;
-      // M is finite, so 2^(m - M) is 0 for an empty partition (m = -inf) and for lanes past np
-      const float mq = sl[D], lq = sl[D + 1];
-      lsum += lq * fast_exp2(q < np ? mq - M : kNegInf);
-    }
-    const float l = wave_sum(lsum);
-    // this lane: columns 4c .. 4c + 3 of partitions qo + sub * PPI + k * WPR * PPI
     const int c = lane % LPP, qo = lane / LPP;
+    float M = kNegInf, l = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int q0 = sub * PPI; q0 < np; q0 += WPR * PPI * U) {
+    if (np <= WPR * PPI * U) {  // wave-uniform
+      // One round trip: every load of the row (the partitions' m and l, lane q holding
+      // partition q, and this lane's output columns) is issued before any is used.
+      const float* ss = base + (int64_t)(lane < np ? lane : 0) * SF;
+      const float ms = ss[D], ls = ss[D + 1];
       f32x4 o[U];
       float mq[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int q = q0 + qo + u * WPR * PPI;
+        const int q = sub * PPI + qo + u * WPR * PPI;
         const float* sl = base + (int64_t)(q < np ? q : 0) * SF;
         o[u] = *reinterpret_cast<const f32x4*>(sl + 4 * c);
         mq[u] = sl[D];
       }
+      M = wave_max(lane < np ? ms : kNegInf);
+      // M is finite, so 2^(m - M) is 0 for an empty partition (m = -inf) and for lanes past np
+      l = wave_sum(ls * fast_exp2(lane < np ? ms - M : kNegInf));
 #pragma unroll
       for (int u = 0; u < U; ++u) {
-        const int q = q0 + qo + u * WPR * PPI;
-        const float wq = fast_exp2(q < np ? mq[u] - M : kNegInf);  // empty partition: weight 0, O_p = 0
-        acc += wq * o[u];
+        const int q = sub * PPI + qo + u * WPR * PPI;
+        acc += fast_exp2(q < np ? mq[u] - M : kNegInf) * o[u];  // empty partition: weight 0, O_p = 0
+      }
+    } else {
+      // M and l over all partitions; lanes past np read partition 0 and drop it
+      for (int q0 = 0; q0 < np; q0 += 64) {
+        const int q = q0 + lane;
+        const float mq = base[(int64_t)(q < np ? q : 0) * SF + D];
+        M = fmaxf(M, q < np ? mq : kNegInf);
+      }
+      M = wave_max(M);
+      float lsum = 0.f;
+      for (int q0 = 0; q0 < np; q0 += 64) {
+        const int q = q0 + lane;
+        const float* sl = base + (int64_t)(q < np ? q : 0) * SF;
+        // M is finite, so 2^(m - M) is 0 for an empty partition (m = -inf) and for lanes past np
+        const float mq = sl[D], lq = sl[D + 1];
+        lsum += lq * fast_exp2(q < np ? mq - M : kNegInf);
+      }
+      l = wave_sum(lsum);
+      // this lane: columns 4c .. 4c + 3 of partitions qo + sub * PPI + k * WPR * PPI
+      for (int q0 = sub * PPI; q0 < np; q0 += WPR * PPI * U) {
+        f32x4 o[U];
+        float mq[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int q = q0 + qo + u * WPR * PPI;
+          const float* sl = base + (int64_t)(q < np ? q : 0) * SF;
+          o[u] = *reinterpret_cast<const f32x4*>(sl + 4 * c);
+          mq[u] = sl[D];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int q = q0 + qo + u * WPR * PPI;
+          const float wq = fast_exp2(q < np ? mq[u] - M : kNegInf);  // empty partition: weight 0, O_p = 0
+          acc += wq * o[u];
+        }
       }
     }
 #pragma unroll
