@@ -566,20 +566,20 @@ __global__ __launch_bounds__(64) void valu_attn_kernel(AttnParams p) {
   const int lane = threadIdx.x & 63;
   const int total = wave_uniform(p.ctrl[2]);
   // Items.  In a batch where sequences share pages with a neighbour (branches of one
-  // prompt), workgroup b takes items π(b), π(b) + grid, ... in the planner's sequence order
-  // (pre_v: a sequence's items row-head by row-head, partitions innermost), and the grid is
-  // a few times the resident workgroups, so items start in dispatch order.  π permutes each block of
-  // 32 workgroups so that XCD x (workgroups go to the XCDs in turn) takes items 4x .. 4x + 3
-  // of the block.  The readers of a page (one head and partition in neighbouring sequences,
-  // Hq x partitions items apart: a multiple of 32 for 32 query heads) then run close in
-  // time on one XCD and share its reads through L2.  Otherwise only the resident
-  // workgroups work: b takes item b, then the resident count plus a ticket from one
-  // counter, so every wavefront stays busy to the end whatever the mix of item lengths.
-  // Tickets follow the sequence order too, except in batches with few items per resident
-  // wavefront, where the planner orders the rows' last partitions after all other items,
-  // longest first (pre_a, pre_b), so that the items left at the end are the short ones.
-  // Thread 0 takes the ticket between two barriers (the workgroup is this one wavefront),
-  // so no lane-dependent branch spans the item loop.
+  // prompt), workgroup b takes items π(b), π(b) + grid, ... in the planner's sequence
+  // order (pre_v: a sequence's items row-head by row-head, partitions innermost), and the
+  // grid is a few times the resident workgroups, so items start in dispatch order.  π
+  // permutes each block of 32 workgroups so that XCD x (workgroups go to the XCDs in turn)
+  // takes items 4x .. 4x + 3 of the block.  The readers of a page (one head and partition
+  // in neighbouring sequences, Hq x partitions items apart: a multiple of 32 for 32 query
+  // heads) then run close in time on one XCD and share its reads through L2.  Otherwise
+  // only the resident workgroups work: b takes item b, then the resident count plus a
+  // ticket from one counter, so every wavefront stays busy to the end whatever the mix of
+  // item lengths.  Tickets follow the sequence order too, except in batches with few items
+  // per resident wavefront, where the planner orders the rows' last partitions after all
+  // other items, longest first (pre_a, pre_b), so that the items left at the end are the
+  // short ones.  Thread 0 takes the ticket between two barriers (the workgroup is this one
+  // wavefront), so no lane-dependent branch spans the item loop.
   const bool strided = wave_uniform(p.ctrl[6]) != 0;
   const int b = (int)blockIdx.x;
   // no first item (its block of 32 starts past the end) or, with tickets, not resident: no work
@@ -620,7 +620,8 @@ __global__ __launch_bounds__(64) void valu_attn_kernel(AttnParams p) {
     const SeqWork w = seq_work(p.is_f32, p.G, p.Hq, p.Hkv, si.q_len, si.L - ex.koff);
     // sequence order: partitions innermost; ticket order: the partitions before the last,
     // innermost, or the last partition of row-head `local`
-    const int np = by_len ? w.nparts - 1 : w.nparts;
+    // (in the length order an item before the last partitions has 2 or more in its sequence)
+    const int np = by_len ? max(w.nparts - 1, 1) : w.nparts;
     const int pidx = last_part ? w.nparts - 1 : local % np;
     const int rh = last_part ? local : local / np;
     const int h = rh % p.Hq;
