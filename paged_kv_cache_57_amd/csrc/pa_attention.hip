@@ -279,7 +279,9 @@ __device__ inline SeqHit find_seq(const int* sk, SkipTable t, const int32_t* pre
 
 // ---------------------------------------------------------------- planner
 // One workgroup: checks every sequence, records it, and writes the exclusive
-// prefix sums of its items per worker class and of its rows to merge.
+// prefix sums of its items per worker class and of its rows to merge; for small
+// batches also the VALU worker's length order (a second pass: a counting sort of
+// the sequences by the length of their last partition).
 __device__ inline i32x4 wave_incl_scan(i32x4 v, int lane) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
