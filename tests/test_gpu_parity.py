@@ -157,6 +157,7 @@ RAGGED = [
     ("bf16", 2, 2, 64, [1, 3], [33000, 700]),                     # >= 32 partitions: four waves merge a row
     ("f32", 2, 2, 64, [1, 2], [33500, 40]),                       # the same for float32 (1024-key partitions)
     ("f32", 4, 4, 128, [1, 3], [9000, 130]),                      # float32 at head_dim 128: 9 partitions merged
+    ("bf16", 2, 2, 128, [1, 1, 2], [20000, 9000, 100]),           # 20 and 9 partitions: one wavefront, load rounds
 ]
 
 
