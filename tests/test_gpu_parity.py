@@ -318,6 +318,15 @@ def test_many_sequences(pa):
     run_and_check(pa, w, label="5000 sequences")
 
 
+def test_length_order_over_many_sequences(pa):
+    # 1500 one-head decode sequences: few VALU items per resident wavefront, so the planner
+    # sorts the last partitions by length, over two chunks of 1024 sequences in both passes
+    rng = np.random.default_rng(33)
+    cl = rng.integers(1, 3000, size=1500)
+    w = W.random_ragged(33, "bf16", 1, 1, 128, [1] * len(cl), [int(x) for x in cl])
+    run_and_check(pa, w, label="length order, 1500 sequences")
+
+
 def test_very_long_contexts(pa):
     """Contexts of 131,072 keys: 256 VALU partitions (MHA decode, bf16 and float32) and
     512 MFMA partitions (GQA decode) merged per row, plus a 130-row prefill chunk at the
